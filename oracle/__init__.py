@@ -1,0 +1,197 @@
+"""CPU oracle for blockwise NF4/FP4 quantization and the 4-bit x bf16 product.
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may load it; the product library never does.
+
+A thin numpy wrapper over ``nf4_oracle.c`` (plain C, built with gcc, no SIMD
+intrinsics, no BLAS). bf16 arrays are carried as ``numpy.uint16`` bit patterns.
+Every function states which passage of the pages it follows; see the C file's
+header for the sources and the readings taken where the pages are silent.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnf4_oracle.so")
+
+NF4 = 0
+FP4 = 1
+QUANT_TYPES = {"nf4": NF4, "fp4": FP4}
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile nf4_oracle.c with gcc into libnf4_oracle.so (IEEE binary32, no
+    contraction, no fast-math)."""
+    from oracle.build import build_oracle
+
+    return build_oracle(force=force)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    i64 = ctypes.c_int64
+    i32 = ctypes.c_int
+    lib.orc_norm_ppf.restype = ctypes.c_double
+    lib.orc_norm_ppf.argtypes = [ctypes.c_double]
+    lib.orc_codebook.restype = i32
+    lib.orc_codebook.argtypes = [i32, P]
+    lib.orc_nearest_code.restype = i32
+    lib.orc_nearest_code.argtypes = [i32, ctypes.c_float]
+    lib.orc_f32_to_bf16.restype = ctypes.c_uint16
+    lib.orc_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.orc_quantize.restype = i32
+    lib.orc_quantize.argtypes = [P, i64, i32, i32, P, P]
+    lib.orc_double_quant.restype = i32
+    lib.orc_double_quant.argtypes = [P, i64, i32, P, P]
+    lib.orc_dequantize.restype = i32
+    lib.orc_dequantize.argtypes = [P, i64, i32, i32, P, P, P, i32, P, P]
+    lib.orc_matmul_bf16.restype = i32
+    lib.orc_matmul_bf16.argtypes = [P, P, i64, i64, i64, P]
+    lib.orc_matmul_bf16_sampled.restype = i32
+    lib.orc_matmul_bf16_sampled.argtypes = [P, P, i64, P, P, i64, P]
+    lib.orc_gemv_quantized.restype = i32
+    lib.orc_gemv_quantized.argtypes = [P, i64, P, i64, i64, i32, i32, P, P, P, i32, P]
+    _lib = lib
+    return lib
+
+
+def _qt(quant_type) -> int:
+    if isinstance(quant_type, str):
+        return QUANT_TYPES[quant_type]
+    return int(quant_type)
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise ValueError(f"oracle {what} rejected its arguments (rc={rc})")
+
+
+def norm_ppf(p: float) -> float:
+    """Standard normal quantile, bisection on the C library's erfc."""
+    return _load().orc_norm_ppf(float(p))
+
+
+def codebook(quant_type="nf4") -> np.ndarray:
+    """fp32[16] code values indexed by the 4-bit code (NF4 page, table
+    数学原理对比 row 数值表示; FP4 per the page's closing notes)."""
+    out = np.zeros(16, dtype=np.float32)
+    _check(_load().orc_codebook(_qt(quant_type), _ptr(out)), "codebook")
+    return out
+
+
+def nearest_code(s: float, quant_type="nf4") -> int:
+    """Code of the codebook value nearest to the fp32 value s (ties to the
+    smaller value)."""
+    return int(_load().orc_nearest_code(_qt(quant_type), ctypes.c_float(float(s))))
+
+
+def f32_to_bf16(f: float) -> int:
+    return int(_load().orc_f32_to_bf16(ctypes.c_float(float(f))))
+
+
+def num_blocks(n: int, bs: int) -> int:
+    return (n + bs - 1) // bs
+
+
+def quantize(w_bf16: np.ndarray, blocksize: int = 64, quant_type="nf4"):
+    """Blockwise quantize a flattened bf16 tensor. Returns (packed uint8[ceil(n/2)],
+    absmax float32[ceil(n/bs)])."""
+    w = np.ascontiguousarray(w_bf16.reshape(-1), dtype=np.uint16)
+    n = w.size
+    packed = np.zeros((n + 1) // 2, dtype=np.uint8)
+    absmax = np.zeros(num_blocks(n, blocksize), dtype=np.float32)
+    _check(_load().orc_quantize(_ptr(w), n, blocksize, _qt(quant_type), _ptr(packed), _ptr(absmax)),
+           "quantize")
+    return packed, absmax
+
+
+def double_quant(absmax: np.ndarray, blocksize2: int = 256):
+    """Quantize fp32 block scales to int8 with one fp32 scale per group.
+    Returns (q int8[nb], s2 float32[ceil(nb/bs2)])."""
+    a = np.ascontiguousarray(absmax.reshape(-1), dtype=np.float32)
+    nb = a.size
+    q = np.zeros(nb, dtype=np.int8)
+    s2 = np.zeros(num_blocks(nb, blocksize2), dtype=np.float32)
+    _check(_load().orc_double_quant(_ptr(a), nb, blocksize2, _ptr(q), _ptr(s2)), "double_quant")
+    return q, s2
+
+
+def dequantize(packed: np.ndarray, n: int, blocksize: int = 64, quant_type="nf4", absmax=None,
+               absmax_q=None, absmax_scale=None, blocksize2: int = 256):
+    """Dequantize. Returns (fp32[n], bf16 bit patterns uint16[n])."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    out32 = np.zeros(n, dtype=np.float32)
+    out16 = np.zeros(n, dtype=np.uint16)
+    a = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if absmax_q is None else np.ascontiguousarray(absmax_q, dtype=np.int8)
+    s2 = None if absmax_scale is None else np.ascontiguousarray(absmax_scale, dtype=np.float32)
+    _check(_load().orc_dequantize(_ptr(p), n, blocksize, _qt(quant_type), _ptr(a), _ptr(q), _ptr(s2),
+                                  blocksize2, _ptr(out32), _ptr(out16)), "dequantize")
+    return out32, out16
+
+
+def matmul_bf16(x_bf16: np.ndarray, wc_bf16: np.ndarray) -> np.ndarray:
+    """fp64 y = x @ Wc^T for bf16 x [M, K] and bf16 Wc [N, K]."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(wc_bf16, dtype=np.uint16)
+    M, K = x.shape
+    N, K2 = w.shape
+    assert K == K2
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(_load().orc_matmul_bf16(_ptr(x), _ptr(w), M, N, K, _ptr(y)), "matmul")
+    return y
+
+
+def matmul_bf16_sampled(x_bf16: np.ndarray, wc_bf16: np.ndarray, ms, ns) -> np.ndarray:
+    """fp64 y[i] = sum_k Wc[ns[i], k] * x[ms[i], k] for the listed positions."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    w = np.ascontiguousarray(wc_bf16, dtype=np.uint16)
+    K = x.shape[1]
+    assert w.shape[1] == K
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    assert ms.size == ns.size
+    assert ms.size == 0 or (ms.min() >= 0 and ms.max() < x.shape[0] and ns.min() >= 0
+                            and ns.max() < w.shape[0])
+    y = np.zeros(ms.size, dtype=np.float64)
+    _check(_load().orc_matmul_bf16_sampled(_ptr(x), _ptr(w), K, _ptr(ms), _ptr(ns), ms.size, _ptr(y)),
+           "matmul_sampled")
+    return y
+
+
+def gemv_quantized(x_bf16: np.ndarray, packed: np.ndarray, N: int, K: int, blocksize: int = 64,
+                   quant_type="nf4", absmax=None, absmax_q=None, absmax_scale=None,
+                   blocksize2: int = 256) -> np.ndarray:
+    """fp64 y [M, N] = x @ bf16(dequant(W))^T, dequantizing row by row."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    M = x.shape[0]
+    assert x.shape[1] == K
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    a = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if absmax_q is None else np.ascontiguousarray(absmax_q, dtype=np.int8)
+    s2 = None if absmax_scale is None else np.ascontiguousarray(absmax_scale, dtype=np.float32)
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(_load().orc_gemv_quantized(_ptr(x), M, _ptr(p), N, K, blocksize, _qt(quant_type), _ptr(a),
+                                      _ptr(q), _ptr(s2), blocksize2, _ptr(y)), "gemv")
+    return y
