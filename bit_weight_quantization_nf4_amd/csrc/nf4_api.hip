@@ -1,0 +1,209 @@
+// nf4_api.hip -- the extern "C" boundary of libnf4 (declared in include/nf4.h):
+// argument validation, device checks and dispatch to the kernel launchers.
+// Every check runs before the first launch, so a rejected call writes nothing.
+#include <string.h>
+
+#include <atomic>
+
+#include "../../include/nf4.h"
+#include "nf4_internal.h"
+
+using namespace nf4;
+
+namespace {
+
+bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
+  return v >= lo && v <= hi && (v & (v - 1)) == 0;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device result of the architecture check: 0 unknown, 1 ok, 2 not gfx950.
+std::atomic<int> g_arch_state[64];
+
+nf4_status check_device() {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+    (void)hipGetLastError();
+    return NF4_ERR_DEVICE;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return NF4_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return NF4_ERR_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return NF4_ERR_DEVICE;
+    st = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? NF4_OK : NF4_ERR_UNSUPPORTED;
+}
+
+nf4_status from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_DEVICE; }
+
+// Validates a quantized-tensor descriptor; fills the kernels' scale source.
+nf4_status check_qweight(const nf4_qweight *w, ScaleArgs *sc) {
+  if (w == nullptr) return NF4_ERR_INVALID_ARGUMENT;
+  if (w->n < 0) return NF4_ERR_INVALID_ARGUMENT;
+  if (w->quant_type != NF4_QUANT_NF4 && w->quant_type != NF4_QUANT_FP4)
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (!is_pow2_in(w->blocksize, 32, 4096)) return NF4_ERR_INVALID_ARGUMENT;
+  if (w->double_quant != 0 && w->double_quant != 1) return NF4_ERR_INVALID_ARGUMENT;
+  if (w->n > 0 && w->packed == nullptr) return NF4_ERR_INVALID_ARGUMENT;
+  if (w->double_quant) {
+    if (!is_pow2_in(w->blocksize2, 64, 4096)) return NF4_ERR_INVALID_ARGUMENT;
+    if (w->n > 0 && (w->absmax_q == nullptr || w->absmax_scale == nullptr))
+      return NF4_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w->absmax_q) || !aligned16(w->absmax_scale)) return NF4_ERR_MISALIGNED;
+  } else {
+    if (w->n > 0 && w->absmax == nullptr) return NF4_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w->absmax)) return NF4_ERR_MISALIGNED;
+  }
+  if (!aligned16(w->packed)) return NF4_ERR_MISALIGNED;
+  sc->absmax = w->absmax;
+  sc->absmax_q = w->absmax_q;
+  sc->absmax_scale = w->absmax_scale;
+  sc->double_quant = w->double_quant;
+  sc->log2_bs2 = w->double_quant ? __builtin_ctz((unsigned)w->blocksize2) : 0;
+  return NF4_OK;
+}
+
+nf4_status check_product(const void *x, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+                         int32_t compute_dtype, int32_t out_dtype, void *y, ScaleArgs *sc) {
+  nf4_status st = check_qweight(w, sc);
+  if (st != NF4_OK) return st;
+  if (M < 0 || N < 0 || K <= 0) return NF4_ERR_INVALID_ARGUMENT;
+  if ((int64_t)N * (int64_t)K != w->n) return NF4_ERR_INVALID_ARGUMENT;
+  if (out_dtype != NF4_DTYPE_BF16 && out_dtype != NF4_DTYPE_FP32) return NF4_ERR_INVALID_ARGUMENT;
+  if (compute_dtype != NF4_DTYPE_BF16 && compute_dtype != NF4_DTYPE_FP32)
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (compute_dtype != NF4_DTYPE_BF16) return NF4_ERR_UNSUPPORTED;
+  if (K % w->blocksize != 0) return NF4_ERR_UNSUPPORTED;
+  if (M > 0 && N > 0 && (x == nullptr || y == nullptr)) return NF4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(y)) return NF4_ERR_MISALIGNED;
+  return NF4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t nf4_abi_version(void) { return NF4_ABI_VERSION; }
+
+const char *nf4_status_string(int32_t status) {
+  switch (status) {
+    case NF4_OK:
+      return "NF4_OK";
+    case NF4_ERR_INVALID_ARGUMENT:
+      return "NF4_ERR_INVALID_ARGUMENT: null pointer, negative size, unknown enum or shape mismatch";
+    case NF4_ERR_UNSUPPORTED:
+      return "NF4_ERR_UNSUPPORTED: request not implemented by this build, or device is not gfx950";
+    case NF4_ERR_MISALIGNED:
+      return "NF4_ERR_MISALIGNED: a device pointer is not 16-byte aligned";
+    case NF4_ERR_DEVICE:
+      return "NF4_ERR_DEVICE: no HIP device, or a HIP call or kernel launch failed";
+    default:
+      return "unknown nf4 status";
+  }
+}
+
+int64_t nf4_packed_bytes(int64_t n) { return n < 0 ? -1 : (n + 1) / 2; }
+
+int64_t nf4_num_blocks(int64_t n, int32_t blocksize) {
+  if (n < 0 || blocksize <= 0) return -1;
+  return (n + blocksize - 1) / blocksize;
+}
+
+nf4_status nf4_codebook(int32_t quant_type, float values[16]) {
+  if (values == nullptr) return NF4_ERR_INVALID_ARGUMENT;
+  if (quant_type != NF4_QUANT_NF4 && quant_type != NF4_QUANT_FP4) return NF4_ERR_INVALID_ARGUMENT;
+  const CodeTables &t = code_tables(quant_type);
+  memcpy(values, t.value, sizeof t.value);
+  return NF4_OK;
+}
+
+nf4_status nf4_device_check(void) { return check_device(); }
+
+nf4_status nf4_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_t quant_type,
+                        int32_t double_quant, uint8_t *packed, float *absmax, int8_t *absmax_q,
+                        float *absmax_scale, void *stream) {
+  if (n < 0) return NF4_ERR_INVALID_ARGUMENT;
+  if (quant_type != NF4_QUANT_NF4 && quant_type != NF4_QUANT_FP4) return NF4_ERR_INVALID_ARGUMENT;
+  if (!is_pow2_in(blocksize, 32, 4096)) return NF4_ERR_INVALID_ARGUMENT;
+  if (double_quant != 0 && double_quant != 1) return NF4_ERR_INVALID_ARGUMENT;
+  if (n > 0 && (w_bf16 == nullptr || packed == nullptr || absmax == nullptr))
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (double_quant && n > 0 && (absmax_q == nullptr || absmax_scale == nullptr))
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(w_bf16) || !aligned16(packed) || !aligned16(absmax)) return NF4_ERR_MISALIGNED;
+  if (double_quant && (!aligned16(absmax_q) || !aligned16(absmax_scale))) return NF4_ERR_MISALIGNED;
+  if (n == 0) return NF4_OK;
+  nf4_status st = check_device();
+  if (st != NF4_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = from_hip(launch_quantize(static_cast<const uint16_t *>(w_bf16), n, blocksize, quant_type,
+                                packed, absmax, s));
+  if (st != NF4_OK || !double_quant) return st;
+  const int64_t nb = (n + blocksize - 1) / blocksize;
+  return from_hip(launch_double_quant(absmax, nb, 256, absmax_q, absmax_scale, s));
+}
+
+nf4_status nf4_double_quant(const float *absmax, int64_t nb, int32_t blocksize2, int8_t *absmax_q,
+                            float *absmax_scale, void *stream) {
+  if (nb < 0) return NF4_ERR_INVALID_ARGUMENT;
+  if (!is_pow2_in(blocksize2, 64, 4096)) return NF4_ERR_INVALID_ARGUMENT;
+  if (nb > 0 && (absmax == nullptr || absmax_q == nullptr || absmax_scale == nullptr))
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(absmax) || !aligned16(absmax_q) || !aligned16(absmax_scale))
+    return NF4_ERR_MISALIGNED;
+  if (nb == 0) return NF4_OK;
+  nf4_status st = check_device();
+  if (st != NF4_OK) return st;
+  return from_hip(launch_double_quant(absmax, nb, blocksize2, absmax_q, absmax_scale,
+                                      reinterpret_cast<hipStream_t>(stream)));
+}
+
+nf4_status nf4_dequantize(const nf4_qweight *w, int32_t out_dtype, void *out, void *stream) {
+  ScaleArgs sc;
+  nf4_status st = check_qweight(w, &sc);
+  if (st != NF4_OK) return st;
+  if (out_dtype != NF4_DTYPE_BF16 && out_dtype != NF4_DTYPE_FP32) return NF4_ERR_INVALID_ARGUMENT;
+  if (w->n > 0 && out == nullptr) return NF4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out)) return NF4_ERR_MISALIGNED;
+  if (w->n == 0) return NF4_OK;
+  st = check_device();
+  if (st != NF4_OK) return st;
+  return from_hip(launch_dequantize(w->packed, w->n, w->blocksize, w->quant_type, sc,
+                                    out_dtype == NF4_DTYPE_BF16, out,
+                                    reinterpret_cast<hipStream_t>(stream)));
+}
+
+nf4_status nf4_gemv(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+                    int32_t compute_dtype, int32_t out_dtype, void *y, void *stream) {
+  ScaleArgs sc;
+  nf4_status st = check_product(x_bf16, M, w, N, K, compute_dtype, out_dtype, y, &sc);
+  if (st != NF4_OK) return st;
+  if (M > 16) return NF4_ERR_INVALID_ARGUMENT;
+  if (M == 0 || N == 0) return NF4_OK;
+  st = check_device();
+  if (st != NF4_OK) return st;
+  return from_hip(launch_gemv(static_cast<const uint16_t *>(x_bf16), M, w->packed, N, K,
+                              w->blocksize, w->quant_type, sc, out_dtype == NF4_DTYPE_BF16, y,
+                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+                    int32_t compute_dtype, int32_t out_dtype, void *y, void *stream) {
+  ScaleArgs sc;
+  nf4_status st = check_product(x_bf16, M, w, N, K, compute_dtype, out_dtype, y, &sc);
+  if (st != NF4_OK) return st;
+  if (M == 0 || N == 0) return NF4_OK;
+  st = check_device();
+  if (st != NF4_OK) return st;
+  return from_hip(launch_gemm(static_cast<const uint16_t *>(x_bf16), M, w->packed, N, K,
+                              w->blocksize, w->quant_type, sc, out_dtype == NF4_DTYPE_BF16, y,
+                              reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,29 @@
+// nf4_internal.h -- host-side interface between the C ABI layer (nf4_api.hip)
+// and the kernel launchers. Launchers assume validated arguments.
+#pragma once
+
+#include "nf4_common.h"
+
+namespace nf4 {
+
+// Tables for NF4 / FP4, derived on first use (nf4_tables.hip).
+const CodeTables &code_tables(int quant_type);
+
+hipError_t launch_quantize(const uint16_t *w, int64_t n, int blocksize, int quant_type,
+                           uint8_t *packed, float *absmax, hipStream_t stream);
+
+hipError_t launch_double_quant(const float *absmax, int64_t nb, int blocksize2, int8_t *q,
+                               float *s2, hipStream_t stream);
+
+hipError_t launch_dequantize(const uint8_t *packed, int64_t n, int blocksize, int quant_type,
+                             const ScaleArgs &sc, bool out_bf16, void *out, hipStream_t stream);
+
+hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
+                       int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
+                       void *y, hipStream_t stream);
+
+hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
+                       int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
+                       void *y, hipStream_t stream);
+
+}  // namespace nf4

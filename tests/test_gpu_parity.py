@@ -1,0 +1,325 @@
+"""GPU parity: the HIP path (through the C ABI via the thin binding) against the
+CPU oracle on the same seeded inputs.
+
+Bar: packed codes, absmax, double-quant bytes and dequantized fp32/bf16 values
+bit-exact; products in fp32 within relative L2 <= 1e-4 and, per element,
+|y - y_ref| <= 1e-3 * ||W_c[n, :]|| * ||x[m, :]|| against the fp64 oracle; the
+bf16-output run equal to RNE of the fp32-output run; repeated runs bitwise
+identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from workloads import to_u16
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 1e-4
+PER_ELEM = 1e-3
+
+
+@pytest.fixture(scope="module")
+def nf4():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import bit_weight_quantization_nf4_amd as m
+
+    assert m.lib().nf4_device_check() == 0, "device is not gfx950"
+    return m
+
+
+def dev(t):
+    return t.to("cuda")
+
+
+def u16_to_f64(a):
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def check_quant(nf4, orc, w_cpu, bs, qt, dq):
+    """Quantize on GPU and oracle; assert bit-exact outputs. Returns both."""
+    qs = nf4.quantize(dev(w_cpu), bs, qt, double_quant=dq)
+    w16 = to_u16(w_cpu.reshape(-1))
+    p_ref, a_ref = orc.quantize(w16, bs, qt)
+    p = qs.packed.cpu().numpy()
+    a = qs.absmax.cpu().numpy()
+    assert np.array_equal(p, p_ref), f"packed codes differ ({np.sum(p != p_ref)} bytes)"
+    assert np.array_equal(a.view(np.uint32), a_ref.view(np.uint32)), "absmax differs"
+    ref = dict(packed=p_ref, absmax=a_ref)
+    if dq:
+        q_ref, s_ref = orc.double_quant(a_ref, 256)
+        assert np.array_equal(qs.absmax_q.cpu().numpy(), q_ref), "absmax_q differs"
+        assert np.array_equal(qs.absmax_scale.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+        ref.update(absmax_q=q_ref, absmax_scale=s_ref)
+    return qs, ref
+
+
+def oracle_scales(ref, dq):
+    if dq:
+        return dict(absmax_q=ref["absmax_q"], absmax_scale=ref["absmax_scale"])
+    return dict(absmax=ref["absmax"])
+
+
+def check_dequant(nf4, orc, qs, ref, bs, qt, dq):
+    n = qs.n
+    w32_ref, w16_ref = orc.dequantize(ref["packed"], n, bs, qt, **oracle_scales(ref, dq))
+    w32 = nf4.dequantize(qs, torch.float32).reshape(-1).cpu().numpy()
+    w16 = to_u16(nf4.dequantize(qs, torch.bfloat16).reshape(-1).cpu())
+    assert np.array_equal(w32.view(np.uint32), w32_ref.view(np.uint32)), "fp32 dequant differs"
+    assert np.array_equal(w16, w16_ref), "bf16 dequant differs"
+    return w16_ref
+
+
+def check_product(y32, y16, ref, wc16, x16):
+    """Tolerance bar against the fp64 oracle plus bf16 == RNE(fp32)."""
+    y = y32.cpu().numpy().astype(np.float64)
+    err = np.abs(y - ref)
+    rel = np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= REL_L2, f"relative L2 error {rel:.3e}"
+    wn = np.linalg.norm(u16_to_f64(wc16), axis=1)
+    xn = np.linalg.norm(u16_to_f64(x16), axis=1)
+    bound = PER_ELEM * np.outer(xn, wn)
+    assert np.all(err <= bound + 1e-30), f"max err/bound {np.max(err / (bound + 1e-30)):.3e}"
+    if y16 is not None:
+        assert torch.equal(y16.cpu().view(torch.int16), y32.to(torch.bfloat16).cpu().view(torch.int16))
+    return rel
+
+
+# ----------------------------------------------------------------- quantize
+
+
+@pytest.mark.parametrize("cfg", [workloads.TINY, workloads.SQUARE_OUTLIERS], ids=lambda c: c.name)
+def test_quantize_dequant_small_configs(nf4, orc, cfg):
+    m = cfg.matrices[0]
+    w = m.make()
+    for bs in cfg.blocksizes:
+        qs, ref = check_quant(nf4, orc, w, bs, "nf4", cfg.double_quant)
+        check_dequant(nf4, orc, qs, ref, bs, "nf4", cfg.double_quant)
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_quantize_dequant_mlp_config(nf4, orc, qt):
+    for m in workloads.MLP.matrices:
+        w = m.make()
+        qs, ref = check_quant(nf4, orc, w, 64, qt, True)
+        check_dequant(nf4, orc, qs, ref, 64, qt, True)
+
+
+def _all_bf16_classes():
+    a_bits = (0x3F80 | np.arange(128)).astype(np.uint16)
+    allx = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    xf = (allx.astype(np.uint32) << 16).view(np.float32)
+    blocks = []
+    for ab in a_bits:
+        af = (np.array([ab], np.uint32) << 16).view(np.float32)[0]
+        xs = allx[np.isfinite(xf) & (np.abs(xf) <= af)]
+        xs = np.concatenate([xs, np.zeros((-len(xs)) % 63, np.uint16)]).reshape(-1, 63)
+        blocks.append(np.concatenate([np.full((xs.shape[0], 1), ab, np.uint16), xs], axis=1))
+    return np.concatenate(blocks).reshape(-1)
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_quantize_every_bf16_class(nf4, orc, qt):
+    """Every normal (x, a) significand/exponent class: the kernel's reciprocal
+    normalisation and cell lookup give the oracle's codes everywhere."""
+    w = workloads.from_u16(_all_bf16_classes())
+    check_quant(nf4, orc, w, 64, qt, False)
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_quantize_extreme_scales(nf4, orc, qt):
+    """Blocks whose absmax sits at or beyond the fast-path range, including
+    bf16 subnormals and the largest finite values, plus all-zero blocks."""
+    base = workloads.normal_bf16((40, 64), 1.0, 77).float().clamp(-3.5, 3.5)
+    scales = [2.0 ** e for e in (-140, -133, -126, -110, -101, -100, -99, -60, 0, 60, 100,
+                                 119, 120, 121, 125)]
+    rows = [to_u16((base[i % 40] * s).to(torch.bfloat16)) for i, s in enumerate(scales)]
+    rows.append(np.zeros(64, np.uint16))
+    rows.append(np.full(64, 0x7F7F, np.uint16))  # largest finite bf16
+    rows.append(np.concatenate([np.full(32, 0xFF7F, np.uint16), np.full(32, 0x7E96, np.uint16)]))
+    rows.append(np.arange(1, 65, dtype=np.uint16))  # bf16 subnormals only
+    w = workloads.from_u16(np.stack(rows))
+    assert torch.isfinite(w.float()).all()
+    check_quant(nf4, orc, w, 64, qt, True)
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128, 256, 512, 1024, 2048, 4096])
+def test_quantize_blocksizes_and_ragged_lengths(nf4, orc, bs):
+    for n in (3 * bs + 517, 2 * bs, bs - 8, 1, 2, 7, 9, 17, 63, 65, 513):
+        if n <= 0:
+            continue
+        w = workloads.normal_bf16((n,), 0.02, 1000 + n)
+        for qt in ("nf4", "fp4"):
+            qs, ref = check_quant(nf4, orc, w, bs, qt, n > 300)
+            check_dequant(nf4, orc, qs, ref, bs, qt, n > 300)
+
+
+def test_quantize_empty(nf4):
+    qs = nf4.quantize(torch.empty(0, dtype=torch.bfloat16, device="cuda"), 64, "nf4", True)
+    assert qs.packed.numel() == 0 and qs.absmax.numel() == 0
+
+
+# ------------------------------------------------------------- double quant
+
+
+@pytest.mark.parametrize("bs2", [64, 128, 256, 512, 1024, 2048, 4096])
+def test_double_quant(nf4, orc, bs2):
+    rng = np.random.default_rng(bs2)
+    for nb in (1, 3, bs2 - 1, bs2, bs2 + 1, 5 * bs2 + 37):
+        a = (np.abs(rng.standard_normal(nb)) * 0.05).astype(np.float32)
+        if nb > 2 * bs2:
+            a[bs2:2 * bs2] = 0  # an all-zero group
+        q, s2 = nf4.double_quant(torch.from_numpy(a).cuda(), bs2)
+        q_ref, s_ref = orc.double_quant(a, bs2)
+        assert np.array_equal(q.cpu().numpy(), q_ref)
+        assert np.array_equal(s2.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_double_quant_ties(nf4, orc):
+    a = np.array([127.0, 62.5, 63.5, 0.5, 1.5, 2.5, 1.0, 0.25] * 40, np.float32)
+    q, s2 = nf4.double_quant(torch.from_numpy(a).cuda(), 256)
+    q_ref, s_ref = orc.double_quant(a, 256)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert q_ref[1] == 62 and q_ref[2] == 64
+
+
+# ------------------------------------------------------------------ dequant
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_dequant_every_code_and_bf16_scale(nf4, orc, qt):
+    """All 16 codes times every finite non-negative bf16 absmax (fp32 and bf16
+    outputs, bit-exact), through the plain-absmax path."""
+    a = (np.arange(0x7F80, dtype=np.uint32) << 16).view(np.float32)
+    nb = a.size
+    codes = (np.arange(nb * 64) * 7 + np.arange(nb * 64) // 64) % 16
+    packed = ((codes[0::2] << 4) | codes[1::2]).astype(np.uint8)
+    qs = nf4.QuantState(torch.from_numpy(packed).cuda(), torch.from_numpy(a).cuda(), None, None,
+                        (nb * 64,), 64, qt, False)
+    ref = dict(packed=packed, absmax=a)
+    check_dequant(nf4, orc, qs, ref, 64, qt, False)
+
+
+# ---------------------------------------------------------------- products
+
+
+def _gemv_case(nf4, orc, w_cpu, x_cpu, bs, qt, dq, check_quantize=True):
+    N, K = w_cpu.shape
+    qs, ref = check_quant(nf4, orc, w_cpu, bs, qt, dq)
+    w32_ref, wc16 = orc.dequantize(ref["packed"], N * K, bs, qt, **oracle_scales(ref, dq))
+    x16 = to_u16(x_cpu)
+    y_ref = orc.matmul_bf16(x16, wc16.reshape(N, K))
+    xd = dev(x_cpu)
+    y32 = nf4.gemv(xd, qs, torch.float32)
+    y16 = nf4.gemv(xd, qs, torch.bfloat16)
+    rel = check_product(y32, y16, y_ref, wc16.reshape(N, K), x16)
+    assert torch.equal(nf4.gemv(xd, qs, torch.float32), y32), "GEMV is not deterministic"
+    return rel
+
+
+@pytest.mark.parametrize("cfg", [workloads.TINY, workloads.SQUARE_OUTLIERS], ids=lambda c: c.name)
+def test_gemv_small_configs(nf4, orc, cfg):
+    m = cfg.matrices[0]
+    _gemv_case(nf4, orc, m.make(), cfg.activations(m.cols, 1), 64, "nf4", cfg.double_quant)
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+@pytest.mark.parametrize("which", [0, 1], ids=["up-11008x4096", "down-4096x11008"])
+def test_gemv_mlp_config(nf4, orc, qt, which):
+    """Batched decode M in {1, 4, 8, 16}: the oracle runs once on 16 rows and
+    each M uses the leading rows."""
+    m = workloads.MLP.matrices[which]
+    w = m.make()
+    N, K = w.shape
+    qs, ref = check_quant(nf4, orc, w, 64, qt, True)
+    _, wc16 = orc.dequantize(ref["packed"], N * K, 64, qt, **oracle_scales(ref, True))
+    wc16 = wc16.reshape(N, K)
+    x = workloads.MLP.activations(K, 16)
+    x16 = to_u16(x)
+    y_ref = orc.matmul_bf16(x16, wc16)
+    for M in workloads.MLP.ms:
+        xd = dev(x[:M])
+        y32 = nf4.gemv(xd, qs, torch.float32)
+        y16 = nf4.gemv(xd, qs, torch.bfloat16)
+        check_product(y32, y16, y_ref[:M], wc16, x16[:M])
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemv_ragged_shapes(nf4, orc, bs, dq):
+    for (N, K, M) in [(1, bs, 1), (15, 2 * bs, 3), (17, 160 if bs == 32 else 5 * bs, 16),
+                      (33, 4128 if bs == 32 else 33 * bs, 2), (100, 3 * bs, 7)]:
+        w = workloads.normal_bf16((N, K), 0.02, N * 31 + K)
+        x = workloads.normal_bf16((M, K), 1.0, N + K + M)
+        _gemv_case(nf4, orc, w, x, bs, "nf4", dq)
+
+
+def test_gemm_small_shapes(nf4, orc):
+    for (M, N, K, bs, dq, qt) in [(1, 64, 64, 64, False, "nf4"), (5, 130, 256, 64, True, "nf4"),
+                                  (128, 128, 128, 64, True, "fp4"), (130, 257, 96, 32, False, "nf4"),
+                                  (300, 200, 512, 128, True, "nf4"), (64, 1, 64, 64, False, "fp4")]:
+        w = workloads.normal_bf16((N, K), 0.02, M + N + K)
+        x = workloads.normal_bf16((M, K), 1.0, M * N + K)
+        qs, ref = check_quant(nf4, orc, w, bs, qt, dq)
+        _, wc16 = orc.dequantize(ref["packed"], N * K, bs, qt, **oracle_scales(ref, dq))
+        x16 = to_u16(x)
+        y_ref = orc.matmul_bf16(x16, wc16.reshape(N, K))
+        xd = dev(x)
+        y32 = nf4.gemm(xd, qs, torch.float32)
+        y16 = nf4.gemm(xd, qs, torch.bfloat16)
+        check_product(y32, y16, y_ref, wc16.reshape(N, K), x16)
+
+
+def test_gemm_prefill_config(nf4, orc):
+    """Full prefill shape 2048 x 4096 x 14336, NF4 bs64 + double quant:
+    quantize bit-exact; 4096 sampled outputs against the fp64 oracle; all
+    outputs: bf16 == RNE(fp32), determinism, and the first 16 rows against the
+    (separately parity-tested) GEMV kernel."""
+    cfg = workloads.PREFILL
+    m = cfg.matrices[0]
+    w = m.make()
+    N, K = w.shape
+    M = cfg.ms[0]
+    qs, ref = check_quant(nf4, orc, w, 64, "nf4", True)
+    _, wc16 = orc.dequantize(ref["packed"], N * K, 64, "nf4", **oracle_scales(ref, True))
+    wc16 = wc16.reshape(N, K)
+    x = cfg.activations(K, M)
+    x16 = to_u16(x)
+    xd = dev(x)
+    y32 = nf4.gemm(xd, qs, torch.float32)
+    y16 = nf4.gemm(xd, qs, torch.bfloat16)
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(nf4.gemm(xd, qs, torch.float32), y32), "GEMM is not deterministic"
+    rng = np.random.default_rng(5)
+    ms = rng.integers(0, M, 4096)
+    ns = rng.integers(0, N, 4096)
+    ms[:4] = [0, M - 1, 0, M - 1]
+    ns[:4] = [0, 0, N - 1, N - 1]
+    ys_ref = orc.matmul_bf16_sampled(x16, wc16, ms, ns)
+    ys = y32.cpu().numpy().astype(np.float64)[ms, ns]
+    bound = PER_ELEM * np.linalg.norm(u16_to_f64(wc16)[ns], axis=1) * np.linalg.norm(
+        u16_to_f64(x16)[ms], axis=1)
+    assert np.all(np.abs(ys - ys_ref) <= bound)
+    assert np.linalg.norm(ys - ys_ref) / np.linalg.norm(ys_ref) <= REL_L2
+    yv = nf4.gemv(xd[:16], qs, torch.float32)
+    diff = (yv - y32[:16]).abs()
+    assert torch.all(diff <= 1e-4 * (y32[:16].abs() + yv.abs()) + 1e-3)
+
+
+@pytest.mark.parametrize("bs", [64, 128, 256])
+def test_stack7b_sampled_matrices(nf4, orc, bs):
+    """7B-shaped stack at each blocksize: first and last layer's q-shaped and
+    mlp-shaped matrices, quantize + double quant + dequant bit-exact and the
+    M=1 GEMV within tolerance."""
+    mats = workloads.STACK_7B.matrices
+    for mat in (mats[0], mats[4], mats[-1]):
+        w = mat.make()
+        N, K = w.shape
+        qs, ref = check_quant(nf4, orc, w, bs, "nf4", True)
+        wc16 = check_dequant(nf4, orc, qs, ref, bs, "nf4", True).reshape(N, K)
+        x = workloads.normal_bf16((1, K), 1.0, mat.seed + 1000)
+        x16 = to_u16(x)
+        y_ref = orc.matmul_bf16(x16, wc16)
+        y32 = nf4.gemv(dev(x), qs, torch.float32)
+        check_product(y32, None, y_ref, wc16, x16)
