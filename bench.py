@@ -1,0 +1,279 @@
+"""Benchmark of the NF4 hot path on one MI355X.
+
+One step = one pass of the whole path over the 7B-shaped stack (32 layers x
+(4 x [4096, 4096] + 3 x [11008, 4096]) bf16 weights, N(0, 0.02^2), NF4 with
+double quantization at blocksize 64 by default):
+  1. quantize + double-quant every weight (and the prefill weight),
+  2. dequantize every weight to bf16,
+  3. decode GEMV (M = 1, independent seeded x per matrix) through every weight,
+  4. one prefill GEMM, X[2048, 4096] . W[14336, 4096]^T (NF4 bs 64 + double
+     quant, fp32 accumulation, bf16 output).
+Inputs are generated on the GPU from seeded generators and are resident in HBM
+before timing. Each phase is captured once in a HIP graph and replayed, so
+host launch overhead is not measured; HIP events between phases give per-phase
+device time.
+
+Prints ONE JSON line. `value` is the effective bandwidth of the decode GEMV
+(algorithmic bytes: 4-bit codes + 8-bit scales + per-group fp32 scales + x + y,
+divided by GEMV device time). The GEMM's TFLOP/s and each phase's own figures
+are reported next to it, with roofline fractions against MI355X peaks (HBM
+8 TB/s, dense bf16 MFMA 2.5 PFLOP/s). `cpu_baseline` times the CPU oracle on a
+bounded sample of the same workload (test infrastructure, single thread).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--bs", type=int, default=64, choices=[32, 64, 128, 256, 512, 1024, 2048, 4096])
+    ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample (0 disables it)")
+    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemm")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_weight_quantization_nf4_amd as nf4
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if nf4.lib().nf4_device_check() != 0:
+        raise RuntimeError("device 0 is not gfx950")
+    dev = torch.device("cuda", 0)
+    bs = args.bs
+    phases = args.phases.split(",")
+
+    stack = workloads.stack_7b(args.layers)
+    prefill = workloads.PREFILL
+
+    def gpu_normal(shape, sigma, seed):
+        g = torch.Generator(device=dev).manual_seed(seed)
+        t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        if sigma != 1.0:
+            t.mul_(sigma)
+        return t.to(torch.bfloat16)
+
+    # ---- resident inputs and preallocated outputs
+    mats = []
+    for m in stack.matrices:
+        w = gpu_normal((m.rows, m.cols), m.sigma, m.seed)
+        x = gpu_normal((1, m.cols), 1.0, m.seed + 1000)
+        qs = nf4.quantize(w, bs, "nf4", double_quant=True)
+        mats.append(dict(spec=m, w=w, x=x, qs=qs,
+                         wd=torch.empty_like(w),
+                         y=torch.empty((1, m.rows), dtype=torch.float32, device=dev)))
+    pm = prefill.matrices[0]
+    pw = gpu_normal((pm.rows, pm.cols), pm.sigma, pm.seed)
+    px = gpu_normal((prefill.ms[0], pm.cols), 1.0, prefill.x_seed)
+    pqs = nf4.quantize(pw, 64, "nf4", double_quant=True)
+    py = torch.empty((prefill.ms[0], pm.rows), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def ph_quantize():
+        for d in mats:
+            nf4.quantize(d["w"], bs, "nf4", True, out=d["qs"])
+        nf4.quantize(pw, 64, "nf4", True, out=pqs)
+
+    def ph_dequantize():
+        for d in mats:
+            nf4.dequantize(d["qs"], out=d["wd"])
+
+    # decode GEMV: the seven independent products of a layer share one launch
+    layers = [mats[i:i + 7] for i in range(0, len(mats), 7)]
+
+    def ph_gemv():
+        for grp in layers:
+            nf4.gemv_grouped([d["x"] for d in grp], [d["qs"] for d in grp],
+                             outs=[d["y"] for d in grp])
+
+    def ph_gemm():
+        nf4.gemm(px, pqs, out=py)
+
+    fns = dict(quantize=ph_quantize, dequantize=ph_dequantize, gemv=ph_gemv, gemm=ph_gemm)
+
+    # ---- capture each phase in a graph (after an eager warm-up call)
+    graphs = {}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for p in phases:
+            fns[p]()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for p in phases:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fns[p]()
+        graphs[p] = g
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for p in phases:
+            graphs[p].replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region
+    ev = {p: [] for p in phases}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for p in phases:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            graphs[p].replay()
+            b.record()
+            ev[p].append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {p: sum(a.elapsed_time(b) for a, b in ev[p]) / args.steps for p in phases}
+
+    # ---- algorithmic work per step
+    def meta_bytes(n, blocksize):
+        nb = -(-n // blocksize)
+        return nb + 4 * (-(-nb // 256))  # int8 scale per block + fp32 per 256 blocks
+
+    n_stack = sum(d["spec"].rows * d["spec"].cols for d in mats)
+    n_pre = pm.rows * pm.cols
+    work = {}
+    # quantize: read bf16, write codes + fp32 absmax; double quant: read absmax, write int8 + fp32
+    qbytes = 0
+    qlaunches = 0
+    for n, b in [(d["spec"].rows * d["spec"].cols, bs) for d in mats] + [(n_pre, 64)]:
+        nb = -(-n // b)
+        qbytes += 2 * n + (n + 1) // 2 + 4 * nb + 4 * nb + nb + 4 * (-(-nb // 256))
+        qlaunches += 2
+    work["quantize"] = dict(bytes=qbytes, launches=qlaunches)
+    work["dequantize"] = dict(bytes=sum((n + 1) // 2 + meta_bytes(n, bs) + 2 * n
+                                        for n in (d["spec"].rows * d["spec"].cols for d in mats)),
+                              launches=len(mats))
+    gbytes = 0
+    for d in mats:
+        N, K = d["spec"].rows, d["spec"].cols
+        gbytes += N * K // 2 + meta_bytes(N * K, bs) + 2 * K + 4 * N
+    work["gemv"] = dict(bytes=gbytes, launches=len(layers))
+    M = prefill.ms[0]
+    work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols, launches=1)
+
+    phase_out = {}
+    for p in phases:
+        t = ms[p] / 1e3
+        w = work[p]
+        if "bytes" in w:
+            gbs = w["bytes"] / t / 1e9
+            phase_out[p] = dict(ms=round(ms[p], 4), gb_per_s=round(gbs, 1),
+                                hbm_frac=round(gbs / HBM_PEAK_GBS, 4), launches=w["launches"],
+                                algorithmic_bytes=w["bytes"])
+        else:
+            tf = w["flops"] / t / 1e12
+            phase_out[p] = dict(ms=round(ms[p], 4), tflops=round(tf, 1),
+                                mfma_frac=round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                                launches=w["launches"], flops=w["flops"])
+
+    gemv_gbs = phase_out.get("gemv", {}).get("gb_per_s")
+    result = {
+        "metric": "NF4 GEMV effective GB/s (% of HBM peak); NF4 GEMM TFLOP/s (% MFMA peak)",
+        "value": gemv_gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 0.02^2) bf16 weights, N(0, 1) bf16 activations, on-GPU generators)",
+        "config": {
+            "workload": f"7B-shaped stack: {args.layers} layers x (4 x [4096,4096] + 3 x "
+                        f"[11008,4096]) NF4 bs{bs} + double quant (256); decode GEMV M=1 per "
+                        "matrix (the 7 products of a layer in one grouped launch); + prefill GEMM 2048x4096x14336 NF4 bs64 + double quant",
+            "blocksize": bs, "quant_type": "nf4", "double_quant": True,
+            "stack_params": n_stack, "gemv_m": 1, "gemm_mnk": [M, pm.rows, pm.cols],
+        },
+    }
+    if "gemv" in phase_out:
+        g = phase_out["gemv"]
+        result["roofline"] = {
+            "kernel": "gemv_kernel (NF4 decode GEMV, M=1, one launch per layer of 7 products)",
+            "bound": "hbm", "achieved": g["gb_per_s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": g["hbm_frac"], "traffic": None,
+            "per_launch_us": round(ms["gemv"] * 1e3 / work["gemv"]["launches"], 3),
+            "algorithmic_bytes_per_launch": work["gemv"]["bytes"] / work["gemv"]["launches"],
+        }
+    if "gemm" in phase_out:
+        g = phase_out["gemm"]
+        result["roofline_gemm"] = {
+            "kernel": "gemm_kernel (NF4 prefill GEMM)", "bound": "mfma", "achieved": g["tflops"],
+            "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": g["mfma_frac"],
+            "traffic": None,
+        }
+    result["phases"] = phase_out
+
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(mats, bs, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(mats, bs, target_s):
+    """The CPU oracle's decode GEMV on a bounded sample of the same workload: it
+    quantizes the sampled weights itself (from the same bf16 inputs), then its
+    timed leg is the GEMV, matrix by matrix until ~target_s seconds of work.
+    Its result is also compared with the GPU's y for those matrices."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    oracle.build(force=False)
+    done_bytes, done_s, count, worst = 0, 0.0, 0, 0.0
+    for d in mats:
+        N, K = d["spec"].rows, d["spec"].cols
+        w16 = workloads.to_u16(d["w"].cpu().reshape(-1))
+        x16 = workloads.to_u16(d["x"].cpu())
+        p, a = oracle.quantize(w16, bs, "nf4")
+        q, s2 = oracle.double_quant(a, 256)
+        t = time.perf_counter()
+        y = oracle.gemv_quantized(x16, p, N, K, bs, "nf4", absmax_q=q, absmax_scale=s2)
+        done_s += time.perf_counter() - t
+        nb = -(-(N * K) // bs)
+        done_bytes += N * K // 2 + nb + 4 * (-(-nb // 256)) + 2 * K + 4 * N
+        yg = d["y"].cpu().numpy().astype(np.float64)
+        worst = max(worst, float(np.linalg.norm(yg - y) / np.linalg.norm(y)))
+        count += 1
+        if done_s >= target_s:
+            break
+    return {
+        "value": round(done_bytes / done_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"oracle decode GEMV (M=1, fp64 sums) over the first {count} matrices of the "
+                  f"stack ({done_bytes / 1e6:.1f} MB algorithmic), {done_s:.1f} s single-threaded; "
+                  f"GPU y vs oracle y rel-L2 max {worst:.2e}",
+    }
+
+
+if __name__ == "__main__":
+    main()

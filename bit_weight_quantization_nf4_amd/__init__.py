@@ -70,6 +70,10 @@ _SIGNATURES = [
     ("nf4_gemv", ctypes.c_int32,
      [_P, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    ("nf4_gemv_grouped", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.POINTER(QWeightDesc),
+      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+      ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p), _P]),
     ("nf4_gemm", ctypes.c_int32,
      [_P, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, _P, _P]),
@@ -250,6 +254,42 @@ def gemv(x: torch.Tensor, qs: QuantState, out_dtype=torch.float32, out=None) -> 
     return _product(lib().nf4_gemv, "nf4_gemv", x, qs, out_dtype, out)
 
 
+GEMV_MAX_GROUP = 16
+
+
+def gemv_grouped(xs, qss, out_dtype=torch.float32, outs=None):
+    """nf4_gemv_grouped: several independent decode products in one launch.
+    xs[i] is [M, K_i] bf16 (same M for all), qss[i] the quantized [N_i, K_i]
+    weight. Returns the list of y_i [M, N_i]."""
+    count = len(xs)
+    if count != len(qss) or count > GEMV_MAX_GROUP:
+        raise ValueError("gemv_grouped takes matching lists of at most 16 problems")
+    if count == 0:
+        return []
+    xs2, ys, descs, Ns, Ks = [], [], [], [], []
+    for i, (x, qs) in enumerate(zip(xs, qss)):
+        if x.dtype != torch.bfloat16 or not x.is_cuda or len(qs.shape) != 2:
+            raise TypeError("gemv_grouped expects bf16 GPU activations and [N, K] weights")
+        N, K = (int(v) for v in qs.shape)
+        x2 = _dev(x.reshape(-1, K))
+        y = outs[i] if outs is not None else torch.empty((x2.shape[0], N), dtype=out_dtype,
+                                                         device=x.device)
+        xs2.append(x2)
+        ys.append(y)
+        descs.append(qs.desc())
+        Ns.append(N)
+        Ks.append(K)
+    M = xs2[0].shape[0]
+    Xarr = (ctypes.c_void_p * count)(*[t.data_ptr() for t in xs2])
+    Yarr = (ctypes.c_void_p * count)(*[t.data_ptr() for t in ys])
+    Darr = (QWeightDesc * count)(*descs)
+    Narr = (ctypes.c_int32 * count)(*Ns)
+    Karr = (ctypes.c_int32 * count)(*Ks)
+    _check(lib().nf4_gemv_grouped(count, Xarr, M, Darr, Narr, Karr, DTYPE_BF16, _DT[ys[0].dtype],
+                                  Yarr, _stream(xs2[0])), "nf4_gemv_grouped")
+    return ys
+
+
 def gemm(x: torch.Tensor, qs: QuantState, out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
     """nf4_gemm: y[M, N] = x[M, K] . bf16(W)^T for any M."""
     return _product(lib().nf4_gemm, "nf4_gemm", x, qs, out_dtype, out)
@@ -257,5 +297,5 @@ def gemm(x: torch.Tensor, qs: QuantState, out_dtype=torch.bfloat16, out=None) ->
 
 __all__ = [
     "QuantState", "QWeightDesc", "Nf4Error", "lib", "exported_names", "codebook", "packed_bytes",
-    "num_blocks", "quantize", "double_quant", "dequantize", "gemv", "gemm",
+    "num_blocks", "quantize", "double_quant", "dequantize", "gemv", "gemv_grouped", "gemm",
 ]

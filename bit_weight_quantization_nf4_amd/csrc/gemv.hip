@@ -1,5 +1,6 @@
-// gemv.hip -- decode product y[M, N] = x[M, K] . bf16(dequant(W))[N, K]^T for
-// 1 <= M <= 16, on gfx950 matrix cores.
+// gemv.hip -- decode products y_i[M, N_i] = x_i[M, K_i] . bf16(dequant(W_i))^T
+// for 1 <= M <= 16, one or several independent problems per launch, on gfx950
+// matrix cores.
 //
 // [repo page ossradar.top bitsandbytes, release notes 0.50.0: 4-bit inference
 //  at batch 1 uses a 4-bit GEMV, batches 2..64 a fused 4-bit dequantize + GEMM
@@ -7,21 +8,26 @@
 //  "Configuration": weights are dequantized to the bf16 compute dtype before
 //  the product.]
 //
-// Design (memory-bound: the 4-bit weights are read once, x is tiny):
-//  - one workgroup = 8 waves over 16*NG weight rows; the waves split K and
-//    their partial sums are added in a fixed order through LDS, so results are
-//    bitwise reproducible without atomics;
+// Design (HBM-bound: every 4-bit weight is read once; x is tiny):
+//  - work items are (problem, group of 16*NG weight rows); persistent
+//    workgroups of 8 waves walk the item list, so several small products (the
+//    projections of one layer) share one launch and the machine stays full;
+//  - inside an item the 8 waves split K; their partial sums are added in a
+//    fixed order through LDS, so results are bitwise reproducible;
 //  - the contraction runs on v_mfma_f32_16x16x32_bf16 with x as the A operand
-//    (rows m >= M are zero) and the dequantized weights as the B operand.
-//    Lane (n, kg) of the B operand needs 8 consecutive k of weight row n,
-//    i.e. exactly one 32-bit word of packed codes; each lane loads 16 bytes =
-//    32 codes (k-range 32kg..32kg+31 of a 128-wide chunk) and feeds four MFMAs.
-//    The A operand is permuted the same way, so the k order inside the chunk
-//    does not matter;
-//  - dequantization per code: one bit-field extract of 4*code from a pre-shifted
-//    word, one LDS read of the fp32 code value, one multiply by the block scale,
-//    and half a v_cvt_pk_bf16_f32 -- exactly the dequantize kernel's bf16
-//    weight, so the product is that of the bf16 compute-dtype weights.
+//    (rows m >= M only feed outputs that are never stored) and dequantized
+//    weights as the B operand. Lane (n, kg) of the B operand needs 8
+//    consecutive k of weight row n, i.e. one 32-bit word of packed codes; a
+//    lane loads 16 bytes = 32 codes and feeds four MFMAs. The A operand is
+//    permuted the same way, so the k order inside a chunk does not matter;
+//  - dequantization goes through an LDS table indexed by a whole code BYTE:
+//    entry e holds the fp32 code values of its two nibbles, so one 8-byte LDS
+//    read serves two weights. The table is stored 32 times, interleaved so
+//    that copy (lane % 32) sits in its own bank pair (entry e of copy c at
+//    byte 256*e + 8*c): lookups never conflict, and the address is the code
+//    byte moved into bits 15..8 of the lane's base by one v_perm_b32. Per two
+//    weights: 1 perm, 1 LDS read, 2 multiplies by the block scale, 1
+//    v_cvt_pk_bf16_f32 -- the same bf16 weights the dequantize kernel writes.
 #include "nf4_internal.h"
 
 namespace nf4 {
@@ -29,147 +35,248 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kChunk = 128;  // codes of one row per wave step
+constexpr int kChunk = 128;                 // codes of one row per wave step
+constexpr int kCopies = 32;                 // interleaved copies of the pair table
+constexpr int kTableBytes = 256 * 256;      // 256 entries x 256-byte rows
+constexpr int kMaxGroup = 16;
+// Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9, and an offset
+// past every buffer's end.
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kOutOfRange = 0x7fffffff;
 
-struct GemvArgs {
+struct GemvProblem {
   const uint16_t *x;
   const uint8_t *packed;
   void *y;
-  int32_t M, N, K;
-  int32_t log2_bs;
-  ScaleArgs sc;
+  const float *absmax;
+  const int8_t *absmax_q;
+  const float *absmax_scale;
+  int32_t N, K;
+  int32_t log2_bs, log2_bs2;
+  int32_t item_begin;  // first work item of this problem
+};
+
+struct GemvArgs {
+  GemvProblem p[kMaxGroup];
+  int32_t count;
+  int32_t M;
+  int32_t total_items;
   float value[16];
 };
 
-// 8 codes of one packed word -> 4 registers of bf16 pairs in k order.
-__device__ __forceinline__ bf16x8 dequant8(uint32_t word, float ap, const char *tb) {
-  const uint32_t even4 = (word >> 2) & 0x3c3c3c3cu;
-  const uint32_t odd4 = (word << 2) & 0x3c3c3c3cu;
+// 8 codes of one packed word -> 4 registers of bf16 pairs in k order (byte j
+// holds element 2j in its high nibble and 2j+1 in its low nibble).
+__device__ __forceinline__ bf16x8 dequant8(uint32_t word, float ap, const char *tbl,
+                                           uint32_t lane_base) {
   uint32_t out[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float c0 = *reinterpret_cast<const float *>(tb + ((even4 >> (8 * j)) & 0xffu));
-    const float c1 = *reinterpret_cast<const float *>(tb + ((odd4 >> (8 * j)) & 0xffu));
-    out[j] = pack_bf16x2(c0 * ap, c1 * ap);
+    // bytes of the address: [0] lane_base[0] (= 8 * copy), [1] code byte j, [2..3] zero
+    const uint32_t addr = __builtin_amdgcn_perm(word, lane_base, 0x0c0c0000u | ((4u + j) << 8));
+    const f32x2 c = *reinterpret_cast<const f32x2 *>(tbl + addr);
+    out[j] = pack_bf16x2(c.x * ap, c.y * ap);
   }
   uint4 v = make_uint4(out[0], out[1], out[2], out[3]);
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int NG, bool OUT_BF16>
+template <int NG, int CPW, bool DQ, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
-  __shared__ float table[16];
-  __shared__ float red[kWaves][NG][4][64];
-  if (threadIdx.x < 16) table[threadIdx.x] = args.value[threadIdx.x];
+  __shared__ __attribute__((aligned(16))) char lds[kTableBytes + kWaves * NG * 4 * 64 * 4];
+  const char *tbl = lds;
+  float *red = reinterpret_cast<float *>(lds + kTableBytes);  // [kWaves][NG][4][64]
+
+  // Pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy.
+  // Consecutive lanes write consecutive copies (no bank conflicts); in pass i
+  // every entry has e >> 4 == i.
+  {
+    const float lo = args.value[(threadIdx.x >> 5) & 15];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int idx = threadIdx.x + kThreads * i;  // e = idx / 32, copy = idx % 32
+      const f32x2 v = {args.value[i], lo};
+      *reinterpret_cast<f32x2 *>(lds + 256 * (idx >> 5) + 8 * (idx & 31)) = v;
+    }
+  }
   __syncthreads();
-  const char *tb = reinterpret_cast<const char *>(table);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int nl = lane & 15;  // B column (weight row in the group) / A row (m)
   const int kg = lane >> 4;  // which 32-code piece of the chunk
-  const int row0 = blockIdx.x * 16 * NG;
-  const int K = args.K;
-  const int nch = (K + kChunk - 1) / kChunk;
-  const int c_begin = (wave * nch) / kWaves;
-  const int c_end = ((wave + 1) * nch) / kWaves;
+  const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
+  const int M = args.M;
 
-  f32x4 acc[NG];
+  for (int item = blockIdx.x; item < args.total_items; item += gridDim.x) {
+    int pi = 0;
+    while (pi + 1 < args.count && args.p[pi + 1].item_begin <= item) ++pi;
+    const GemvProblem &P = args.p[pi];
+    const int N = P.N, K = P.K;
+    const int row0 = (item - P.item_begin) * 16 * NG;
+    const int nch = (K + kChunk - 1) / kChunk;
+    const int c_begin = (wave * nch) / kWaves;
+    const int c_end = ((wave + 1) * nch) / kWaves;
+    const int kg_last = (K - (nch - 1) * kChunk) >> 5;  // valid pieces in the last chunk
+
+    f32x4 acc[NG];
 #pragma unroll
-  for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const bool m_ok = nl < args.M;
-  const uint16_t *xrow = args.x + (int64_t)(m_ok ? nl : 0) * K;
-
-  for (int c = c_begin; c < c_end; ++c) {
-    const int k0 = c * kChunk + 32 * kg;
-    const bool k_ok = k0 < K;  // K % 32 == 0: the piece is all in or all out
-    uint4 xa[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      xa[s] = (m_ok && k_ok) ? *reinterpret_cast<const uint4 *>(xrow + k0 + 8 * s)
-                             : make_uint4(0, 0, 0, 0);
-    uint4 pw[NG];
-    float ap[NG];
+    // Activations through a buffer resource: lanes whose row m >= M get an
+    // out-of-range offset, which returns zeros without a memory access, so
+    // only the M live rows of the A operand are fetched.
+    const __amdgpu_buffer_rsrc_t xres =
+        __builtin_amdgcn_make_buffer_rsrc((void *)P.x, (short)0, M * K * 2, kBufferFlags);
+    const int xoff0 = nl < M ? (nl * K + 32 * kg) * 2 : kOutOfRange;
+    bool row_ok[NG];
+    const uint8_t *prow[NG];
+    int64_t brow[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       const int row = row0 + 16 * g + nl;
-      if (row < args.N && k_ok) {
-        const int64_t e = (int64_t)row * K + k0;
-        pw[g] = *reinterpret_cast<const uint4 *>(args.packed + e / 2);
-        ap[g] = block_scale(args.sc, e >> args.log2_bs);
-      } else {
-        pw[g] = make_uint4(0, 0, 0, 0);
-        ap[g] = 0.0f;
-      }
+      row_ok[g] = row < N;
+      const int64_t e = (int64_t)(row_ok[g] ? row : N - 1) * K + 32 * kg;
+      prow[g] = P.packed + e / 2;
+      brow[g] = e;
     }
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const uint32_t words[4] = {pw[g].x, pw[g].y, pw[g].z, pw[g].w};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 b = dequant8(words[s], ap[g], tb);
-        bf16x8 a = __builtin_bit_cast(bf16x8, xa[s]);
-        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[g], 0, 0, 0);
-      }
-    }
-  }
 
-  // Cross-wave reduction in a fixed order.
+    for (int cb = c_begin; cb < c_end; cb += CPW) {
+      // every load of the batch first (clamped, unconditional) ...
+      uint4 xa[CPW][4];
+      uint4 pw[CPW][NG];
+      float sf[CPW][NG];
+      int32_t sq[CPW][NG];
+      bool ok[CPW];
 #pragma unroll
-  for (int g = 0; g < NG; ++g)
+      for (int i = 0; i < CPW; ++i) {
+        int c = cb + i;
+        ok[i] = c < c_end && (c < nch - 1 || kg < kg_last);
+        if (c >= c_end) c = c_end - 1;
+        // a piece past K (last chunk only) reads the chunk start instead
+        const int kc = c * kChunk - ((c == nch - 1 && kg >= kg_last) ? 32 * kg : 0);
+        const int xoff = xoff0 == kOutOfRange ? kOutOfRange : xoff0 + 2 * kc;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][g][r][lane] = acc[g][r];
-  __syncthreads();
-  for (int v = threadIdx.x; v < NG * 4 * 64; v += kThreads) {
-    const int g = v / 256, r = (v / 64) % 4, l = v % 64;
-    float sum = 0.0f;
+        for (int s = 0; s < 4; ++s)
+          xa[i][s] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff, 16 * s, 0));
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) sum += red[w][g][r][l];
-    // D layout of the 16x16 MFMA: lane l holds rows 4*(l/16)+r of column l%16.
-    const int m = 4 * (l >> 4) + r;
-    const int n = row0 + 16 * g + (l & 15);
-    if (m < args.M && n < args.N) {
-      const int64_t o = (int64_t)m * args.N + n;
-      if (OUT_BF16)
-        reinterpret_cast<uint16_t *>(args.y)[o] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xffffu);
-      else
-        reinterpret_cast<float *>(args.y)[o] = sum;
+        for (int g = 0; g < NG; ++g) {
+          pw[i][g] = *reinterpret_cast<const uint4 *>(prow[g] + kc / 2);
+          const int64_t b = (brow[g] + kc) >> P.log2_bs;
+          if (DQ) {
+            sq[i][g] = P.absmax_q[b];
+            sf[i][g] = P.absmax_scale[b >> P.log2_bs2];
+          } else {
+            sq[i][g] = 1;
+            sf[i][g] = P.absmax[b];
+          }
+        }
+      }
+      // ... then the arithmetic
+#pragma unroll
+      for (int i = 0; i < CPW; ++i)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          float ap = DQ ? (float)sq[i][g] * sf[i][g] : sf[i][g];
+          ap = (ok[i] && row_ok[g]) ? ap : 0.0f;
+          const uint32_t words[4] = {pw[i][g].x, pw[i][g].y, pw[i][g].z, pw[i][g].w};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            bf16x8 b = dequant8(words[s], ap, tbl, lane_base);
+            bf16x8 a = __builtin_bit_cast(bf16x8, xa[i][s]);
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[g], 0, 0, 0);
+          }
+        }
+    }
+
+    // Cross-wave reduction in a fixed order (the first barrier also fences
+    // the previous item's reads of the buffer).
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[((wave * NG + g) * 4 + r) * 64 + lane] = acc[g][r];
+    __syncthreads();
+    for (int v = threadIdx.x; v < NG * 4 * 64; v += kThreads) {
+      const int g = v / 256, r = (v / 64) % 4, l = v % 64;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += red[((w * NG + g) * 4 + r) * 64 + l];
+      // D layout of the 16x16 MFMA: lane l holds rows 4*(l/16)+r of column l%16.
+      const int m = 4 * (l >> 4) + r;
+      const int n = row0 + 16 * g + (l & 15);
+      if (m < M && n < N) {
+        const int64_t o = (int64_t)m * N + n;
+        if (OUT_BF16)
+          reinterpret_cast<uint16_t *>(P.y)[o] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xffffu);
+        else
+          reinterpret_cast<float *>(P.y)[o] = sum;
+      }
     }
   }
 }
 
-template <int NG>
-hipError_t launch_ng(const GemvArgs &args, bool out_bf16, hipStream_t stream) {
-  dim3 grid((unsigned)((args.N + 16 * NG - 1) / (16 * NG)));
+template <int NG, int CPW, bool DQ>
+hipError_t launch_cfg(const GemvArgs &args, int grid, bool out_bf16, hipStream_t stream) {
   if (out_bf16)
-    hipLaunchKernelGGL((gemv_kernel<NG, true>), grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((gemv_kernel<NG, CPW, DQ, true>), dim3(grid), dim3(kThreads), 0, stream,
+                       args);
   else
-    hipLaunchKernelGGL((gemv_kernel<NG, false>), grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((gemv_kernel<NG, CPW, DQ, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       args);
   return hipGetLastError();
+}
+
+template <bool DQ>
+hipError_t launch_dq(const GemvArgs &args, int ng, int cpw, int grid, bool out_bf16,
+                     hipStream_t stream) {
+  if (ng == 2) return launch_cfg<2, 2, DQ>(args, grid, out_bf16, stream);
+  if (cpw == 2) return launch_cfg<1, 2, DQ>(args, grid, out_bf16, stream);
+  return launch_cfg<1, 4, DQ>(args, grid, out_bf16, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
-                       int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
-                       void *y, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
+int gemv_max_group() { return kMaxGroup; }
+
+hipError_t launch_gemv_grouped(int count, const GemvDesc *descs, int M, int quant_type,
+                               bool double_quant, bool out_bf16, hipStream_t stream) {
+  if (count == 0 || M == 0) return hipSuccess;
+  if (count > kMaxGroup) return hipErrorInvalidValue;
   const CodeTables &t = code_tables(quant_type);
+  const int ng = M > 4 ? 2 : 1;
   GemvArgs args;
-  args.x = x;
-  args.packed = packed;
-  args.y = y;
+  args.count = 0;
   args.M = M;
-  args.N = N;
-  args.K = K;
-  args.log2_bs = __builtin_ctz((unsigned)blocksize);
-  args.sc = sc;
+  int items = 0, max_k = 0;
+  for (int i = 0; i < count; ++i) {
+    const GemvDesc &d = descs[i];
+    if (d.N == 0) continue;
+    GemvProblem &p = args.p[args.count++];
+    p.x = d.x;
+    p.packed = d.packed;
+    p.y = d.y;
+    p.absmax = d.sc.absmax;
+    p.absmax_q = d.sc.absmax_q;
+    p.absmax_scale = d.sc.absmax_scale;
+    p.N = d.N;
+    p.K = d.K;
+    p.log2_bs = __builtin_ctz((unsigned)d.blocksize);
+    p.log2_bs2 = d.sc.log2_bs2;
+    p.item_begin = items;
+    items += (d.N + 16 * ng - 1) / (16 * ng);
+    max_k = d.K > max_k ? d.K : max_k;
+  }
+  if (args.count == 0) return hipSuccess;
+  args.total_items = items;
   for (int i = 0; i < 16; ++i) args.value[i] = t.value[i];
-  // Wider row groups share each x chunk across more weight rows; keep at
-  // least ~2 workgroups per CU.
-  if (M > 4 && N >= 16 * 2 * 512) return launch_ng<2>(args, out_bf16, stream);
-  return launch_ng<1>(args, out_bf16, stream);
+  const int per_wave = ((max_k + kChunk - 1) / kChunk + kWaves - 1) / kWaves;
+  const int cpw = per_wave <= 2 ? 2 : 4;
+  // Two workgroups fit per CU (LDS); more items than that are walked in turn.
+  const int cap = 2 * device_cu_count();
+  const int grid = items < cap ? items : cap;
+  return double_quant ? launch_dq<true>(args, ng, cpw, grid, out_bf16, stream)
+                      : launch_dq<false>(args, ng, cpw, grid, out_bf16, stream);
 }
 
 }  // namespace nf4

@@ -42,6 +42,8 @@ nf4_status check_device() {
 
 nf4_status from_hip(hipError_t e) { return e == hipSuccess ? NF4_OK : NF4_ERR_DEVICE; }
 
+std::atomic<int> g_cu_count[64];
+
 // Validates a quantized-tensor descriptor; fills the kernels' scale source.
 nf4_status check_qweight(const nf4_qweight *w, ScaleArgs *sc) {
   if (w == nullptr) return NF4_ERR_INVALID_ARGUMENT;
@@ -86,6 +88,19 @@ nf4_status check_product(const void *x, int32_t M, const nf4_qweight *w, int32_t
 }
 
 }  // namespace
+
+int nf4::device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 extern "C" {
 
@@ -181,16 +196,41 @@ nf4_status nf4_dequantize(const nf4_qweight *w, int32_t out_dtype, void *out, vo
 
 nf4_status nf4_gemv(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                     int32_t compute_dtype, int32_t out_dtype, void *y, void *stream) {
-  ScaleArgs sc;
-  nf4_status st = check_product(x_bf16, M, w, N, K, compute_dtype, out_dtype, y, &sc);
-  if (st != NF4_OK) return st;
+  return nf4_gemv_grouped(1, &x_bf16, M, w, &N, &K, compute_dtype, out_dtype, &y, stream);
+}
+
+nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
+                            const nf4_qweight *w, const int32_t *N, const int32_t *K,
+                            int32_t compute_dtype, int32_t out_dtype, void *const *y,
+                            void *stream) {
+  if (count < 0 || count > NF4_GEMV_MAX_GROUP) return NF4_ERR_INVALID_ARGUMENT;
+  if (count == 0) return NF4_OK;
+  if (x_bf16 == nullptr || w == nullptr || N == nullptr || K == nullptr || y == nullptr)
+    return NF4_ERR_INVALID_ARGUMENT;
+  GemvDesc descs[NF4_GEMV_MAX_GROUP];
+  for (int i = 0; i < count; ++i) {
+    ScaleArgs sc;
+    nf4_status st =
+        check_product(x_bf16[i], M, &w[i], N[i], K[i], compute_dtype, out_dtype, y[i], &sc);
+    if (st != NF4_OK) return st;
+    if (w[i].quant_type != w[0].quant_type || w[i].double_quant != w[0].double_quant)
+      return NF4_ERR_UNSUPPORTED;
+    descs[i] = GemvDesc{static_cast<const uint16_t *>(x_bf16[i]), w[i].packed, y[i], sc, N[i],
+                        K[i], w[i].blocksize};
+  }
   if (M > 16) return NF4_ERR_INVALID_ARGUMENT;
-  if (M == 0 || N == 0) return NF4_OK;
-  st = check_device();
+  for (int i = 0; i < count; ++i)
+    if (K[i] > (1 << 26)) return NF4_ERR_UNSUPPORTED;  // 31-bit activation offsets
+  if (M == 0) return NF4_OK;
+  nf4_status st = check_device();
   if (st != NF4_OK) return st;
-  return from_hip(launch_gemv(static_cast<const uint16_t *>(x_bf16), M, w->packed, N, K,
-                              w->blocksize, w->quant_type, sc, out_dtype == NF4_DTYPE_BF16, y,
-                              reinterpret_cast<hipStream_t>(stream)));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const bool dq = w[0].double_quant != 0, bf16_out = out_dtype == NF4_DTYPE_BF16;
+  bool short_k = true;
+  for (int i = 0; i < count; ++i) short_k = short_k && K[i] <= gemv1_max_k();
+  if (M == 1 && short_k)
+    return from_hip(launch_gemv1_grouped(count, descs, w[0].quant_type, dq, bf16_out, s));
+  return from_hip(launch_gemv_grouped(count, descs, M, w[0].quant_type, dq, bf16_out, s));
 }
 
 nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,

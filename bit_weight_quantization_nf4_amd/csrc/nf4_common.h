@@ -54,6 +54,16 @@ __device__ __forceinline__ float block_scale(const ScaleArgs &sc, int64_t b) {
   return sc.absmax[b];
 }
 
+// Bit-field extract of 8 bits at a constant offset as one v_bfe_u32 (the
+// compiler otherwise splits a chain of extracts from one pre-shifted word
+// into a shift and a mask per field).
+template <int OFF>
+__device__ __forceinline__ uint32_t bfe8(uint32_t v) {
+  uint32_t r;
+  asm("v_bfe_u32 %0, %1, %2, 8" : "=v"(r) : "v"(v), "i"(OFF));
+  return r;
+}
+
 // Two fp32 -> packed bf16 pair with round-to-nearest-even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 f = {lo, hi};

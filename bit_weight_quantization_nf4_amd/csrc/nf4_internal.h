@@ -18,9 +18,31 @@ hipError_t launch_double_quant(const float *absmax, int64_t nb, int blocksize2, 
 hipError_t launch_dequantize(const uint8_t *packed, int64_t n, int blocksize, int quant_type,
                              const ScaleArgs &sc, bool out_bf16, void *out, hipStream_t stream);
 
-hipError_t launch_gemv(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
-                       int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
-                       void *y, hipStream_t stream);
+// One decode product of a group launched together by launch_gemv_grouped.
+struct GemvDesc {
+  const uint16_t *x;      // [M, K] bf16
+  const uint8_t *packed;  // [N*K/2]
+  void *y;                // [M, N]
+  ScaleArgs sc;
+  int32_t N, K, blocksize;
+};
+
+// Largest number of products in one grouped launch.
+int gemv_max_group();
+
+// All products share M, the quant type (one code table) and the double-quant
+// flag; blocksizes and shapes may differ.
+hipError_t launch_gemv_grouped(int count, const GemvDesc *descs, int M, int quant_type,
+                               bool double_quant, bool out_bf16, hipStream_t stream);
+
+// Single-activation-row products (M = 1) for K <= gemv1_max_k(): waves own
+// whole rows; same grouping rules as launch_gemv_grouped.
+int gemv1_max_k();
+hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type,
+                                bool double_quant, bool out_bf16, hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
 
 hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
                        int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,

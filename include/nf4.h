@@ -145,11 +145,31 @@ nf4_status nf4_dequantize(const nf4_qweight *w, int32_t out_dtype, void *out, vo
  * 4-bit dequantize + GEMM for batch 1..64]:
  *   y[m, j] = sum_k bf16(dequant(W)[j, k]) * x[m, k],  fp32 accumulation,
  * x bf16 [M, K] row-major, W the quantized [N, K] tensor (w->n == N*K), y [M, N]
- * row-major in out_dtype (bf16 = RNE of the fp32 result). 1 <= M <= 16.
+ * row-major in out_dtype (bf16 = RNE of the fp32 result). 1 <= M <= 16;
+ * K <= 2^26 (NF4_ERR_UNSUPPORTED above).
  * compute_dtype must be NF4_DTYPE_BF16. The reduction order is fixed, so
  * repeated calls give identical bits. */
 nf4_status nf4_gemv(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                     int32_t compute_dtype, int32_t out_dtype, void *y, void *stream);
+
+/* Largest `count` accepted by nf4_gemv_grouped. */
+#define NF4_GEMV_MAX_GROUP 16
+
+/* Several independent decode products in ONE launch -- e.g. the projections of
+ * one transformer layer at one decode position [repo page 0.50.0: kernels for
+ * 4-bit inference chosen by shape; one launch keeps all CUs busy where a single
+ * small GEMV cannot]. For i < count:
+ *   y[i][m, j] = sum_k bf16(dequant(w[i])[j, k]) * x[i][m, k],
+ * with the layouts and rules of nf4_gemv for each product. x_bf16, w, N, K and
+ * y are HOST arrays of `count` entries (the tensors they point to are on the
+ * device). All products share M (1..16), the quant type and the double-quant
+ * flag (NF4_ERR_UNSUPPORTED otherwise); shapes and blocksizes may differ.
+ * 0 <= count <= NF4_GEMV_MAX_GROUP. Each product's result is bitwise the same
+ * as nf4_gemv on it alone. */
+nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
+                            const nf4_qweight *w, const int32_t *N, const int32_t *K,
+                            int32_t compute_dtype, int32_t out_dtype, void *const *y,
+                            void *stream);
 
 /* Prefill product, any M >= 1: the same contraction as nf4_gemv, computed with
  * bf16 matrix cores on dequantized weight tiles and fp32 accumulation [repo

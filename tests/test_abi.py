@@ -40,7 +40,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(nf4):
     declared = header_functions()
-    assert len(declared) == 11
+    assert len(declared) == 12
     handle = ctypes.CDLL(nf4.LIB_PATH)
     for name in declared:
         assert hasattr(handle, name), name
@@ -135,6 +135,28 @@ def test_product_validation(nf4, entry):
     assert call(0, 64, 128, x=None, y=None) == OK
     if entry == "nf4_gemv":
         assert call(17, 64, 128) == INVALID
+
+
+def test_grouped_validation(nf4):
+    L = nf4.lib()
+    P = ctypes.c_void_p
+    d = (nf4.QWeightDesc * 2)(_desc(nf4, n=64 * 128), _desc(nf4, n=64 * 256))
+    xs = (P * 2)(A, A)
+    ys = (P * 2)(B, B)
+    Ns = (ctypes.c_int32 * 2)(64, 64)
+    Ks = (ctypes.c_int32 * 2)(128, 256)
+    g = L.nf4_gemv_grouped
+    assert g(17, xs, 1, d, Ns, Ks, 0, 1, ys, None) == INVALID
+    assert g(-1, xs, 1, d, Ns, Ks, 0, 1, ys, None) == INVALID
+    assert g(2, None, 1, d, Ns, Ks, 0, 1, ys, None) == INVALID
+    assert g(2, xs, 17, d, Ns, Ks, 0, 1, ys, None) == INVALID
+    assert g(0, None, 1, None, None, None, 0, 1, None, None) == OK
+    Kbad = (ctypes.c_int32 * 2)(128, 100)
+    assert g(2, xs, 1, d, Ns, Kbad, 0, 1, ys, None) == INVALID  # second product N*K != n
+    mixed = (nf4.QWeightDesc * 2)(_desc(nf4, n=64 * 128), _desc(nf4, n=64 * 256, qt=1))
+    assert g(2, xs, 1, mixed, Ns, Ks, 0, 1, ys, None) == UNSUPPORTED
+    ys_bad = (P * 2)(B, MIS)
+    assert g(2, xs, 1, d, Ns, Ks, 0, 1, ys_bad, None) == MISALIGNED
 
 
 def test_no_device_is_reported(nf4):

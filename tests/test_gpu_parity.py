@@ -255,6 +255,29 @@ def test_gemv_ragged_shapes(nf4, orc, bs, dq):
         _gemv_case(nf4, orc, w, x, bs, "nf4", dq)
 
 
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemv_grouped_matches_single_and_oracle(nf4, orc, dq):
+    """One grouped launch over differently shaped products (two blocksizes,
+    ragged rows): each result is bitwise the single-product result and within
+    tolerance of the oracle."""
+    shapes = [(4096, 4096, 64), (1000, 512, 128), (33, 160, 32), (11008, 4096, 64), (16, 64, 64)]
+    for M in (1, 3, 16):
+        qss, xs, refs = [], [], []
+        for i, (N, K, bs) in enumerate(shapes):
+            w = workloads.normal_bf16((N, K), 0.02, 700 + i)
+            x = workloads.normal_bf16((M, K), 1.0, 800 + i + M)
+            qs, ref = check_quant(nf4, orc, w, bs, "nf4", dq)
+            _, wc16 = orc.dequantize(ref["packed"], N * K, bs, "nf4", **oracle_scales(ref, dq))
+            refs.append((orc.matmul_bf16(to_u16(x), wc16.reshape(N, K)), wc16.reshape(N, K),
+                         to_u16(x)))
+            qss.append(qs)
+            xs.append(dev(x))
+        ys = nf4.gemv_grouped(xs, qss, torch.float32)
+        for y, x, qs, (y_ref, wc16, x16) in zip(ys, xs, qss, refs):
+            assert torch.equal(y, nf4.gemv(x, qs, torch.float32))
+            check_product(y, None, y_ref, wc16, x16)
+
+
 def test_gemm_small_shapes(nf4, orc):
     for (M, N, K, bs, dq, qt) in [(1, 64, 64, 64, False, "nf4"), (5, 130, 256, 64, True, "nf4"),
                                   (128, 128, 128, 64, True, "fp4"), (130, 257, 96, 32, False, "nf4"),
