@@ -7,19 +7,22 @@
 //  "Configuration": weights are dequantized to the bf16 compute dtype.]
 //
 // Design (HBM-bound; every 4-bit weight is read exactly once):
-//  - a wave owns whole weight rows. Lane l reads the 16-byte code slices at
-//    k = 2048 j + 32 l (j < J = ceil(K / 2048)), so each load instruction
-//    streams 1 KB of one row and the lane's activations x[k .. k+31] stay in
-//    registers for every row of the problem;
-//  - the rows of all problems of the launch are split into contiguous ranges,
-//    one per wave, so activations are reloaded only where a range crosses into
-//    the next problem; each wave issues the loads of two rows before using
-//    them;
+//  - a wave owns whole weight rows. Lane l reads the 32 code bytes at
+//    k = 4096 j + 64 l (j < J = ceil(K / 4096)) as two 16-byte loads, so each
+//    load instruction streams 1 KB of one row, one block scale per lane covers
+//    them (two at blocksize 32), and the lane's activations x[k .. k+63] stay
+//    in registers for every row of the problem;
+//  - the waves of the launch are split among its problems in proportion to
+//    their rows, and each wave takes a contiguous range of one problem's rows,
+//    so a wave loads its activations once; it keeps the loads of the next row
+//    in flight while it computes the current one;
 //  - dequantization: the same conflict-free LDS pair table as the batched
 //    kernel (entry = fp32 code values of both nibbles of a code byte, one copy
 //    per bank pair, address built by one v_perm_b32), times the block scale,
 //    rounded to bf16 pairs with v_cvt_pk_bf16_f32 -- the dequantize kernel's
-//    bf16 weights -- then v_dot2_f32_bf16 with the bf16 activations;
+//    bf16 weights -- then v_dot2_f32_bf16 with the bf16 activations. This
+//    arithmetic (about 19 VALU cycles per two weights), not HBM, sets the
+//    kernel's pace;
 //  - a row ends with a fixed-order DPP reduction across the wave (no atomics),
 //    so results are bitwise reproducible.
 #include "nf4_internal.h"
@@ -29,10 +32,16 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kSlice = 2048;           // codes of one row per wave-wide load
+constexpr int kSlice = 4096;           // codes of one row per slice (64 per lane)
 constexpr int kCopies = 32;            // interleaved copies of the pair table
 constexpr int kTableBytes = 256 * 256; // 256 entries x 256-byte rows
 constexpr int kMaxGroup = 16;
+// false: each wave takes a contiguous range of its problem's rows; true: rows
+// go to the problem's waves round-robin (row w, w + waves, ...). Both measure
+// the same; contiguous ranges keep each wave's reads sequential.
+constexpr bool kInterleave = false;
+// Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
+constexpr int kBufferFlags = 0x00020000;
 
 struct Gemv1Problem {
   const uint16_t *x;
@@ -43,13 +52,12 @@ struct Gemv1Problem {
   const float *absmax_scale;
   int32_t N, K;
   int32_t log2_bs, log2_bs2;
-  int64_t row_begin;  // first row of this problem in the concatenated row list
+  int32_t wave_begin, waves;  // the waves of the launch that share this problem's rows
 };
 
 struct Gemv1Args {
   Gemv1Problem p[kMaxGroup];
   int32_t count;
-  int64_t total_rows;
   float value[16];
 };
 
@@ -74,146 +82,293 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// 8 codes of one packed word times the block scale, dotted with 8 bf16
-// activations (4 packed pairs), accumulated in fp32.
-__device__ __forceinline__ float dot8(uint32_t word, float ap, const uint32_t xp[4],
-                                      const char *tbl, uint32_t lane_base, float acc) {
+// 32 codes (one 16-byte piece) times the block scale, dotted with 32 bf16
+// activations (16 packed pairs): all 16 table reads are issued before the
+// arithmetic, and two accumulators alternate, so table-read latency and the
+// accumulation chain overlap with other work of the wave.
+__device__ __forceinline__ void dot32(const uint4 &pw, float ap, const uint32_t xp[16],
+                                      const char *tbl, uint32_t lane_base, float &acc0,
+                                      float &acc1) {
+  const uint32_t wd[4] = {pw.x, pw.y, pw.z, pw.w};
+  f32x2 c[16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t addr = __builtin_amdgcn_perm(word, lane_base, 0x0c0c0000u | ((4u + j) << 8));
-    const f32x2 c = *reinterpret_cast<const f32x2 *>(tbl + addr);
-    const uint32_t w2 = pack_bf16x2(c.x * ap, c.y * ap);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w2),
-                                          __builtin_bit_cast(bf16x2_t, xp[j]), acc, false);
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t addr =
+        __builtin_amdgcn_perm(wd[i >> 2], lane_base, 0x0c0c0000u | ((4u + (i & 3)) << 8));
+    c[i] = *reinterpret_cast<const f32x2 *>(tbl + addr);
   }
-  return acc;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const uint32_t w0 = pack_bf16x2(c[i].x * ap, c[i].y * ap);
+    const uint32_t w1 = pack_bf16x2(c[i + 1].x * ap, c[i + 1].y * ap);
+    acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w0),
+                                           __builtin_bit_cast(bf16x2_t, xp[i]), acc0, false);
+    acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w1),
+                                           __builtin_bit_cast(bf16x2_t, xp[i + 1]), acc1, false);
+  }
 }
 
-template <int J, bool DQ, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void gemv1_kernel(Gemv1Args args) {
+// Loads of one weight row: per slice, 64 codes (two 16-byte pieces) per lane
+// plus the raw block scales (one block per lane, two when blocksize is 32).
+template <int J, bool BS32>
+struct RowLoads {
+  uint4 pw[J][2];
+  float sf[J][BS32 ? 2 : 1];
+  int32_t sq[J][BS32 ? 2 : 1];
+};
+
+// Waves per SIMD the register budget is sized for: x for J slices lives in
+// registers, so longer rows trade occupancy for registers.
+template <int J>
+constexpr int waves_per_simd() { return J == 1 ? 4 : 2; }
+
+template <int J, int NBUF, bool DQ, bool BS32, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(waves_per_simd<J>(), waves_per_simd<J>())))
+void gemv1_kernel(Gemv1Args args) {
+  constexpr int NS = BS32 ? 2 : 1;  // scales per lane per slice
   __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
   // Pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy.
-  // Consecutive lanes write consecutive copies (no bank conflicts); in pass i
-  // every entry has e >> 4 == i.
-  {
-    const float lo = args.value[(threadIdx.x >> 5) & 15];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int idx = threadIdx.x + kThreads * i;  // e = idx / 32, copy = idx % 32
-      const f32x2 v = {args.value[i], lo};
-      *reinterpret_cast<f32x2 *>(tbl + 256 * (idx >> 5) + 8 * (idx & 31)) = v;
-    }
+  // Consecutive threads write consecutive copies (no bank conflicts).
+  for (int idx = threadIdx.x; idx < 256 * kCopies; idx += kThreads) {
+    const int e = idx / kCopies, copy = idx % kCopies;
+    const f32x2 v = {args.value[e >> 4], args.value[e & 15]};
+    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * copy) = v;
   }
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
-  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * kWaves;
-  const int64_t r_begin = wave * args.total_rows / nwaves;
-  const int64_t r_end = (wave + 1) * args.total_rows / nwaves;
+  // wave index made explicitly uniform, so row bookkeeping stays scalar
+  const int wave = (int)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 
-  int pi = -1;
-  int64_t p_end = 0;  // first row after the current problem
-  Gemv1Problem P;
-  uint32_t xv[J][16];  // x[2048 j + 32 lane .. +31] as bf16 pairs
-  bool sl_ok[J];
+  // Each problem has its own set of waves, each with a contiguous range of
+  // that problem's rows (a uniform loop finds it, so every problem field is a
+  // scalar). A wave never switches problems, so its prefetch never restarts.
+  for (int pi = 0; pi < args.count; ++pi) {
+    const int w = wave - args.p[pi].wave_begin;
+    if (w < 0 || w >= args.p[pi].waves) continue;
+    const int64_t Np = args.p[pi].N, nw = args.p[pi].waves;
+    // this wave's rows of the problem: row(i) = first + i * stride, i < cnt
+    int64_t first, stride, cnt;
+    if (kInterleave) {  // the problem's waves sweep its rows side by side
+      first = w;
+      stride = nw;
+      cnt = (Np - w + nw - 1) / nw;
+    } else {  // a contiguous range per wave
+      first = w * Np / nw;
+      stride = 1;
+      cnt = (w + 1) * Np / nw - first;
+    }
+    if (cnt <= 0) continue;
+    const uint16_t *x = args.p[pi].x;
+    const uint8_t *packed = args.p[pi].packed;
+    const float *absmax = args.p[pi].absmax;
+    const int8_t *absmax_q = args.p[pi].absmax_q;
+    const float *absmax_scale = args.p[pi].absmax_scale;
+    void *y = args.p[pi].y;
+    const int K = args.p[pi].K;
+    const int log2_bs = args.p[pi].log2_bs, log2_bs2 = args.p[pi].log2_bs2;
+    const uint32_t row_bytes = (uint32_t)K >> 1;
+    const uint32_t row_blocks = (uint32_t)K >> log2_bs;
+    // blocksize 32: a lane's 64 codes span two blocks (only in the BS32
+    // variant, which a launch uses when any of its problems has bs 32)
+    const bool two_blocks = BS32 && log2_bs == 5;
 
-  for (int64_t r = r_begin; r < r_end; r += 2) {
-    if (r >= p_end) {
-      // next problem: the one containing row r
-      do {
-        ++pi;
-      } while (pi + 1 < args.count && args.p[pi + 1].row_begin <= r);
-      P = args.p[pi];
-      p_end = P.row_begin + P.N;
+    // Slice j, lane l: codes k0 .. k0+63 with k0 = 4096 j + 64 l, as two
+    // 32-code pieces (each wholly inside or outside K, since K % 32 == 0).
+    // An absent piece reads zeros and gets block scale 0.
+    bool ok[J][2];
+    uint32_t voff[J], kb[J], kb2[J];  // kb2: the lane's second block (bs 32), else kb
+    uint32_t xv[J][32];         // x[k0 .. k0+63] as bf16 pairs
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int k0 = kSlice * j + 32 * lane;
-        sl_ok[j] = k0 < P.K;
-        const uint4 *src = reinterpret_cast<const uint4 *>(P.x + (sl_ok[j] ? k0 : 0));
+    for (int j = 0; j < J; ++j) {
+      const int k0 = kSlice * j + 64 * lane;
+      ok[j][0] = k0 < K;
+      ok[j][1] = k0 + 32 < K;
+      voff[j] = ok[j][0] ? (uint32_t)k0 >> 1 : 0x80000000u;  // past the row: reads zeros
+      kb[j] = ok[j][0] ? (uint32_t)k0 >> log2_bs : 0u;
+      kb2[j] = (two_blocks && ok[j][1]) ? kb[j] + 1 : kb[j];
+      // x[k0 .. k0+63]: past K the buffer returns zeros, without a branch
+      const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)x, (short)0, (int)(2u * (uint32_t)K), kBufferFlags);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 v = sl_ok[j] ? src[q] : make_uint4(0, 0, 0, 0);
-          xv[j][4 * q] = v.x;
-          xv[j][4 * q + 1] = v.y;
-          xv[j][4 * q + 2] = v.z;
-          xv[j][4 * q + 3] = v.w;
-        }
+      for (int q = 0; q < 8; ++q) {
+        const uint4 v = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, 2 * k0, 16 * q, 0));
+        xv[j][4 * q] = v.x;
+        xv[j][4 * q + 1] = v.y;
+        xv[j][4 * q + 2] = v.z;
+        xv[j][4 * q + 3] = v.w;
       }
     }
-    // two rows of this problem (the second may not exist)
-    const int64_t rl = r - P.row_begin;
-    const bool has2 = r + 1 < r_end && r + 1 < p_end;
-    uint4 pw[2][J];
-    float sf[2][J];
-    int32_t sq[2][J];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int64_t row = rl + (t == 1 && has2 ? 1 : 0);
+
+    // Row loads go through buffer resources whose base is the (wave-uniform)
+    // row start: lane offsets stay 32-bit, no 64-bit vector addresses are
+    // formed, and an out-of-range offset returns zeros without an access.
+    const uint32_t kAll = 0xffffffffu;
+    auto load_row = [&](int64_t rl) {
+      RowLoads<J, BS32> L;
+      const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)(packed + (uint64_t)rl * row_bytes), (short)0, (int)row_bytes, kBufferFlags);
+      // first block of the row, and its group split into a group base and
+      // the block's place inside that group (64-bit safe)
+      const uint64_t rb = (uint64_t)rl * row_blocks;
+      const uint64_t gbase = rb >> log2_bs2;
+      const uint32_t rb_in = (uint32_t)(rb & (((uint64_t)1 << log2_bs2) - 1));
+      // scales first: a wait for a row's scale then leaves its codes in flight
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        const int64_t e = row * P.K + (sl_ok[j] ? kSlice * j + 32 * lane : 0);
-        pw[t][j] = *reinterpret_cast<const uint4 *>(P.packed + e / 2);
-        const int64_t b = e >> P.log2_bs;
         if (DQ) {
-          sq[t][j] = P.absmax_q[b];
-          sf[t][j] = P.absmax_scale[b >> P.log2_bs2];
+          const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+              (void *)(absmax_q + rb), (short)0, (int)kAll, kBufferFlags);
+          L.sq[j][0] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)kb[j], 0, 0);
+          if constexpr (BS32)  // kb2 == kb unless a second block exists
+            L.sq[j][1] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)kb2[j], 0, 0);
+          // group scale: a per-lane load (lanes of one group share a cache
+          // line); no branch, so the waits of later rows stay exact
+          const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+              (void *)(absmax_scale + gbase), (short)0, (int)kAll, kBufferFlags);
+          L.sf[j][0] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(
+                         srs, (int)(((rb_in + kb[j]) >> log2_bs2) << 2), 0, 0));
+          if constexpr (BS32)
+            L.sf[j][1] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(
+                           srs, (int)(((rb_in + kb2[j]) >> log2_bs2) << 2), 0, 0));
         } else {
-          sq[t][j] = 1;
-          sf[t][j] = P.absmax[b];
+          const __amdgpu_buffer_rsrc_t ars = __builtin_amdgcn_make_buffer_rsrc(
+              (void *)(absmax + rb), (short)0, (int)kAll, kBufferFlags);
+          L.sq[j][0] = 1;
+          L.sf[j][0] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(ars, (int)(kb[j] << 2), 0, 0));
+          if constexpr (BS32) {
+            L.sq[j][1] = 1;
+            L.sf[j][1] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(ars, (int)(kb2[j] << 2), 0, 0));
+          }
         }
       }
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float acc = 0.0f;
 #pragma unroll
       for (int j = 0; j < J; ++j) {
-        float ap = DQ ? (float)sq[t][j] * sf[t][j] : sf[t][j];
-        ap = sl_ok[j] ? ap : 0.0f;
-        acc = dot8(pw[t][j].x, ap, &xv[j][0], tbl, lane_base, acc);
-        acc = dot8(pw[t][j].y, ap, &xv[j][4], tbl, lane_base, acc);
-        acc = dot8(pw[t][j].z, ap, &xv[j][8], tbl, lane_base, acc);
-        acc = dot8(pw[t][j].w, ap, &xv[j][12], tbl, lane_base, acc);
+        L.pw[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   prs, (int)voff[j], 0, 0));
+        L.pw[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   prs, (int)voff[j], 16, 0));
       }
-      const float sum = wave_sum(acc);
-      if (lane == 63 && (t == 0 || has2)) {
-        const int64_t row = rl + t;
-        if (OUT_BF16)
-          reinterpret_cast<uint16_t *>(P.y)[row] = (uint16_t)(pack_bf16x2(sum, 0.0f) & 0xffffu);
-        else
-          reinterpret_cast<float *>(P.y)[row] = sum;
+      // keep the scheduler from hoisting the previous row's arithmetic (and
+      // its waits) above these loads
+      __builtin_amdgcn_sched_barrier(0);
+      return L;
+    };
+
+    constexpr uint32_t kOutBytes = OUT_BF16 ? 2u : 4u;
+    auto compute_row = [&](const RowLoads<J, BS32> &L, int64_t r) {
+      float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const int si = BS32 ? p : 0;
+          float ap = DQ ? (float)L.sq[j][si] * L.sf[j][si] : L.sf[j][si];
+          ap = ok[j][p] ? ap : 0.0f;
+          dot32(L.pw[j][p], ap, &xv[j][16 * p], tbl, lane_base, acc0, acc1);
+        }
+      }
+      const float sum = wave_sum(acc0 + acc1);
+      // Lane 63 holds the total. Every lane issues the store (no branch, so
+      // the compiler counts it and its waits for later rows stay exact); the
+      // buffer is the one output element, and the other lanes' offsets lie
+      // past it, so their stores are dropped.
+      const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)((char *)y + (uint64_t)r * kOutBytes), (short)0, (int)kOutBytes, kBufferFlags);
+      const uint32_t yoff = lane == 63 ? 0u : 0x80000000u;
+      if (OUT_BF16)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(sum, 0.0f) & 0xffffu), yrs,
+                                              (int)yoff, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sum), yrs, (int)yoff,
+                                              0, 0);
+    };
+
+    // NBUF row buffers in turn: the loads of the next NBUF-1 rows are in
+    // flight while the current row computes (per SIMD the arithmetic of a row
+    // takes about as long as its bytes take to arrive). An iteration handles
+    // NBUF rows with one straight-line body; every prefetch is unconditional
+    // (clamped to the last row), so the wait before a row counts only that
+    // row's own loads.
+    const int64_t last = cnt - 1;
+    auto row_at = [&](int64_t i) { return first + (i < last ? i : last) * stride; };
+    RowLoads<J, BS32> buf[NBUF];
+#pragma unroll
+    for (int b = 0; b + 1 < NBUF; ++b) buf[b] = load_row(row_at(b));
+    for (int64_t i = 0; i < cnt; i += NBUF) {
+#pragma unroll
+      for (int b = 0; b < NBUF; ++b) {
+        buf[(b + NBUF - 1) % NBUF] = load_row(row_at(i + b + NBUF - 1));
+        // rows past the range are skipped (a uniform branch); written this
+        // way, the compiler's waits before each row count exactly the loads
+        // of the rows still ahead
+        if (i + b <= last) compute_row(buf[b], row_at(i + b));
       }
     }
-    if (!has2 && r + 1 < r_end) r -= 1;  // the second row was in the next problem
+    return;  // a wave serves one problem
   }
 }
 
-template <int J, bool DQ>
-hipError_t launch_j(const Gemv1Args &args, int grid, bool out_bf16, hipStream_t stream) {
+// Splits the waves of the launch among the problems in proportion to their
+// rows (each gets at least one, and no more than it has rows); returns the
+// grid size.
+template <int J>
+int assign_waves(Gemv1Args &args, int64_t rows) {
+  // at least two rows per wave; as many workgroups as fit on the chip at once
+  // (4 SIMDs per CU, each holding waves_per_simd waves of a workgroup)
+  const int64_t want = (rows + 2 * kWaves - 1) / (2 * kWaves);
+  const int64_t cap = (int64_t)device_cu_count() * (4 * waves_per_simd<J>() / kWaves);
+  int64_t grid = want < cap ? want : cap;
+  const int64_t min_grid = (args.count + kWaves - 1) / kWaves;
+  grid = grid > min_grid ? grid : min_grid;
+  const int64_t spare = grid * kWaves - args.count;  // beyond the one wave each
+  int wb = 0;
+  for (int i = 0; i < args.count; ++i) {
+    Gemv1Problem &p = args.p[i];
+    int64_t nw = p.N * spare / rows;
+    nw = nw < 1 ? 1 : (nw > p.N ? p.N : nw);
+    p.wave_begin = wb;
+    p.waves = (int)nw;
+    wb += (int)nw;
+  }
+  return (int)grid;
+}
+
+template <int J, bool DQ, bool BS32>
+hipError_t launch_j(Gemv1Args &args, int64_t rows, bool out_bf16, hipStream_t stream) {
+  // one row in flight while one computes: deeper prefetch measured no faster
+  // (the row's arithmetic, not memory latency, sets the pace)
+  constexpr int NBUF = 2;
+  const int grid = assign_waves<J>(args, rows);
   if (out_bf16)
-    hipLaunchKernelGGL((gemv1_kernel<J, DQ, true>), dim3(grid), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, args);
   else
-    hipLaunchKernelGGL((gemv1_kernel<J, DQ, false>), dim3(grid), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, args);
   return hipGetLastError();
 }
 
-template <bool DQ>
-hipError_t launch_dq(const Gemv1Args &args, int j, int grid, bool out_bf16, hipStream_t stream) {
+template <bool DQ, bool BS32>
+hipError_t launch_dq(Gemv1Args &args, int64_t rows, int j, bool out_bf16, hipStream_t stream) {
   switch (j) {
-    case 1: return launch_j<1, DQ>(args, grid, out_bf16, stream);
-    case 2: return launch_j<2, DQ>(args, grid, out_bf16, stream);
-    case 3: return launch_j<3, DQ>(args, grid, out_bf16, stream);
-    case 4: return launch_j<4, DQ>(args, grid, out_bf16, stream);
-    case 6: return launch_j<6, DQ>(args, grid, out_bf16, stream);
-    default: return launch_j<8, DQ>(args, grid, out_bf16, stream);
+    case 1: return launch_j<1, DQ, BS32>(args, rows, out_bf16, stream);
+    case 2: return launch_j<2, DQ, BS32>(args, rows, out_bf16, stream);
+    case 3: return launch_j<3, DQ, BS32>(args, rows, out_bf16, stream);
+    default: return launch_j<4, DQ, BS32>(args, rows, out_bf16, stream);
   }
 }
 
 }  // namespace
 
-int gemv1_max_k() { return 8 * kSlice; }
+int gemv1_max_k() { return 4 * kSlice; }
 
 hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type,
                                 bool double_quant, bool out_bf16, hipStream_t stream) {
@@ -224,6 +379,7 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
   args.count = 0;
   int64_t rows = 0;
   int max_k = 0;
+  bool bs32 = false;
   for (int i = 0; i < count; ++i) {
     const GemvDesc &d = descs[i];
     if (d.N == 0) continue;
@@ -238,22 +394,18 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
     p.K = d.K;
     p.log2_bs = __builtin_ctz((unsigned)d.blocksize);
     p.log2_bs2 = d.sc.log2_bs2;
-    p.row_begin = rows;
     rows += d.N;
     max_k = d.K > max_k ? d.K : max_k;
+    bs32 = bs32 || d.blocksize == 32;
   }
   if (args.count == 0) return hipSuccess;
-  args.total_rows = rows;
   for (int i = 0; i < 16; ++i) args.value[i] = t.value[i];
-  int j = (max_k + kSlice - 1) / kSlice;
-  if (j == 5) j = 6;
-  if (j == 7) j = 8;
-  // at least two rows per wave; two workgroups per CU (LDS-limited)
-  const int64_t want = (rows + 2 * kWaves - 1) / (2 * kWaves);
-  const int64_t cap = 2 * device_cu_count();
-  const int grid = (int)(want < cap ? want : cap);
-  return double_quant ? launch_dq<true>(args, j, grid, out_bf16, stream)
-                      : launch_dq<false>(args, j, grid, out_bf16, stream);
+  const int j = (max_k + kSlice - 1) / kSlice;
+  if (bs32)
+    return double_quant ? launch_dq<true, true>(args, rows, j, out_bf16, stream)
+                        : launch_dq<false, true>(args, rows, j, out_bf16, stream);
+  return double_quant ? launch_dq<true, false>(args, rows, j, out_bf16, stream)
+                      : launch_dq<false, false>(args, rows, j, out_bf16, stream);
 }
 
 }  // namespace nf4

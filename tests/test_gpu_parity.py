@@ -255,6 +255,20 @@ def test_gemv_ragged_shapes(nf4, orc, bs, dq):
         _gemv_case(nf4, orc, w, x, bs, "nf4", dq)
 
 
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemv_single_row_long_k(nf4, orc, bs, dq):
+    """M = 1 across row lengths that take one to four 4096-code slices per
+    lane group, ragged last slices, an odd number of blocks per row (bs 32:
+    a lane's two blocks can then straddle a double-quant group), the longest
+    row the single-row kernel takes and one code block past it."""
+    for i, K in enumerate([4096 + bs, 6144, 8192 + 3 * bs, 12288 + bs, 16384, 16384 + bs]):
+        N = 45 + i
+        w = workloads.normal_bf16((N, K), 0.02, 9100 + K + bs)
+        x = workloads.normal_bf16((1, K), 1.0, 9200 + K)
+        _gemv_case(nf4, orc, w, x, bs, "nf4", dq)
+
+
 @pytest.mark.parametrize("dq", [False, True])
 def test_gemv_grouped_matches_single_and_oracle(nf4, orc, dq):
     """One grouped launch over differently shaped products (two blocksizes,
