@@ -37,6 +37,26 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per launch measured by two rocprofv3 counter passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch) over this benchmark, each scaled by what the same
+# counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x
+# 1.000); the summary is profiles/bench_7b_stack_hbm_bytes.md. A figure holds only
+# for the kernel source it was taken on (its SHA-256); after any change to that
+# source the benchmark reports null until the counters are taken again.
+MEASURED_TRAFFIC = {
+    "gemv1.hip": ("2848113b8be9756f8dcffa3a69c0c6f1eb9b83c1c3a85c55e69f2b6c8a1ba117", 105570479),
+    "gemm.hip": ("3534be05539c4357a7f1376cfcac86d9f6c90abad45cdc79e6bc02dcb632736b", 356051140),
+}
+
+
+def measured_traffic(source):
+    import hashlib
+
+    digest, nbytes = MEASURED_TRAFFIC[source]
+    path = os.path.join(ROOT, "bit_weight_quantization_nf4_amd", "csrc", source)
+    with open(path, "rb") as f:
+        return nbytes if hashlib.sha256(f.read()).hexdigest() == digest else None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -47,7 +67,9 @@ def parse():
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemm")
+    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemm",
+                    help="comma list of quantize, dequantize, gemv, gemm; 'copy' adds a plain "
+                         "1 GiB device copy, the known-size reference for HBM byte counters")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch each phase eagerly instead of replaying a captured HIP graph")
     return ap.parse_args()
@@ -119,7 +141,16 @@ def main():
     def ph_gemm():
         nf4.gemm(px, pqs, out=py)
 
-    fns = dict(quantize=ph_quantize, dequantize=ph_dequantize, gemv=ph_gemv, gemm=ph_gemm)
+    copy_src = copy_dst = None
+    if "copy" in phases:
+        copy_src = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+        copy_dst = torch.empty_like(copy_src)
+
+    def ph_copy():
+        copy_dst.copy_(copy_src)
+
+    fns = dict(quantize=ph_quantize, dequantize=ph_dequantize, gemv=ph_gemv, gemm=ph_gemm,
+               copy=ph_copy)
 
     # ---- capture each phase in a graph (after an eager warm-up call)
     graphs = {}
@@ -193,6 +224,7 @@ def main():
     work["gemv"] = dict(bytes=gbytes, launches=len(layers))
     M = prefill.ms[0]
     work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols, launches=1)
+    work["copy"] = dict(bytes=2 * (1 << 30), launches=1)
 
     phase_out = {}
     for p in phases:
@@ -238,7 +270,7 @@ def main():
         result["roofline"] = {
             "kernel": "gemv1_kernel (NF4 decode GEMV, M=1, one launch per layer of 7 products)",
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gemv1.hip"),
             "per_launch_us": round(us, 3),
             "algorithmic_bytes_per_launch": per_launch,
         }
@@ -248,7 +280,7 @@ def main():
         result["roofline_gemm"] = {
             "kernel": "gemm_kernel (NF4 prefill GEMM)", "bound": "mfma", "achieved": round(tf, 1),
             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic("gemm.hip"),
             "per_launch_us": round(us, 3),
         }
     result["phases"] = phase_out
