@@ -238,6 +238,8 @@ nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t
   ScaleArgs sc;
   nf4_status st = check_product(x_bf16, M, w, N, K, compute_dtype, out_dtype, y, &sc);
   if (st != NF4_OK) return st;
+  // a tile's offsets into x, the codes and y are 32-bit
+  if (K > (1 << 22) || N > (1 << 21)) return NF4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return NF4_OK;
   st = check_device();
   if (st != NF4_OK) return st;

@@ -174,7 +174,8 @@ nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
 /* Prefill product, any M >= 1: the same contraction as nf4_gemv, computed with
  * bf16 matrix cores on dequantized weight tiles and fp32 accumulation [repo
  * page 0.50.0: fused 4-bit dequantize + GEMM in place of dequantize +
- * F.linear]. Same layouts and rules as nf4_gemv. */
+ * F.linear]. Same layouts and rules as nf4_gemv, except that M is any
+ * M >= 0, and K <= 2^22 and N <= 2^21 (NF4_ERR_UNSUPPORTED above). */
 nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                     int32_t compute_dtype, int32_t out_dtype, void *y, void *stream);
 

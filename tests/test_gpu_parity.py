@@ -295,7 +295,10 @@ def test_gemv_grouped_matches_single_and_oracle(nf4, orc, dq):
 def test_gemm_small_shapes(nf4, orc):
     for (M, N, K, bs, dq, qt) in [(1, 64, 64, 64, False, "nf4"), (5, 130, 256, 64, True, "nf4"),
                                   (128, 128, 128, 64, True, "fp4"), (130, 257, 96, 32, False, "nf4"),
-                                  (300, 200, 512, 128, True, "nf4"), (64, 1, 64, 64, False, "fp4")]:
+                                  (300, 200, 512, 128, True, "nf4"), (64, 1, 64, 64, False, "fp4"),
+                                  # double quant with more block scales per tile than the
+                                  # kernel stages on chip (bs 32, long rows)
+                                  (65, 230, 3072, 32, True, "nf4")]:
         w = workloads.normal_bf16((N, K), 0.02, M + N + K)
         x = workloads.normal_bf16((M, K), 1.0, M * N + K)
         qs, ref = check_quant(nf4, orc, w, bs, qt, dq)
