@@ -157,6 +157,9 @@ nf4_status nf4_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_
   nf4_status st = check_device();
   if (st != NF4_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (double_quant && quantize_dq_fused(blocksize, 256))
+    return from_hip(launch_quantize_dq(static_cast<const uint16_t *>(w_bf16), n, blocksize,
+                                       quant_type, packed, absmax, absmax_q, absmax_scale, s));
   st = from_hip(launch_quantize(static_cast<const uint16_t *>(w_bf16), n, blocksize, quant_type,
                                 packed, absmax, s));
   if (st != NF4_OK || !double_quant) return st;

@@ -15,6 +15,14 @@ hipError_t launch_quantize(const uint16_t *w, int64_t n, int blocksize, int quan
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int blocksize2, int8_t *q,
                                float *s2, hipStream_t stream);
 
+// Quantization and double quantization (groups of blocksize2 scales) in one
+// launch, for the pairs where quantize_dq_fused() is true; results equal
+// launch_quantize followed by launch_double_quant.
+bool quantize_dq_fused(int blocksize, int blocksize2);
+hipError_t launch_quantize_dq(const uint16_t *w, int64_t n, int blocksize, int quant_type,
+                              uint8_t *packed, float *absmax, int8_t *absmax_q,
+                              float *absmax_scale, hipStream_t stream);
+
 hipError_t launch_dequantize(const uint8_t *packed, int64_t n, int blocksize, int quant_type,
                              const ScaleArgs &sc, bool out_bf16, void *out, hipStream_t stream);
 

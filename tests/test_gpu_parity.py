@@ -155,6 +155,21 @@ def test_quantize_blocksizes_and_ragged_lengths(nf4, orc, bs):
             check_dequant(nf4, orc, qs, ref, bs, qt, n > 300)
 
 
+@pytest.mark.parametrize("bs", [64, 128, 256])
+def test_quantize_with_double_quant_groups(nf4, orc, bs):
+    """Quantization with double quantization in one pass: whole and ragged
+    groups of 256 blocks, an all-zero group and one whose largest scale sits
+    in its last block, and more groups than one launch has workgroups (each
+    then loops over several groups)."""
+    g = 256 * bs
+    for n in (g, 3 * g + 5 * bs + 17, 2 * g - 1, 2049 * g + 3 * bs + 1):
+        w = workloads.normal_bf16((n,), 0.02, 31 * n + bs).float()
+        w[g:2 * g] = 0.0
+        if n > 3 * g:
+            w[3 * g - 1] = 4.0
+        check_quant(nf4, orc, w.to(torch.bfloat16), bs, "nf4", True)
+
+
 def test_quantize_empty(nf4):
     qs = nf4.quantize(torch.empty(0, dtype=torch.bfloat16, device="cuda"), 64, "nf4", True)
     assert qs.packed.numel() == 0 and qs.absmax.numel() == 0
