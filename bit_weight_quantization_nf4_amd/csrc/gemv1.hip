@@ -16,6 +16,11 @@
 //    their rows, and each wave takes a contiguous range of one problem's rows,
 //    so a wave loads its activations once; it keeps the loads of the next row
 //    in flight while it computes the current one;
+//  - start-up: a wave finds its problem with one batch of scalar loads and
+//    issues its activation and first-row loads before the workgroup builds
+//    the table, so their latency overlaps the table build and the barrier;
+//  - balance: a wave's issue priority falls as its rows get done, so the
+//    waves sharing a SIMD finish together instead of oldest-first;
 //  - dequantization: the same conflict-free LDS pair table as the batched
 //    kernel (entry = fp32 code values of both nibbles of a code byte, one copy
 //    per bank pair, address built by one v_perm_b32), times the block scale,
@@ -30,8 +35,6 @@
 namespace nf4 {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kSlice = 4096;           // codes of one row per slice (64 per lane)
 constexpr int kCopies = 32;            // interleaved copies of the pair table
 constexpr int kTableBytes = 256 * 256; // 256 entries x 256-byte rows
@@ -52,13 +55,19 @@ struct Gemv1Problem {
   const float *absmax_scale;
   int32_t N, K;
   int32_t log2_bs, log2_bs2;
-  int32_t wave_begin, waves;  // the waves of the launch that share this problem's rows
 };
 
+// The fields every wave reads first (code values, wave ranges, row counts)
+// lead the argument block, so one batch of scalar loads brings them all.
 struct Gemv1Args {
+  float value[16];
+  // problem i (of N = rows[i] rows) is served by launch waves wave_begin[i] ..
+  // wave_begin[i] + waves[i] - 1; unused entries have waves[i] = 0
+  int32_t wave_begin[kMaxGroup];
+  int32_t waves[kMaxGroup];
+  int32_t rows[kMaxGroup];
   Gemv1Problem p[kMaxGroup];
   int32_t count;
-  float value[16];
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -122,45 +131,74 @@ struct RowLoads {
 template <int J>
 constexpr int waves_per_simd() { return J == 1 ? 4 : 2; }
 
+// Two workgroups share a CU (each holds a 64 KB pair table and half of every
+// SIMD's waves).
+template <int J>
+constexpr int block_waves() { return 2 * waves_per_simd<J>(); }
+
 template <int J, int NBUF, bool DQ, bool BS32, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(64 * block_waves<J>())
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<J>(), waves_per_simd<J>())))
 void gemv1_kernel(Gemv1Args args) {
-  constexpr int NS = BS32 ? 2 : 1;  // scales per lane per slice
+  constexpr int kWaves = block_waves<J>();
+  constexpr int kThreads = 64 * kWaves;
   __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
-  // Pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy.
-  // Consecutive threads write consecutive copies (no bank conflicts).
-  for (int idx = threadIdx.x; idx < 256 * kCopies; idx += kThreads) {
-    const int e = idx / kCopies, copy = idx % kCopies;
-    const f32x2 v = {args.value[e >> 4], args.value[e & 15]};
-    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * copy) = v;
-  }
-  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
   // wave index made explicitly uniform, so row bookkeeping stays scalar
-  const int wave = (int)blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wave_in_block = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wave = (int)blockIdx.x * kWaves + wave_in_block;
 
   // Each problem has its own set of waves, each with a contiguous range of
-  // that problem's rows (a uniform loop finds it, so every problem field is a
-  // scalar). A wave never switches problems, so its prefetch never restarts.
-  for (int pi = 0; pi < args.count; ++pi) {
-    const int w = wave - args.p[pi].wave_begin;
-    if (w < 0 || w >= args.p[pi].waves) continue;
-    const int64_t Np = args.p[pi].N, nw = args.p[pi].waves;
+  // that problem's rows. The wave finds its problem with independent scalar
+  // loads of the wave ranges (no chain of dependent argument loads), so
+  // every wave issues its first memory loads equally early. A wave never
+  // switches problems, so its prefetch never restarts. A wave without rows
+  // (small launches) still builds its share of the table.
+  int wb[kMaxGroup], wn[kMaxGroup], wr[kMaxGroup];
+  float val[16];
+#pragma unroll
+  for (int i = 0; i < kMaxGroup; ++i) {
+    wb[i] = args.wave_begin[i];
+    wn[i] = args.waves[i];
+    wr[i] = args.rows[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) val[i] = args.value[i];
+  // keep these loads in the first batch, ahead of the wave's vector loads
+  __builtin_amdgcn_sched_barrier(0);
+  int pi = -1, w = 0, nwv = 1, nrows = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxGroup; ++i) {
+    const int d = wave - wb[i];
+    const bool hit = d >= 0 && d < wn[i];
+    pi = hit ? i : pi;
+    w = hit ? d : w;
+    nwv = hit ? wn[i] : nwv;
+    nrows = hit ? wr[i] : nrows;
+  }
+  {
+    const bool has_problem = pi >= 0;
+    if (!has_problem) pi = 0;
+    const int64_t Np = nrows, nw = nwv;
     // this wave's rows of the problem: row(i) = first + i * stride, i < cnt
     int64_t first, stride, cnt;
     if (kInterleave) {  // the problem's waves sweep its rows side by side
       first = w;
       stride = nw;
       cnt = (Np - w + nw - 1) / nw;
-    } else {  // a contiguous range per wave
-      first = w * Np / nw;
+    } else {  // a contiguous range per wave: rows [w N / nw, (w + 1) N / nw)
+      // in 32-bit pieces: w N / nw = w q + w r / nw with N = q nw + r, w r < nw^2
+      const uint32_t q = (uint32_t)nrows / (uint32_t)nwv, r = (uint32_t)nrows % (uint32_t)nwv;
+      const uint32_t f0 = (uint32_t)w * q + ((uint32_t)w * r) / (uint32_t)nwv;
+      const uint32_t f1 = (uint32_t)(w + 1) * q + ((uint32_t)(w + 1) * r) / (uint32_t)nwv;
+      first = f0;
       stride = 1;
-      cnt = (w + 1) * Np / nw - first;
+      cnt = (int64_t)f1 - (int64_t)f0;
     }
-    if (cnt <= 0) continue;
+    if (!has_problem) cnt = 0;
+    const bool active = cnt > 0;
     const uint16_t *x = args.p[pi].x;
     const uint8_t *packed = args.p[pi].packed;
     const float *absmax = args.p[pi].absmax;
@@ -297,12 +335,42 @@ void gemv1_kernel(Gemv1Args args) {
     // NBUF rows with one straight-line body; every prefetch is unconditional
     // (clamped to the last row), so the wait before a row counts only that
     // row's own loads.
-    const int64_t last = cnt - 1;
+    // (a wave without rows prefetches a valid row, first, and computes none)
+    const int64_t last = cnt > 0 ? cnt - 1 : 0;
     auto row_at = [&](int64_t i) { return first + (i < last ? i : last) * stride; };
     RowLoads<J, BS32> buf[NBUF];
 #pragma unroll
     for (int b = 0; b + 1 < NBUF; ++b) buf[b] = load_row(row_at(b));
+
+    // Pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy,
+    // built while the first loads are in flight, two copies per 16-byte
+    // store; consecutive threads write consecutive copies (no bank
+    // conflicts). The 64 stores of a wave cover entries base .. base + 3, so
+    // value[e >> 4] is one scalar and value[e & 15] one of four.
+#pragma unroll
+    for (int k = 0; k < 256 * kCopies / 2 / kThreads; ++k) {
+      const int base = (k * kThreads + 64 * wave_in_block) / (kCopies / 2);
+      const int q = lane / (kCopies / 2);
+      const float hi = val[base >> 4];
+      const float l0 = val[base & 15], l1 = val[(base & 15) + 1];
+      const float l2 = val[(base & 15) + 2], l3 = val[(base & 15) + 3];
+      const float lo = q == 0 ? l0 : (q == 1 ? l1 : (q == 2 ? l2 : l3));
+      const f32x4 v = {hi, lo, hi, lo};
+      *reinterpret_cast<f32x4 *>(tbl + 256 * (base + q) + 16 * (lane % (kCopies / 2))) = v;
+    }
+    __syncthreads();
+    if (!active) return;
+    // Issue priority falls as the wave's rows get done (four steps): a SIMD
+    // otherwise issues for its oldest wave first, so its waves finish one
+    // after another and the last runs alone, waiting on memory; with waves
+    // that are behind going first they finish together (and late starters
+    // catch up).
+    const int64_t q1 = cnt / 4, q2 = cnt / 2, q3 = (3 * cnt) / 4;
     for (int64_t i = 0; i < cnt; i += NBUF) {
+      if (i < q1) __builtin_amdgcn_s_setprio(3);
+      else if (i < q2) __builtin_amdgcn_s_setprio(2);
+      else if (i < q3) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
 #pragma unroll
       for (int b = 0; b < NBUF; ++b) {
         buf[(b + NBUF - 1) % NBUF] = load_row(row_at(i + b + NBUF - 1));
@@ -312,7 +380,6 @@ void gemv1_kernel(Gemv1Args args) {
         if (i + b <= last) compute_row(buf[b], row_at(i + b));
       }
     }
-    return;  // a wave serves one problem
   }
 }
 
@@ -321,8 +388,8 @@ void gemv1_kernel(Gemv1Args args) {
 // grid size.
 template <int J>
 int assign_waves(Gemv1Args &args, int64_t rows) {
+  constexpr int kWaves = block_waves<J>();
   // at least two rows per wave; as many workgroups as fit on the chip at once
-  // (4 SIMDs per CU, each holding waves_per_simd waves of a workgroup)
   const int64_t want = (rows + 2 * kWaves - 1) / (2 * kWaves);
   const int64_t cap = (int64_t)device_cu_count() * (4 * waves_per_simd<J>() / kWaves);
   int64_t grid = want < cap ? want : cap;
@@ -334,8 +401,9 @@ int assign_waves(Gemv1Args &args, int64_t rows) {
     Gemv1Problem &p = args.p[i];
     int64_t nw = p.N * spare / rows;
     nw = nw < 1 ? 1 : (nw > p.N ? p.N : nw);
-    p.wave_begin = wb;
-    p.waves = (int)nw;
+    args.wave_begin[i] = wb;
+    args.waves[i] = (int)nw;
+    args.rows[i] = p.N;
     wb += (int)nw;
   }
   return (int)grid;
@@ -348,11 +416,11 @@ hipError_t launch_j(Gemv1Args &args, int64_t rows, bool out_bf16, hipStream_t st
   constexpr int NBUF = 2;
   const int grid = assign_waves<J>(args, rows);
   if (out_bf16)
-    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, true>), dim3(grid), dim3(kThreads), 0,
-                       stream, args);
+    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, true>), dim3(grid),
+                       dim3(64 * block_waves<J>()), 0, stream, args);
   else
-    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, false>), dim3(grid), dim3(kThreads), 0,
-                       stream, args);
+    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, false>), dim3(grid),
+                       dim3(64 * block_waves<J>()), 0, stream, args);
   return hipGetLastError();
 }
 
@@ -377,6 +445,11 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
   const CodeTables &t = code_tables(quant_type);
   Gemv1Args args;
   args.count = 0;
+  for (int i = 0; i < kMaxGroup; ++i) {
+    args.wave_begin[i] = 0;
+    args.waves[i] = 0;
+    args.rows[i] = 0;
+  }
   int64_t rows = 0;
   int max_k = 0;
   bool bs32 = false;
