@@ -229,11 +229,24 @@ nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
   if (st != NF4_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const bool dq = w[0].double_quant != 0, bf16_out = out_dtype == NF4_DTYPE_BF16;
-  bool short_k = true;
-  for (int i = 0; i < count; ++i) short_k = short_k && K[i] <= gemv1_max_k();
-  if (M == 1 && short_k)
-    return from_hip(launch_gemv1_grouped(count, descs, w[0].quant_type, dq, bf16_out, s));
-  return from_hip(launch_gemv_grouped(count, descs, M, w[0].quant_type, dq, bf16_out, s));
+  if (M > 1)
+    return from_hip(launch_gemv_grouped(count, descs, M, w[0].quant_type, dq, bf16_out, s));
+  // M = 1: the single-row kernel takes the rows it can, the batched kernel the
+  // longer ones (one launch each), so every product is computed exactly as
+  // it would be on its own
+  GemvDesc one[NF4_GEMV_MAX_GROUP], many[NF4_GEMV_MAX_GROUP];
+  int n_one = 0, n_many = 0;
+  for (int i = 0; i < count; ++i) {
+    if (K[i] <= gemv1_max_k()) one[n_one++] = descs[i];
+    else many[n_many++] = descs[i];
+  }
+  if (n_one > 0) {
+    st = from_hip(launch_gemv1_grouped(n_one, one, w[0].quant_type, dq, bf16_out, s));
+    if (st != NF4_OK) return st;
+  }
+  if (n_many > 0)
+    st = from_hip(launch_gemv_grouped(n_many, many, 1, w[0].quant_type, dq, bf16_out, s));
+  return st;
 }
 
 nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,

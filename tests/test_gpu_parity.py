@@ -285,11 +285,25 @@ def test_gemv_single_row_long_k(nf4, orc, bs, dq):
 
 
 @pytest.mark.parametrize("dq", [False, True])
+def test_gemv_batched_tile_counts(nf4, orc, dq):
+    """Batched decode from a handful to thousands of 16-row tiles (more work
+    items than workgroups, so each workgroup takes several in turn), with
+    ragged rows and a ragged last 128-code step."""
+    for (N, K, M) in [(2001, 1088, 16), (20000, 512, 2), (40000, 256, 5), (70007, 128, 16),
+                      (100, 256, 3)]:
+        w = workloads.normal_bf16((N, K), 0.02, 4200 + N + K)
+        x = workloads.normal_bf16((M, K), 1.0, 4300 + N + M)
+        _gemv_case(nf4, orc, w, x, 64, "nf4", dq)
+
+
+@pytest.mark.parametrize("dq", [False, True])
 def test_gemv_grouped_matches_single_and_oracle(nf4, orc, dq):
-    """One grouped launch over differently shaped products (two blocksizes,
-    ragged rows): each result is bitwise the single-product result and within
-    tolerance of the oracle."""
-    shapes = [(4096, 4096, 64), (1000, 512, 128), (33, 160, 32), (11008, 4096, 64), (16, 64, 64)]
+    """One grouped call over differently shaped products (three blocksizes,
+    ragged rows, one row longer than the single-row kernel takes): each
+    result is bitwise the single-product result and within tolerance of the
+    oracle."""
+    shapes = [(4096, 4096, 64), (1000, 512, 128), (33, 160, 32), (11008, 4096, 64), (16, 64, 64),
+              (40, 16448, 64)]
     for M in (1, 3, 16):
         qss, xs, refs = [], [], []
         for i, (N, K, bs) in enumerate(shapes):
