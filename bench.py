@@ -7,7 +7,12 @@ double quantization at blocksize 64 by default):
   2. dequantize every weight to bf16,
   3. decode GEMV (M = 1, independent seeded x per matrix) through every weight,
   4. one prefill GEMM, X[2048, 4096] . W[14336, 4096]^T (NF4 bs 64 + double
-     quant, fp32 accumulation, bf16 output).
+     quant, fp32 accumulation, bf16 output),
+then the same three stack phases at the other blocksizes of the sweep (128,
+256), and the MLP-shaped decode products one matrix per launch: W [11008, 4096]
+and [4096, 11008], NF4 bs 64 + double quant, M in {1, 4, 8, 16}, each timed
+over a rotation of distinct weights (> 1 GB, so HBM, not the 256 MB last-level
+cache, serves them).
 Inputs are generated on the GPU from seeded generators and are resident in HBM
 before timing. Each phase is captured once in a HIP graph and replayed (or,
 with --no-graph, launched eagerly); HIP events between phases give per-phase
@@ -44,7 +49,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # for the kernel source it was taken on (its SHA-256); after any change to that
 # source the benchmark reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "gemv1.hip": ("2848113b8be9756f8dcffa3a69c0c6f1eb9b83c1c3a85c55e69f2b6c8a1ba117", 105572969),
+    "gemv1.hip": ("d5ce77939b9b15c8c6af873cec5ec4ca05bde8d5bd9cfe3b2b0f1cc91a9a04eb", 105753472),
     "gemm.hip": ("9baba3229fe56ef6578454664ee507889d01c24c6ecf3f90b460d01eee38ba0a", 335843173),
 }
 
@@ -61,15 +66,18 @@ def measured_traffic(source):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--bs", type=int, default=64, choices=[32, 64, 128, 256, 512, 1024, 2048, 4096])
     ap.add_argument("--layers", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemm",
-                    help="comma list of quantize, dequantize, gemv, gemm; 'copy' adds a plain "
-                         "1 GiB device copy, the known-size reference for HBM byte counters")
+    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemm,sweep,mlp",
+                    help="comma list of quantize, dequantize, gemv, gemm (the stack at --bs), "
+                         "sweep (quantize, dequantize and gemv at the other blocksizes of "
+                         "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16); "
+                         "'copy' adds a plain 1 GiB device copy, the known-size reference "
+                         "for HBM byte counters")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch each phase eagerly instead of replaying a captured HIP graph")
     return ap.parse_args()
@@ -93,7 +101,14 @@ def main():
         raise RuntimeError("device 0 is not gfx950")
     dev = torch.device("cuda", 0)
     bs = args.bs
-    phases = args.phases.split(",")
+    requested = args.phases.split(",")
+    sweep_bs = [b for b in (64, 128, 256) if b != bs] if "sweep" in requested else []
+    mlp_ms = (1, 4, 8, 16) if "mlp" in requested else ()
+    phases = [p for p in requested if p not in ("sweep", "mlp")]
+    for b in sweep_bs:
+        phases += [f"quantize_bs{b}", f"dequantize_bs{b}", f"gemv_bs{b}"]
+    for m in mlp_ms:
+        phases += [f"mlp_up_m{m}", f"mlp_down_m{m}"]
 
     stack = workloads.stack_7b(args.layers)
     prefill = workloads.PREFILL
@@ -114,6 +129,12 @@ def main():
         mats.append(dict(spec=m, w=w, x=x, qs=qs,
                          wd=torch.empty_like(w),
                          y=torch.empty((1, m.rows), dtype=torch.float32, device=dev)))
+    # the other blocksizes of the sweep share the bf16 weights and outputs
+    for d in mats:
+        d["qs_bs"] = {b: nf4.quantize(d["w"], b, "nf4", double_quant=True) for b in sweep_bs}
+        d["qs_bs"][bs] = d["qs"]
+        d["y_bs"] = {b: torch.empty_like(d["y"]) for b in sweep_bs}
+        d["y_bs"][bs] = d["y"]
     pm = prefill.matrices[0]
     pw = gpu_normal((pm.rows, pm.cols), pm.sigma, pm.seed)
     px = gpu_normal((prefill.ms[0], pm.cols), 1.0, prefill.x_seed)
@@ -121,25 +142,58 @@ def main():
     py = torch.empty((prefill.ms[0], pm.rows), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
 
-    def ph_quantize():
-        for d in mats:
-            nf4.quantize(d["w"], bs, "nf4", True, out=d["qs"])
-        nf4.quantize(pw, 64, "nf4", True, out=pqs)
+    def quantize_at(b, with_prefill):
+        def f():
+            for d in mats:
+                nf4.quantize(d["w"], b, "nf4", True, out=d["qs_bs"][b])
+            if with_prefill:
+                nf4.quantize(pw, 64, "nf4", True, out=pqs)
+        return f
 
-    def ph_dequantize():
-        for d in mats:
-            nf4.dequantize(d["qs"], out=d["wd"])
+    def dequantize_at(b):
+        def f():
+            for d in mats:
+                nf4.dequantize(d["qs_bs"][b], out=d["wd"])
+        return f
 
     # decode GEMV: the seven independent products of a layer share one launch
     layers = [mats[i:i + 7] for i in range(0, len(mats), 7)]
 
-    def ph_gemv():
-        for grp in layers:
-            nf4.gemv_grouped([d["x"] for d in grp], [d["qs"] for d in grp],
-                             outs=[d["y"] for d in grp])
+    def gemv_at(b):
+        def f():
+            for grp in layers:
+                nf4.gemv_grouped([d["x"] for d in grp], [d["qs_bs"][b] for d in grp],
+                                 outs=[d["y_bs"][b] for d in grp])
+        return f
 
     def ph_gemm():
         nf4.gemm(px, pqs, out=py)
+
+    # MLP-shaped products, one matrix per launch, rotating over distinct
+    # weights: the stack's [11008, 4096] matrices (bs 64), and 48 seeded
+    # [4096, 11008] ones
+    mlp = {}
+    if mlp_ms:
+        up = [d["qs_bs"][64] if 64 in d["qs_bs"] else nf4.quantize(d["w"], 64, "nf4", True)
+              for d in mats if d["spec"].rows == 11008]
+        down = []
+        for r in range(48):
+            w = gpu_normal((4096, 11008), 0.02, 7000 + r)
+            down.append(nf4.quantize(w, 64, "nf4", double_quant=True))
+            del w
+        for m in mlp_ms:
+            for name, qss, N, K in (("up", up, 11008, 4096), ("down", down, 4096, 11008)):
+                x = gpu_normal((m, K), 1.0, 7100 + m + K)
+                y = torch.empty((m, N), dtype=torch.float32, device=dev)
+                mlp[f"mlp_{name}_m{m}"] = dict(qss=qss, x=x, y=y, N=N, K=K, M=m)
+
+    def mlp_at(key):
+        e = mlp[key]
+
+        def f():
+            for q in e["qss"]:
+                nf4.gemv(e["x"], q, out=e["y"])
+        return f
 
     copy_src = copy_dst = None
     if "copy" in phases:
@@ -149,8 +203,14 @@ def main():
     def ph_copy():
         copy_dst.copy_(copy_src)
 
-    fns = dict(quantize=ph_quantize, dequantize=ph_dequantize, gemv=ph_gemv, gemm=ph_gemm,
-               copy=ph_copy)
+    fns = dict(quantize=quantize_at(bs, True), dequantize=dequantize_at(bs), gemv=gemv_at(bs),
+               gemm=ph_gemm, copy=ph_copy)
+    for b in sweep_bs:
+        fns[f"quantize_bs{b}"] = quantize_at(b, False)
+        fns[f"dequantize_bs{b}"] = dequantize_at(b)
+        fns[f"gemv_bs{b}"] = gemv_at(b)
+    for key in mlp:
+        fns[key] = mlp_at(key)
 
     # ---- capture each phase in a graph (after an eager warm-up call)
     graphs = {}
@@ -196,6 +256,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = {p: sum(a.elapsed_time(b) for a, b in ev[p]) / args.steps for p in phases}
+    ms_sorted = {p: sorted(a.elapsed_time(b) for a, b in ev[p]) for p in phases}
 
 
     # ---- algorithmic work per step
@@ -206,22 +267,46 @@ def main():
     n_stack = sum(d["spec"].rows * d["spec"].cols for d in mats)
     n_pre = pm.rows * pm.cols
     work = {}
-    # quantize: read bf16, write codes + fp32 absmax; double quant: read absmax, write int8 + fp32
-    qbytes = 0
-    qlaunches = 0
-    for n, b in [(d["spec"].rows * d["spec"].cols, bs) for d in mats] + [(n_pre, 64)]:
-        nb = -(-n // b)
-        qbytes += 2 * n + (n + 1) // 2 + 4 * nb + 4 * nb + nb + 4 * (-(-nb // 256))
-        qlaunches += 2
-    work["quantize"] = dict(bytes=qbytes, launches=qlaunches)
-    work["dequantize"] = dict(bytes=sum((n + 1) // 2 + meta_bytes(n, bs) + 2 * n
-                                        for n in (d["spec"].rows * d["spec"].cols for d in mats)),
-                              launches=len(mats))
-    gbytes = 0
-    for d in mats:
-        N, K = d["spec"].rows, d["spec"].cols
-        gbytes += N * K // 2 + meta_bytes(N * K, bs) + 2 * K + 4 * N
-    work["gemv"] = dict(bytes=gbytes, launches=len(layers))
+
+    def quantize_work(b, with_prefill):
+        # read bf16, write codes, fp32 absmax, int8 scale and fp32 group scale;
+        # blocksizes 64/128/256 do both levels in one pass, the others read
+        # the fp32 absmax back in a second launch
+        fused = b in (64, 128, 256)
+        nbytes, launches = 0, 0
+        sizes = [(d["spec"].rows * d["spec"].cols, b) for d in mats]
+        if with_prefill:
+            sizes.append((n_pre, 64))
+        for n, bb in sizes:
+            nb = -(-n // bb)
+            nbytes += 2 * n + (n + 1) // 2 + 4 * nb + nb + 4 * (-(-nb // 256))
+            nbytes += 0 if fused else 4 * nb
+            launches += 1 if fused else 2
+        return dict(bytes=nbytes, launches=launches)
+
+    def dequantize_work(b):
+        return dict(bytes=sum((n + 1) // 2 + meta_bytes(n, b) + 2 * n
+                              for n in (d["spec"].rows * d["spec"].cols for d in mats)),
+                    launches=len(mats))
+
+    def gemv_work(b):
+        nbytes = 0
+        for d in mats:
+            N, K = d["spec"].rows, d["spec"].cols
+            nbytes += N * K // 2 + meta_bytes(N * K, b) + 2 * K + 4 * N
+        return dict(bytes=nbytes, launches=len(layers))
+
+    work["quantize"] = quantize_work(bs, True)
+    work["dequantize"] = dequantize_work(bs)
+    work["gemv"] = gemv_work(bs)
+    for b in sweep_bs:
+        work[f"quantize_bs{b}"] = quantize_work(b, False)
+        work[f"dequantize_bs{b}"] = dequantize_work(b)
+        work[f"gemv_bs{b}"] = gemv_work(b)
+    for key, e in mlp.items():
+        N, K, m = e["N"], e["K"], e["M"]
+        per = N * K // 2 + meta_bytes(N * K, 64) + 2 * m * K + 4 * m * N
+        work[key] = dict(bytes=per * len(e["qss"]), launches=len(e["qss"]))
     M = prefill.ms[0]
     work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols, launches=1)
     work["copy"] = dict(bytes=2 * (1 << 30), launches=1)
@@ -230,16 +315,19 @@ def main():
     for p in phases:
         t = ms[p] / 1e3
         w = work[p]
+        srt = ms_sorted[p]
+        spread = dict(ms_median=round(srt[len(srt) // 2], 4), ms_min=round(srt[0], 4))
         if "bytes" in w:
             gbs = w["bytes"] / t / 1e9
             phase_out[p] = dict(ms=round(ms[p], 4), gb_per_s=round(gbs, 1),
                                 hbm_frac=round(gbs / HBM_PEAK_GBS, 4), launches=w["launches"],
-                                algorithmic_bytes=w["bytes"])
+                                per_launch_us=round(ms[p] * 1e3 / w["launches"], 3),
+                                algorithmic_bytes=w["bytes"], **spread)
         else:
             tf = w["flops"] / t / 1e12
             phase_out[p] = dict(ms=round(ms[p], 4), tflops=round(tf, 1),
                                 mfma_frac=round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                                launches=w["launches"], flops=w["flops"])
+                                launches=w["launches"], flops=w["flops"], **spread)
 
     gemv_gbs = phase_out.get("gemv", {}).get("gb_per_s")
     result = {
@@ -261,6 +349,9 @@ def main():
                         "matrix (the 7 products of a layer in one grouped launch); + prefill GEMM 2048x4096x14336 NF4 bs64 + double quant",
             "blocksize": bs, "quant_type": "nf4", "double_quant": True,
             "stack_params": n_stack, "gemv_m": 1, "gemm_mnk": [M, pm.rows, pm.cols],
+            "also_timed": "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
+                          "[11008,4096] (up) and [4096,11008] (down) NF4 bs64 + double quant, "
+                          "one product per launch over >1 GB of distinct weights, M = 1/4/8/16",
         },
     }
     if "gemv" in phase_out:
