@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           xa[i][s] = __builtin_bit_cast(
-              uint4, __builtin_amdgcn_raw_buffer_load_b128(xres, xoff, 16 * s, 0));
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                         xres, (int)((uint32_t)xoff + 16u * s), 0, 0));
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
           pw[i][g] = *reinterpret_cast<const uint4 *>(prow[g] + kc / 2);

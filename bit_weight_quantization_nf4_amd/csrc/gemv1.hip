@@ -12,13 +12,18 @@
 //    load instruction streams 1 KB of one row, one block scale per lane covers
 //    them (two at blocksize 32), and the lane's activations x[k .. k+63] stay
 //    in registers for every row of the problem;
-//  - the waves of the launch are split among its problems in proportion to
-//    their rows, and each wave takes a contiguous range of one problem's rows,
-//    so a wave loads its activations once; it keeps the loads of the next row
-//    in flight while it computes the current one;
-//  - start-up: a wave finds its problem with one batch of scalar loads and
-//    issues its activation and first-row loads before the workgroup builds
-//    the table, so their latency overlaps the table build and the barrier;
+//  - the workgroups of the launch (8 waves each) are split among its problems
+//    in proportion to their rows; a workgroup takes a contiguous range of one
+//    problem's rows and each of its waves a contiguous share of that, so
+//    every wave streams whole rows in address order. A wave keeps the loads
+//    of the next row in flight while it computes the current one;
+//  - x is fetched once per workgroup (16 bytes per thread per 4096-code
+//    slice) and handed to the waves through LDS, instead of every wave
+//    fetching all of it: the start-up traffic of a wave is its first rows,
+//    not the activation vector;
+//  - start-up: a workgroup finds its problem with one batch of scalar loads
+//    and issues its activation and first-row loads before it builds the
+//    table, so their latency overlaps the table build and the barrier;
 //  - balance: a wave's issue priority falls as its rows get done, so the
 //    waves sharing a SIMD finish together instead of oldest-first;
 //  - dequantization: the same conflict-free LDS pair table as the batched
@@ -26,8 +31,9 @@
 //    per bank pair, address built by one v_perm_b32), times the block scale,
 //    rounded to bf16 pairs with v_cvt_pk_bf16_f32 -- the dequantize kernel's
 //    bf16 weights -- then v_dot2_f32_bf16 with the bf16 activations. This
-//    arithmetic (about 19 VALU cycles per two weights), not HBM, sets the
-//    kernel's pace;
+//    arithmetic (about 15 VALU cycles per code byte, i.e. per two weights, at
+//    the ~1.9 GHz the chip holds under this load) keeps the SIMDs about 90 %
+//    busy in the main loop: the VALU, not HBM, sets the kernel's pace;
 //  - a row ends with a fixed-order DPP reduction across the wave (no atomics),
 //    so results are bitwise reproducible.
 #include "nf4_internal.h"
@@ -39,10 +45,6 @@ constexpr int kSlice = 4096;           // codes of one row per slice (64 per lan
 constexpr int kCopies = 32;            // interleaved copies of the pair table
 constexpr int kTableBytes = 256 * 256; // 256 entries x 256-byte rows
 constexpr int kMaxGroup = 16;
-// false: each wave takes a contiguous range of its problem's rows; true: rows
-// go to the problem's waves round-robin (row w, w + waves, ...). Both measure
-// the same; contiguous ranges keep each wave's reads sequential.
-constexpr bool kInterleave = false;
 // Word 3 of a raw (untyped, unswizzled) buffer resource on gfx9.
 constexpr int kBufferFlags = 0x00020000;
 
@@ -61,10 +63,10 @@ struct Gemv1Problem {
 // lead the argument block, so one batch of scalar loads brings them all.
 struct Gemv1Args {
   float value[16];
-  // problem i (of N = rows[i] rows) is served by launch waves wave_begin[i] ..
-  // wave_begin[i] + waves[i] - 1; unused entries have waves[i] = 0
-  int32_t wave_begin[kMaxGroup];
-  int32_t waves[kMaxGroup];
+  // problem i (of N = rows[i] rows) is served by workgroups wg_begin[i] ..
+  // wg_begin[i] + wgs[i] - 1; unused entries have wgs[i] = 0
+  int32_t wg_begin[kMaxGroup];
+  int32_t wgs[kMaxGroup];
   int32_t rows[kMaxGroup];
   Gemv1Problem p[kMaxGroup];
   int32_t count;
@@ -131,24 +133,26 @@ struct RowLoads {
 template <int J>
 constexpr int waves_per_simd() { return J == 1 ? 4 : 2; }
 
-// Two workgroups share a CU (each holds a 64 KB pair table and half of every
-// SIMD's waves).
+// A workgroup is 8 waves: two share a CU when a SIMD holds 4 waves, one
+// fills it when it holds 2.
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 template <int J>
-constexpr int block_waves() { return 2 * waves_per_simd<J>(); }
+constexpr int wgs_per_cu() { return 4 * waves_per_simd<J>() / kWaves; }
 
 template <int J, int NBUF, bool DQ, bool BS32, bool OUT_BF16>
-__global__ __launch_bounds__(64 * block_waves<J>())
+__global__ __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(waves_per_simd<J>(), waves_per_simd<J>())))
 void gemv1_kernel(Gemv1Args args) {
-  constexpr int kWaves = block_waves<J>();
-  constexpr int kThreads = 64 * kWaves;
   __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
+  // x of the workgroup's problem, slice j at 8 KB j; lane l's 16-byte piece
+  // q of a slice sits at index 64 q + l, so each piece read is conflict-free
+  __shared__ uint4 xs[J * 512];
 
   const int lane = threadIdx.x & 63;
   const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
   // wave index made explicitly uniform, so row bookkeeping stays scalar
   const int wave_in_block = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int wave = (int)blockIdx.x * kWaves + wave_in_block;
 
   // Each problem has its own set of waves, each with a contiguous range of
   // that problem's rows. The wave finds its problem with independent scalar
@@ -160,43 +164,40 @@ void gemv1_kernel(Gemv1Args args) {
   float val[16];
 #pragma unroll
   for (int i = 0; i < kMaxGroup; ++i) {
-    wb[i] = args.wave_begin[i];
-    wn[i] = args.waves[i];
+    wb[i] = args.wg_begin[i];
+    wn[i] = args.wgs[i];
     wr[i] = args.rows[i];
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) val[i] = args.value[i];
   // keep these loads in the first batch, ahead of the wave's vector loads
   __builtin_amdgcn_sched_barrier(0);
-  int pi = -1, w = 0, nwv = 1, nrows = 0;
+  int pi = -1, g = 0, ng = 1, nrows = 0;
 #pragma unroll
   for (int i = 0; i < kMaxGroup; ++i) {
-    const int d = wave - wb[i];
+    const int d = (int)blockIdx.x - wb[i];
     const bool hit = d >= 0 && d < wn[i];
     pi = hit ? i : pi;
-    w = hit ? d : w;
-    nwv = hit ? wn[i] : nwv;
+    g = hit ? d : g;
+    ng = hit ? wn[i] : ng;
     nrows = hit ? wr[i] : nrows;
   }
   {
     const bool has_problem = pi >= 0;
     if (!has_problem) pi = 0;
-    const int64_t Np = nrows, nw = nwv;
-    // this wave's rows of the problem: row(i) = first + i * stride, i < cnt
-    int64_t first, stride, cnt;
-    if (kInterleave) {  // the problem's waves sweep its rows side by side
-      first = w;
-      stride = nw;
-      cnt = (Np - w + nw - 1) / nw;
-    } else {  // a contiguous range per wave: rows [w N / nw, (w + 1) N / nw)
-      // in 32-bit pieces: w N / nw = w q + w r / nw with N = q nw + r, w r < nw^2
-      const uint32_t q = (uint32_t)nrows / (uint32_t)nwv, r = (uint32_t)nrows % (uint32_t)nwv;
-      const uint32_t f0 = (uint32_t)w * q + ((uint32_t)w * r) / (uint32_t)nwv;
-      const uint32_t f1 = (uint32_t)(w + 1) * q + ((uint32_t)(w + 1) * r) / (uint32_t)nwv;
-      first = f0;
-      stride = 1;
-      cnt = (int64_t)f1 - (int64_t)f0;
-    }
+    // rows [a N / b, (a + 1) N / b) in 32-bit pieces: a N / b = a q + a r / b
+    // with N = q b + r, a r < b^2
+    auto split = [](uint32_t n, uint32_t a, uint32_t b) {
+      const uint32_t q = n / b, r = n % b;
+      return a * q + (a * r) / b;
+    };
+    // the workgroup's rows of the problem, then this wave's contiguous share
+    const uint32_t g0 = split((uint32_t)nrows, (uint32_t)g, (uint32_t)ng);
+    const uint32_t g1 = split((uint32_t)nrows, (uint32_t)g + 1, (uint32_t)ng);
+    const uint32_t w0 = g0 + split(g1 - g0, (uint32_t)wave_in_block, kWaves);
+    const uint32_t w1 = g0 + split(g1 - g0, (uint32_t)wave_in_block + 1, kWaves);
+    const int64_t first = w0, stride = 1;
+    int64_t cnt = (int64_t)w1 - (int64_t)w0;
     if (!has_problem) cnt = 0;
     const bool active = cnt > 0;
     const uint16_t *x = args.p[pi].x;
@@ -227,18 +228,17 @@ void gemv1_kernel(Gemv1Args args) {
       voff[j] = ok[j][0] ? (uint32_t)k0 >> 1 : 0x80000000u;  // past the row: reads zeros
       kb[j] = ok[j][0] ? (uint32_t)k0 >> log2_bs : 0u;
       kb2[j] = (two_blocks && ok[j][1]) ? kb[j] + 1 : kb[j];
-      // x[k0 .. k0+63]: past K the buffer returns zeros, without a branch
+    }
+    // x, once for the workgroup: thread t fetches bytes 16 t .. 16 t + 15 of
+    // every 8 KB slice (past K the buffer returns zeros, without a branch)
+    uint4 xg[J];
+    {
       const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
           (void *)x, (short)0, (int)(2u * (uint32_t)K), kBufferFlags);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const uint4 v = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, 2 * k0, 16 * q, 0));
-        xv[j][4 * q] = v.x;
-        xv[j][4 * q + 1] = v.y;
-        xv[j][4 * q + 2] = v.z;
-        xv[j][4 * q + 3] = v.w;
-      }
+      for (int j = 0; j < J; ++j)
+        xg[j] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(16 * threadIdx.x + 8192 * j), 0, 0));
     }
 
     // Row loads go through buffer resources whose base is the (wave-uniform)
@@ -291,8 +291,10 @@ void gemv1_kernel(Gemv1Args args) {
       for (int j = 0; j < J; ++j) {
         L.pw[j][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                    prs, (int)voff[j], 0, 0));
+        // (all of the offset in the range-checked vector part: a piece past
+        // the row reads zeros)
         L.pw[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                   prs, (int)voff[j], 16, 0));
+                                                   prs, (int)(voff[j] + 16u), 0, 0));
       }
       // keep the scheduler from hoisting the previous row's arithmetic (and
       // its waits) above these loads
@@ -358,8 +360,21 @@ void gemv1_kernel(Gemv1Args args) {
       const f32x4 v = {hi, lo, hi, lo};
       *reinterpret_cast<f32x4 *>(tbl + 256 * (base + q) + 16 * (lane % (kCopies / 2))) = v;
     }
+    // piece t of a slice belongs to lane t / 8, as its piece t % 8
+#pragma unroll
+    for (int j = 0; j < J; ++j) xs[512 * j + 64 * (threadIdx.x % 8) + threadIdx.x / 8] = xg[j];
     __syncthreads();
     if (!active) return;
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 v = xs[512 * j + 64 * q + lane];
+        xv[j][4 * q] = v.x;
+        xv[j][4 * q + 1] = v.y;
+        xv[j][4 * q + 2] = v.z;
+        xv[j][4 * q + 3] = v.w;
+      }
     // Issue priority falls as the wave's rows get done (four steps): a SIMD
     // otherwise issues for its oldest wave first, so its waves finish one
     // after another and the last runs alone, waiting on memory; with waves
@@ -383,30 +398,29 @@ void gemv1_kernel(Gemv1Args args) {
   }
 }
 
-// Splits the waves of the launch among the problems in proportion to their
-// rows (each gets at least one, and no more than it has rows); returns the
-// grid size.
+// Splits the workgroups of the launch among the problems in proportion to
+// their rows (each gets at least one, and no more than it has rows for one
+// per wave); returns the grid size.
 template <int J>
-int assign_waves(Gemv1Args &args, int64_t rows) {
-  constexpr int kWaves = block_waves<J>();
+int assign_wgs(Gemv1Args &args, int64_t rows) {
   // at least two rows per wave; as many workgroups as fit on the chip at once
   const int64_t want = (rows + 2 * kWaves - 1) / (2 * kWaves);
-  const int64_t cap = (int64_t)device_cu_count() * (4 * waves_per_simd<J>() / kWaves);
+  const int64_t cap = (int64_t)device_cu_count() * wgs_per_cu<J>();
   int64_t grid = want < cap ? want : cap;
-  const int64_t min_grid = (args.count + kWaves - 1) / kWaves;
-  grid = grid > min_grid ? grid : min_grid;
-  const int64_t spare = grid * kWaves - args.count;  // beyond the one wave each
+  grid = grid > args.count ? grid : args.count;
+  const int64_t spare = grid - args.count;  // beyond the one workgroup each
   int wb = 0;
   for (int i = 0; i < args.count; ++i) {
-    Gemv1Problem &p = args.p[i];
-    int64_t nw = p.N * spare / rows;
-    nw = nw < 1 ? 1 : (nw > p.N ? p.N : nw);
-    args.wave_begin[i] = wb;
-    args.waves[i] = (int)nw;
+    const Gemv1Problem &p = args.p[i];
+    const int64_t most = (p.N + kWaves - 1) / kWaves;
+    int64_t n = 1 + p.N * spare / rows;
+    n = n > most ? most : n;
+    args.wg_begin[i] = wb;
+    args.wgs[i] = (int)n;
     args.rows[i] = p.N;
-    wb += (int)nw;
+    wb += (int)n;
   }
-  return (int)grid;
+  return wb;
 }
 
 template <int J, bool DQ, bool BS32>
@@ -414,13 +428,13 @@ hipError_t launch_j(Gemv1Args &args, int64_t rows, bool out_bf16, hipStream_t st
   // one row in flight while one computes: deeper prefetch measured no faster
   // (the row's arithmetic, not memory latency, sets the pace)
   constexpr int NBUF = 2;
-  const int grid = assign_waves<J>(args, rows);
+  const int grid = assign_wgs<J>(args, rows);
   if (out_bf16)
-    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, true>), dim3(grid),
-                       dim3(64 * block_waves<J>()), 0, stream, args);
+    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, args);
   else
-    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, false>), dim3(grid),
-                       dim3(64 * block_waves<J>()), 0, stream, args);
+    hipLaunchKernelGGL((gemv1_kernel<J, NBUF, DQ, BS32, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, args);
   return hipGetLastError();
 }
 
@@ -446,8 +460,8 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
   Gemv1Args args;
   args.count = 0;
   for (int i = 0; i < kMaxGroup; ++i) {
-    args.wave_begin[i] = 0;
-    args.waves[i] = 0;
+    args.wg_begin[i] = 0;
+    args.wgs[i] = 0;
     args.rows[i] = 0;
   }
   int64_t rows = 0;

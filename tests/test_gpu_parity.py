@@ -284,6 +284,25 @@ def test_gemv_single_row_long_k(nf4, orc, bs, dq):
         _gemv_case(nf4, orc, w, x, bs, "nf4", dq)
 
 
+@pytest.mark.parametrize("M", [1, 3])
+def test_gemv_reads_no_activation_past_k(nf4, orc, M):
+    """Rows whose length ends half-way through a lane's 64 codes (K % 64 == 32),
+    with NaN bf16 values right after the activations in memory: nothing past
+    x[:, K-1] may reach the sums."""
+    for (N, K) in [(40, 160), (24, 4128)]:
+        w = workloads.normal_bf16((N, K), 0.02, 5100 + K)
+        x = workloads.normal_bf16((M, K), 1.0, 5200 + K + M)
+        qs, ref = check_quant(nf4, orc, w, 32, "nf4", False)
+        _, wc16 = orc.dequantize(ref["packed"], N * K, 32, "nf4", **oracle_scales(ref, False))
+        y_ref = orc.matmul_bf16(to_u16(x), wc16.reshape(N, K))
+        buf = torch.full((M * K + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        buf[:M * K] = dev(x).reshape(-1)
+        xd = buf[:M * K].view(M, K)
+        y32 = nf4.gemv(xd, qs, torch.float32)
+        assert torch.isfinite(y32).all(), "values past the activations were read"
+        check_product(y32, None, y_ref, wc16.reshape(N, K), to_u16(x))
+
+
 @pytest.mark.parametrize("dq", [False, True])
 def test_gemv_batched_tile_counts(nf4, orc, dq):
     """Batched decode from a handful to thousands of 16-row tiles (more work
