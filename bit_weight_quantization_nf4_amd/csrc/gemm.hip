@@ -10,14 +10,20 @@
 // walks K in steps of BK = 64. The waves form a 4 x 2 grid; each owns a
 // 64 x 112 sub-tile = 4 x 7 fragments of v_mfma_f32_16x16x32_bf16, whose
 // fp32 accumulators stay in registers for the whole K walk.
-// Per step the X tile (bf16) and the weight tile -- read as packed codes and
-// dequantized on the fly to the same bf16 values the dequantize kernel
-// produces -- are written to one of two LDS buffers while the matrix cores
-// work on the other: the global loads of step k+1 are issued before the
-// MFMAs of step k, the dequantization and LDS writes follow them, and one
-// barrier per step separates the two buffers. LDS rows are padded by 16
-// bytes, so the 16-byte operand reads of 16 consecutive lanes (16 rows) cover
-// all 64 banks once.
+// Per step two LDS buffers alternate: the MFMAs of step k read one while the
+// other is filled for step k+1 --
+//  - the X tile goes from memory straight into LDS (buffer loads with the LDS
+//    destination), 1 KB per wave instruction, no registers involved;
+//  - the weight tile's codes (loaded into registers a step earlier) are
+//    dequantized to the same bf16 values the dequantize kernel produces and
+//    written to LDS; every thread takes at most one 32-code piece, so the
+//    dequantization work is spread over all waves;
+// and the codes of step k+2 are loaded. One barrier per step; before it a
+// wave waits only for its X loads, not for the code loads issued after them.
+// LDS rows are 128 bytes with the 16-byte chunk c of row r stored at chunk
+// c ^ ((r / 2) mod 8): the operand reads (16 rows, one chunk each) and the
+// row writes then cover every bank once. Staged double-quant scales are held
+// block-column-major, so neighbouring rows read neighbouring bytes.
 // Tile order: consecutive workgroups go to different XCDs (8 of them), so
 // workgroup i takes M tile i % m_tiles and N tile i / m_tiles: with 8 M tiles
 // (M = 2048) each XCD keeps its own X rows hot in its L2 across N tiles.
@@ -31,18 +37,22 @@ constexpr int kWaves = 8, kThreads = 64 * kWaves;
 constexpr int WM = 4, WN = 2;             // wave grid
 constexpr int TM = BM / WM, TN = BN / WN;  // 64 x 112 per wave
 constexpr int FM = TM / 16, FN = TN / 16;  // 4 x 7 fragments
-constexpr int kStride = BK + 8;            // bf16 per LDS row (144 B)
-constexpr int kXPieces = BM * BK / 8;      // 16-byte pieces of the X tile
+constexpr int kStride = BK;                // bf16 per LDS row (128 B, swizzled)
+// 16-byte chunk c of tile row r sits at chunk c ^ ((r / 2) mod 8) of its row:
+// the 16-byte reads of 16 consecutive rows (one chunk each), and the writes of
+// whole rows, then cover every bank once
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kStride + 8 * (chunk ^ ((row >> 1) & 7));
+}
 constexpr int kWPieces = BN * BK / 32;     // 32-code pieces of the weight tile
-// Waves 0-3 (one per SIMD) stage and dequantize the weight tile, waves 4-7
-// stage the X tile; all eight run MFMAs, so on every SIMD the matrix-core
-// work of one wave overlaps the dequantization of the other.
-constexpr int kHalf = kThreads / 2;
-constexpr int kXPer = kXPieces / kHalf;                  // 8
-constexpr int kWPer = (kWPieces + kHalf - 1) / kHalf;    // 2
+constexpr int kWPer = (kWPieces + kThreads - 1) / kThreads;  // weight pieces per thread: 1
 constexpr int kBufferFlags = 0x00020000;
 constexpr uint32_t kOOB = 0x80000000u;     // an offset past every buffer
-static_assert(kXPieces % kHalf == 0, "X tile pieces per thread");
+// s_waitcnt immediates (vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8):
+// all but the newest n memory loads done
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitVm0 = waitcnt_vm(0);
+static_assert(BM * BK * 2 == kWaves * 4 * 1024, "X tile: four 1 KB loads per wave");
 
 struct GemmArgs {
   const uint16_t *x;
@@ -78,6 +88,9 @@ constexpr int kGStage = 512;     // fp32 group scales of one weight tile
 template <bool DQ, bool SQ, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmArgs args) {
+  // memory loads a thread issues per step for the weight tile (codes, plus
+  // the block scales when they are not staged in LDS)
+  constexpr int kCodeLoads = kWPer * (SQ ? 1 : (DQ ? 3 : 2));
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kStride];
   // one spare row past the tile: threads without a weight piece (the last
   // wave) write their zeros there, so the step body needs no branch
@@ -98,15 +111,12 @@ void gemm_kernel(GemmArgs args) {
   const int nk = (K + BK - 1) / BK;
   const uint32_t row_bytes = (uint32_t)K >> 1;
 
-  // X tile (waves 4-7): piece p = xt + kHalf * i is row p / 8, k chunk p % 8.
-  const bool x_role = wave >= 4;
-  const int xt = tid - kHalf;
   const int x_rows = M - m0 < BM ? M - m0 : BM;
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(args.x + (int64_t)m0 * K), (short)0, (int)(2u * (uint32_t)x_rows * (uint32_t)K),
       kBufferFlags);
-  // weight tile (waves 0-3): piece p = tid + kHalf * u (< kWPieces) is row
-  // p / 2, 32-code half p % 2
+  // weight tile: piece p = tid + kThreads * u (< kWPieces) is row p / 2,
+  // 32-code half p % 2
   const int w_rows = N - n0 < BN ? N - n0 : BN;
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(args.packed + (int64_t)n0 * row_bytes), (short)0,
@@ -128,25 +138,15 @@ void gemm_kernel(GemmArgs args) {
       DQ ? (void *)(args.sc.absmax_scale + gbase) : (void *)args.sc.absmax, (short)0,
       (int)(DQ ? 4u * groups : 0u), kBufferFlags);
 
-  uint4 xr[kXPer];
   uint4 wr[kWPer];
   float w_scale[kWPer];
   uint32_t w_blk[kWPer];
   auto load_step = [&](int ks) {
     const int k0 = ks * BK;
-    if (x_role) {
-#pragma unroll
-      for (int i = 0; i < kXPer; ++i) {
-        const int p = xt + kHalf * i;
-        const int row = p >> 3, kc = k0 + 8 * (p & 7);
-        const uint32_t off = kc < K ? 2u * ((uint32_t)row * (uint32_t)K + (uint32_t)kc) : kOOB;
-        xr[i] =
-            __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)off, 0, 0));
-      }
-    } else {
+    {
 #pragma unroll
       for (int u = 0; u < kWPer; ++u) {
-        const int p = tid + kHalf * u;
+        const int p = tid + kThreads * u;
         const int row = p >> 1, kc = k0 + 32 * (p & 1);
         const bool ok = p < kWPieces && row < w_rows && kc < K;
         const uint32_t off = ok ? (uint32_t)row * row_bytes + ((uint32_t)kc >> 1) : kOOB;
@@ -170,30 +170,44 @@ void gemm_kernel(GemmArgs args) {
       }
     }
   };
-  auto store_step = [&](int buf) {
-    if (x_role) {
-      uint16_t *xb = xs[buf];
+  // X tile straight from memory into LDS: wave w fills rows 32 w .. 32 w + 31,
+  // 8 rows (1 KB) per instruction; lane 8 r' + q of an instruction lands at
+  // position q of its row r, so it fetches the chunk that the swizzle puts
+  // there. Rows past M and columns past K read zeros.
+  auto x_direct = [&](int ks, int buf) {
+    const int k0 = ks * BK;
 #pragma unroll
-      for (int i = 0; i < kXPer; ++i) {
-        const int p = xt + kHalf * i;
-        *reinterpret_cast<uint4 *>(&xb[(p >> 3) * kStride + 8 * (p & 7)]) = xr[i];
-      }
-    } else {
+    for (int i = 0; i < 4; ++i) {
+      const int r = (4 * wave + i) * 8 + (lane >> 3), q = lane & 7;
+      const int c = q ^ ((r >> 1) & 7);
+      const int kc = k0 + 8 * c;
+      const uint32_t off = kc < K ? 2u * ((uint32_t)r * (uint32_t)K + (uint32_t)kc) : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xrs, (__attribute__((address_space(3))) void *)&xs[buf][(4 * wave + i) * 512], 16,
+          (int)off, 0, 0, 0);
+    }
+  };
+  auto store_step = [&](int buf) {
+    {
 #pragma unroll
       for (int u = 0; u < kWPer; ++u) {
-        const int p = tid + kHalf * u;
+        const int p = tid + kThreads * u;
         // pieces past the tile go to the spare row
-        uint16_t *wb = &ws[buf][(p < kWPieces ? p >> 1 : BN) * kStride + 32 * (p & 1)];
+        const int wrow = p < kWPieces ? p >> 1 : BN, wc = 4 * (p & 1);
+        uint16_t *wbase = ws[buf];
         float ap = w_scale[u];
         if (SQ) {
+          // q_lds holds the tile's int8 scales block-column-major (row
+          // fastest), so the rows of one wave read neighbouring bytes
           const bool ok = w_blk[u] != 0xffffffffu;
           const uint32_t b = ok ? w_blk[u] : 0u;
-          ap = ok ? (float)q_lds[b] * s2_lds[(blk_in + b) >> log2_bs2] : 0.0f;
+          const uint32_t row = (uint32_t)(p >> 1), kb = b - row * row_blocks;
+          ap = ok ? (float)q_lds[kb * BN + row] * s2_lds[(blk_in + b) >> log2_bs2] : 0.0f;
         }
-        *reinterpret_cast<uint4 *>(wb + 0) = dequant8(wr[u].x, ap, tb);
-        *reinterpret_cast<uint4 *>(wb + 8) = dequant8(wr[u].y, ap, tb);
-        *reinterpret_cast<uint4 *>(wb + 16) = dequant8(wr[u].z, ap, tb);
-        *reinterpret_cast<uint4 *>(wb + 24) = dequant8(wr[u].w, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 0)) = dequant8(wr[u].x, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 1)) = dequant8(wr[u].y, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 2)) = dequant8(wr[u].z, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 3)) = dequant8(wr[u].w, ap, tb);
       }
     }
   };
@@ -207,49 +221,58 @@ void gemm_kernel(GemmArgs args) {
   if (SQ) {
     // the tile's block scales (tile_blocks bytes, contiguous) and the group
     // scales they use (groups floats, contiguous)
-    for (uint32_t i = tid; i < tile_blocks; i += kThreads)
-      q_lds[i] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)i, 0, 0);
+    for (uint32_t i = tid; i < tile_blocks; i += kThreads) {
+      const uint32_t row = i / row_blocks, kb = i - row * row_blocks;
+      q_lds[kb * BN + row] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)i, 0, 0);
+    }
     for (uint32_t i = tid; i < groups; i += kThreads)
       s2_lds[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(4 * i), 0, 0));
   }
   __syncthreads();  // code table, staged scales
+  x_direct(0, 0);
   load_step(0);
   store_step(0);
   load_step(1 < nk ? 1 : nk - 1);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __syncthreads();
 
   // operand rows of this lane: A row wm*64 + 16 fi + lane%16, B row
   // wn*112 + 16 fj + lane%16; k = 32 h + 8 (lane / 16)
-  const int lr = lane & 15, lk = 8 * (lane >> 4);
-  // Step ks: the MFMAs of step ks read buffer ks % 2 while step ks + 1 --
-  // loaded into registers during the previous step -- is dequantized into
-  // the other buffer, then the loads of step ks + 2 are issued. One basic
-  // block per step (no branches: past the last step the loads repeat it and
-  // the writes go to the buffer no one reads any more), so the scheduler can
-  // interleave the dequantization with the matrix-core work.
+  const int lr = lane & 15, lc = lane >> 4;
+  // Step ks: the MFMAs of step ks read buffer ks % 2. Meanwhile the X tile of
+  // step ks + 1 streams into the other buffer, the weight codes of step
+  // ks + 1 (in registers since the previous step) are dequantized into it,
+  // and the codes of step ks + 2 are loaded. Before the step's barrier the
+  // wave waits for its X loads (older than the code loads), not for the code
+  // loads issued after them.
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
+    x_direct(ks + 1 < nk ? ks + 1 : nk - 1, cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
     store_step(cur ^ 1);
     load_step(ks + 2 < nk ? ks + 2 : nk - 1);
+    // both halves' operands first, so the reads of the second half overlap
+    // the first half's matrix-core work
+    bf16x8 a[2][FM], b[2][FN];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      bf16x8 a[FM], b[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a[i] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4 *>(
-                        &xs[cur][(wm * TM + 16 * i + lr) * kStride + 32 * h + lk]));
+        a[h][i] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4 *>(&xs[cur][swz(wm * TM + 16 * i + lr, 4 * h + lc)]));
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        b[j] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4 *>(
-                        &ws[cur][(wn * TN + 16 * j + lr) * kStride + 32 * h + lk]));
+        b[h][j] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4 *>(&ws[cur][swz(wn * TN + 16 * j + lr, 4 * h + lc)]));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCodeLoads));
     __syncthreads();
   }
 
