@@ -160,14 +160,17 @@ def test_quantize_with_double_quant_groups(nf4, orc, bs):
     """Quantization with double quantization in one pass: whole and ragged
     groups of 256 blocks, an all-zero group and one whose largest scale sits
     in its last block, and more groups than one launch has workgroups (each
-    then loops over several groups)."""
+    then loops over several groups). The 33.6M-element case also dequantizes,
+    so the dequantize kernel's waves each take more than one tile."""
     g = 256 * bs
     for n in (g, 3 * g + 5 * bs + 17, 2 * g - 1, 2049 * g + 3 * bs + 1):
         w = workloads.normal_bf16((n,), 0.02, 31 * n + bs).float()
         w[g:2 * g] = 0.0
         if n > 3 * g:
             w[3 * g - 1] = 4.0
-        check_quant(nf4, orc, w.to(torch.bfloat16), bs, "nf4", True)
+        qs, ref = check_quant(nf4, orc, w.to(torch.bfloat16), bs, "nf4", True)
+        if n > 3 * g and bs == 64:
+            check_dequant(nf4, orc, qs, ref, bs, "nf4", True)
 
 
 def test_quantize_empty(nf4):
