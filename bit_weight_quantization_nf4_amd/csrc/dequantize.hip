@@ -10,9 +10,11 @@
 // half; 8 | blocksize, so the 8 share one block scale). Each bf16 store
 // instruction then writes 1 KB without gaps. Stores are non-temporal: the
 // output is written once and not read back by this kernel, so it should not
-// displace other lines from L2. The 16 fp32 code values sit in LDS; a code
-// times 4 is cut from the packed word with one bit-field extract and used as
-// the LDS byte offset.
+// displace other lines from L2. The inputs of a tile (codes, scale parts)
+// are loaded two tiles ahead, so their HBM latency overlaps the stores of
+// the tiles before. The 16 fp32 code values sit in LDS; a code times 4 is cut
+// from the packed word with one bit-field extract and used as the LDS byte
+// offset.
 #include "nf4_internal.h"
 
 namespace nf4 {
@@ -32,7 +34,77 @@ struct DequantArgs {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// The raw inputs of one lane for one whole tile: the packed codes of its two
+// 8-element pieces and what their block scales are made of.
+template <bool DQ>
+struct TileIn {
+  uint32_t word[2];
+  float a[2];      // fp32 absmax (no double quant) or absmax_scale
+  int32_t q[2];    // int8 absmax code (double quant)
+};
+
+template <bool DQ>
+__device__ __forceinline__ TileIn<DQ> load_tile_in(const DequantArgs &args, int64_t tile, int lane) {
+  TileIn<DQ> t;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int64_t e0 = tile * 1024 + 512 * half + 8 * lane;
+    t.word[half] = *reinterpret_cast<const uint32_t *>(args.packed + e0 / 2);
+    const int64_t b = e0 >> args.log2_bs;
+    if (DQ) {
+      t.q[half] = args.sc.absmax_q[b];
+      t.a[half] = args.sc.absmax_scale[b >> args.sc.log2_bs2];
+    } else {
+      t.a[half] = args.sc.absmax[b];
+    }
+  }
+  return t;
+}
+
+// 8 dequantized values of one packed word with block scale ap
+__device__ __forceinline__ void decode8(uint32_t word, float ap, const char *tb, float (&w)[8]) {
+  // byte j of the word holds element 2j in bits 7..4 and 2j+1 in bits 3..0
+  const uint32_t even4 = (word >> 2) & 0x3c3c3c3cu;  // 4 * code(2j) in byte j
+  const uint32_t odd4 = (word << 2) & 0x3c3c3c3cu;   // 4 * code(2j+1) in byte j
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    w[2 * j] = *reinterpret_cast<const float *>(tb + ((even4 >> (8 * j)) & 0xffu)) * ap;
+    w[2 * j + 1] = *reinterpret_cast<const float *>(tb + ((odd4 >> (8 * j)) & 0xffu)) * ap;
+  }
+}
+
 template <bool OUT_BF16>
+__device__ __forceinline__ void store8(void *out, int64_t e0, const float (&w)[8]) {
+  if (OUT_BF16) {
+    u32x4 v;
+    v.x = pack_bf16x2(w[0], w[1]);
+    v.y = pack_bf16x2(w[2], w[3]);
+    v.z = pack_bf16x2(w[4], w[5]);
+    v.w = pack_bf16x2(w[6], w[7]);
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(out) + e0));
+  } else {
+    f32x4 v0, v1;
+    v0.x = w[0]; v0.y = w[1]; v0.z = w[2]; v0.w = w[3];
+    v1.x = w[4]; v1.y = w[5]; v1.z = w[6]; v1.w = w[7];
+    f32x4 *o = reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + e0);
+    __builtin_nontemporal_store(v0, o);
+    __builtin_nontemporal_store(v1, o + 1);
+  }
+}
+
+template <bool OUT_BF16, bool DQ>
+__device__ __forceinline__ void write_tile(const DequantArgs &args, const TileIn<DQ> &in,
+                                           int64_t t, int lane, const char *tb) {
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const float ap = DQ ? (float)in.q[half] * in.a[half] : in.a[half];
+    float w[8];
+    decode8(in.word[half], ap, tb, w);
+    store8<OUT_BF16>(args.out, t * 1024 + 512 * half + 8 * lane, w);
+  }
+}
+
+template <bool OUT_BF16, bool DQ>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) {
   __shared__ float table[16];
   if (threadIdx.x < 16) table[threadIdx.x] = args.value[threadIdx.x];
@@ -40,59 +112,52 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
   const char *tb = reinterpret_cast<const char *>(table);
 
   const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-  const int64_t ntiles = (args.n + 1023) / 1024;
-  for (int64_t tile = ((int64_t)blockIdx.x * kThreads + threadIdx.x) >> 6; tile < ntiles;
-       tile += nwaves) {
+  const int64_t nfull = args.n >> 10;  // whole 1024-element tiles
+
+  // whole tiles, two register sets in turn: the inputs of a wave's tile after
+  // next are loaded as soon as a set has been decoded, so their latency
+  // overlaps the stores of two tiles (indices past the end are clamped: a
+  // harmless reload)
+  if (wave < nfull) {
+    int64_t t = wave;
+    auto clampt = [&](int64_t u) { return u < nfull ? u : t; };
+    TileIn<DQ> a = load_tile_in<DQ>(args, t, lane);
+    TileIn<DQ> b = load_tile_in<DQ>(args, clampt(t + nwaves), lane);
+    for (;;) {
+      write_tile<OUT_BF16, DQ>(args, a, t, lane, tb);
+      a = load_tile_in<DQ>(args, clampt(t + 2 * nwaves), lane);
+      if (t + nwaves >= nfull) break;
+      write_tile<OUT_BF16, DQ>(args, b, t + nwaves, lane, tb);
+      b = load_tile_in<DQ>(args, clampt(t + 3 * nwaves), lane);
+      if (t + 2 * nwaves >= nfull) break;
+      t += 2 * nwaves;
+    }
+  }
+
+  // the ragged last tile, element by element where a piece is cut short
+  if ((args.n & 1023) != 0 && wave == nfull % nwaves) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int64_t e0 = tile * 1024 + 512 * half + 8 * lane;
+      const int64_t e0 = nfull * 1024 + 512 * half + 8 * lane;
       if (e0 >= args.n) continue;
       const float ap = block_scale(args.sc, e0 >> args.log2_bs);
-      const bool full = e0 + 8 <= args.n;
-      uint32_t word;
-      if (full) {
-        word = *reinterpret_cast<const uint32_t *>(args.packed + e0 / 2);
-      } else {
-        const int64_t nbytes = (args.n - e0 + 1) / 2;
-        word = 0;
-        for (int i = 0; i < 4; ++i)
-          if (i < nbytes) word |= (uint32_t)args.packed[e0 / 2 + i] << (8 * i);
-      }
-      // byte j of the word holds element 2j in bits 7..4 and 2j+1 in bits 3..0
-      const uint32_t even4 = (word >> 2) & 0x3c3c3c3cu;  // 4 * code(2j) in byte j
-      const uint32_t odd4 = (word << 2) & 0x3c3c3c3cu;   // 4 * code(2j+1) in byte j
+      const int64_t nbytes = (args.n - e0 + 1) / 2;
+      uint32_t word = 0;
+      for (int i = 0; i < 4; ++i)
+        if (i < nbytes) word |= (uint32_t)args.packed[e0 / 2 + i] << (8 * i);
       float w[8];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        w[2 * j] = *reinterpret_cast<const float *>(tb + ((even4 >> (8 * j)) & 0xffu)) * ap;
-        w[2 * j + 1] = *reinterpret_cast<const float *>(tb + ((odd4 >> (8 * j)) & 0xffu)) * ap;
-      }
-      if (OUT_BF16) {
+      decode8(word, ap, tb, w);
+      if (e0 + 8 <= args.n) {
+        store8<OUT_BF16>(args.out, e0, w);
+      } else if (OUT_BF16) {
         uint16_t *o = reinterpret_cast<uint16_t *>(args.out) + e0;
-        u32x4 v;
-        v.x = pack_bf16x2(w[0], w[1]);
-        v.y = pack_bf16x2(w[2], w[3]);
-        v.z = pack_bf16x2(w[4], w[5]);
-        v.w = pack_bf16x2(w[6], w[7]);
-        if (full) {
-          __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(o));
-        } else {
-          const uint32_t pk[4] = {v.x, v.y, v.z, v.w};
-          for (int i = 0; i < 8 && e0 + i < args.n; ++i)
-            o[i] = (uint16_t)(pk[i / 2] >> (16 * (i & 1)));
-        }
+        for (int i = 0; i < 8 && e0 + i < args.n; ++i) o[i] = (uint16_t)(pack_bf16x2(w[i], 0.0f) & 0xffffu);
       } else {
         float *o = reinterpret_cast<float *>(args.out) + e0;
-        if (full) {
-          f32x4 v0, v1;
-          v0.x = w[0]; v0.y = w[1]; v0.z = w[2]; v0.w = w[3];
-          v1.x = w[4]; v1.y = w[5]; v1.z = w[6]; v1.w = w[7];
-          __builtin_nontemporal_store(v0, reinterpret_cast<f32x4 *>(o));
-          __builtin_nontemporal_store(v1, reinterpret_cast<f32x4 *>(o) + 1);
-        } else {
-          for (int i = 0; i < 8 && e0 + i < args.n; ++i) o[i] = w[i];
-        }
+        for (int i = 0; i < 8 && e0 + i < args.n; ++i) o[i] = w[i];
       }
     }
   }
@@ -111,14 +176,19 @@ hipError_t launch_dequantize(const uint8_t *packed, int64_t n, int blocksize, in
   args.sc = sc;
   args.log2_bs = __builtin_ctz((unsigned)blocksize);
   for (int i = 0; i < 16; ++i) args.value[i] = t.value[i];
-  // one 1024-element tile per wave, at most 16 workgroups per CU
-  int64_t blocks = ((n + 1023) / 1024 + kThreads / 64 - 1) / (kThreads / 64);
-  if (blocks > 256 * 16) blocks = 256 * 16;
+  // about two tiles of 1024 elements per wave, at most 16 workgroups per CU
+  int64_t blocks = ((n + 1023) / 1024 + 4 * 2 - 1) / (4 * 2);
+  if (blocks > 4096) blocks = 4096;
   dim3 grid((unsigned)blocks);
-  if (out_bf16)
-    hipLaunchKernelGGL(dequantize_kernel<true>, grid, dim3(kThreads), 0, stream, args);
+  const bool dq = sc.double_quant != 0;
+  if (out_bf16 && dq)
+    hipLaunchKernelGGL((dequantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, args);
+  else if (out_bf16)
+    hipLaunchKernelGGL((dequantize_kernel<true, false>), grid, dim3(kThreads), 0, stream, args);
+  else if (dq)
+    hipLaunchKernelGGL((dequantize_kernel<false, true>), grid, dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL(dequantize_kernel<false>, grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((dequantize_kernel<false, false>), grid, dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 

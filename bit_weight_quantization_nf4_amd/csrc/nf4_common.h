@@ -18,7 +18,7 @@ constexpr int kQuantNF4 = 0;
 constexpr int kQuantFP4 = 1;
 
 // Number of cells of the quantize lookup: cell i holds every normalised value
-// s with round-to-nearest(16 s + 16) == i, s in [-1, 1].
+// s in [-1, 1] with floor(round-to-nearest(128 s + 128) / 8) == i.
 constexpr int kCells = 33;
 
 // Per-type constant tables, built once on the host and passed to kernels by
@@ -26,8 +26,8 @@ constexpr int kCells = 33;
 struct CodeTables {
   // fp32 code value for each 4-bit code (the dequantization table)
   float value[16];
-  // quantize lookup: within cell i the code is (s > cell_thr[i]) ? hi : lo,
-  // with lo in bits 15..0 and hi in bits 31..16 of cell_codes[i]
+  // quantize lookup: within cell i the code is (s > cell_thr[i]) ? hi : lo;
+  // cell_codes[i] holds lo, hi in bytes 0, 1 and lo << 4, hi << 4 in bytes 2, 3
   float cell_thr[kCells];
   uint32_t cell_codes[kCells];
 };

@@ -95,12 +95,13 @@ void build(int quant_type, CodeTables &t) {
   for (int r = 0; r + 1 < nc; ++r)
     thr[r] = round_down_f32(0.5 * ((double)t.value[codes[r]] + (double)t.value[codes[r + 1]]));
 
-  // Cell lookup. The kernel computes i = RN(16 s + 16) exactly with one fma;
-  // every s with that i lies in [(i - 16.5)/16, (i - 15.5)/16]. The smallest
-  // gap between thresholds (> 0.079) exceeds the cell width (1/16), so at most
-  // one threshold falls inside a cell.
+  // Cell lookup. The kernel computes u = RN(128 s + 128) exactly with one fma
+  // and reads cell i = floor(u / 8); every s of cell i lies in
+  // [(8i - 128.5)/128, (8i - 120.5)/128], width 1/16. The smallest gap between
+  // thresholds (> 0.079) exceeds the cell width, so at most one threshold
+  // falls inside a cell.
   for (int i = 0; i < kCells; ++i) {
-    double lo = (i - 16.5) / 16.0, hi = (i - 15.5) / 16.0;
+    double lo = (8 * i - 128.5) / 128.0, hi = (8 * i - 120.5) / 128.0;
     int below = 0, inside = 0;
     float cut = 4.0f;  // above every s: never crossed
     for (int r = 0; r + 1 < nc; ++r) {
@@ -112,9 +113,10 @@ void build(int quant_type, CodeTables &t) {
       }
     }
     if (inside > 1) abort();  // impossible for these tables (gap > 1/16)
-    int lo_rank = below, hi_rank = std::min(below + inside, nc - 1);
+    const uint32_t cb = (uint32_t)codes[below];
+    const uint32_t ca = (uint32_t)codes[std::min(below + inside, nc - 1)];
     t.cell_thr[i] = cut;
-    t.cell_codes[i] = (uint32_t)codes[lo_rank] | ((uint32_t)codes[hi_rank] << 16);
+    t.cell_codes[i] = cb | (ca << 8) | (cb << 20) | (ca << 28);
   }
 }
 

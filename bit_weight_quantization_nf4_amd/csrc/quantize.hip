@@ -7,23 +7,34 @@
 //  default, 32/128 also used; bs 64 on wave64 CDNA) and 0.50.2 (mask the absmax
 //  store of the partial last block).]
 //
-// Layout of the work: a wave takes tiles of 64 * E elements, E = max(32,
-// bs/64); each 512-element chunk of a tile is one contiguous 16-byte load per
-// lane (8 elements) and one 4-byte store of their packed nibbles. The lanes of
-// a block reduce its absmax with cross-lane max. A wave keeps the loads of its
-// next tile in flight while it encodes the current one. With double
+// Layout of the work. Chunk c is elements [512 c, 512 c + 512); lane l owns
+// 512 c + 8 l .. +7 (one 16-byte load, one 4-byte store of the packed
+// codes). For bs <= 512 a block is bs / 8 neighbouring lanes of one chunk,
+// and each wave walks its own sequence of chunks with kInFlight of them
+// loaded ahead in a rotating register window (the load of a slot's next chunk
+// is issued as soon as the slot has been encoded). Larger blocks take tiles of
+// bs / 64 elements per lane, two tiles in flight per wave. With double
 // quantization at bs 64/128/256 one launch also quantizes the scales: a
 // workgroup owns each group of 256 blocks and meets its scales in LDS.
 //
-// Per element: s = x / a; the code is read from a 33-cell lookup indexed by
-// RN(16 s + 16) (one fma gives that integer exactly), which holds the one
-// decision threshold that can fall inside the cell and the codes on either
-// side of it. Division: q0 = x * RN(1/a) gives the same NF4 code as the
-// correctly rounded RN(x/a) for every bf16 (x, a) pair (checked exhaustively
-// over all significand/exponent classes); FP4 adds the residual correction
-// q1 = q0 + (x - q0 a) RN(1/a) with two fmas, which equals RN(x/a) wherever
-// the result is normal. Both hold while 1/a, the product and the residual stay
-// normal, i.e. for a in [2^-100, 2^120); other blocks take a true division.
+// Per element: s = x / a and the nearest code value. s is q0 = x * RN(1/a):
+// that gives the same NF4 code as the correctly rounded RN(x/a) for every
+// bf16 (x, a) pair (checked exhaustively over all significand/exponent
+// classes); FP4 adds the residual correction q1 = q0 + (x - q0 a) RN(1/a)
+// with two fmas, which equals RN(x/a) wherever the result is normal. Both
+// hold while 1/a, the product and the residual stay normal, i.e. for a in
+// [2^-100, 2^120). a is a bf16 value, so there RN(1/a) is the correctly
+// rounded reciprocal of its significand (a 128-entry table, built on the host
+// with IEEE division) times a power of two. Blocks outside that range (and
+// all-zero blocks) first scale x and a by the power of two 2^sh that brings a
+// into [1, 2): x / a is unchanged, the same arithmetic then holds, and RN(1/a)
+// of the scaled a is an IEEE division. The choice is made per chunk for the
+// whole wave (a ballot), so the common case runs without the scaling.
+//
+// The code of s is read from a 33-cell lookup in LDS (see cell_of), whose
+// entry holds the one decision threshold that can fall inside the cell and
+// the codes on either side of it; one compare and one byte-select move the
+// code into place in the output word.
 #include "nf4_internal.h"
 
 namespace nf4 {
@@ -40,45 +51,100 @@ struct QuantArgs {
   int64_t ntiles;
   float cell_thr[kCells];
   uint32_t cell_codes[kCells];
+  // bits of RN(1 / (1 + k/128)) plus 127 << 23, k = 0..127
+  uint32_t recip[128];
 };
 
 template <int QT>
-__device__ __forceinline__ float normalise(float x, float a, float r, bool fast) {
-  if (fast) {
-    float q0 = x * r;
-    if (QT == kQuantNF4) return q0;
-    float e = __builtin_fmaf(-q0, a, x);
-    return __builtin_fmaf(e, r, q0);
-  }
-  return x / a;
+__device__ __forceinline__ float normalise(float x, float a, float r) {
+  const float q0 = x * r;
+  if (QT == kQuantNF4) return q0;
+  const float e = __builtin_fmaf(-q0, a, x);
+  return __builtin_fmaf(e, r, q0);
 }
 
-// Code of one normalised value through the LDS cell lookup. Finite inputs give
-// cells 0..32; the mask keeps a NaN (from non-finite input) inside the table.
+// Cell lookup: t = 2^23 + RN(128 s + 128) (one fma, the integer exact); its
+// representation's low bits masked to a multiple of 8 are the byte offset of
+// 8-byte entry floor(RN(128 s + 128) / 8). An entry holds a threshold and the
+// codes below / above it, pre-placed as bytes: below, above in bytes 0, 1
+// (low nibble) and below << 4, above << 4 in bytes 2, 3 (high nibble). Any bit
+// pattern of t (a NaN from non-finite input included) stays inside the 64
+// entries.
 constexpr int kLutSize = 64;
 
-__device__ __forceinline__ uint32_t code_of(float s, const uint2 *lut) {
-  float t = __builtin_fmaf(s, 16.0f, 8388624.0f);  // 2^23 + 16 + 16 s, rounded to an integer
-  uint32_t cell = (__float_as_uint(t) - 0x4B000000u) & (kLutSize - 1);
-  uint2 e = lut[cell];
-  return (s > __uint_as_float(e.x)) ? (e.y >> 16) : (e.y & 0xffffu);
+__device__ __forceinline__ uint2 cell_of(float s, const uint2 *lut) {
+  const float t = __builtin_fmaf(s, 128.0f, 8388736.0f);  // 2^23 + 128
+  return *reinterpret_cast<const uint2 *>(reinterpret_cast<const char *>(lut) +
+                                          (__float_as_uint(t) & 0x1f8u));
 }
 
-template <int QT>
-__device__ __forceinline__ uint32_t encode8(const uint32_t d[4], float a, float r, bool fast,
-                                            const uint2 *lut) {
-  uint32_t word = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    // d[j] holds elements 2j (low half) and 2j+1 (high half): byte j of the
-    // output is code(2j) << 4 | code(2j+1).
-    float x0 = __uint_as_float(d[j] << 16);
-    float x1 = __uint_as_float(d[j] & 0xffff0000u);
-    uint32_t c0 = code_of(normalise<QT>(x0, a, r, fast), lut);
-    uint32_t c1 = code_of(normalise<QT>(x1, a, r, fast), lut);
-    word |= (c0 << (8 * j + 4)) | (c1 << (8 * j));
+// Byte J of acc = (s > threshold) ? byte SRC + 1 : byte SRC of the entry's
+// codes; J = 0 clears the other bytes, later J keep them. One compare and
+// one byte-select (SDWA) per code.
+template <int J, int SRC>
+__device__ __forceinline__ void put_code(uint32_t &acc, float s, uint2 e) {
+  const float thr = __uint_as_float(e.x);
+  if constexpr (J == 0) {
+    asm(
+        "v_cmp_gt_f32 vcc, %1, %2\n\t"
+        "s_nop 1\n\t"
+        "v_cndmask_b32_sdwa %0, %3, %3, vcc dst_sel:BYTE_0 dst_unused:UNUSED_PAD "
+        "src0_sel:BYTE_%4 src1_sel:BYTE_%5"
+        : "=v"(acc)
+        : "v"(s), "v"(thr), "v"(e.y), "n"(SRC), "n"(SRC + 1)
+        : "vcc");
+  } else {
+    asm(
+        "v_cmp_gt_f32 vcc, %1, %2\n\t"
+        "s_nop 1\n\t"
+        "v_cndmask_b32_sdwa %0, %3, %3, vcc dst_sel:BYTE_%6 dst_unused:UNUSED_PRESERVE "
+        "src0_sel:BYTE_%4 src1_sel:BYTE_%5"
+        : "+v"(acc)
+        : "v"(s), "v"(thr), "v"(e.y), "n"(SRC), "n"(SRC + 1), "n"(J)
+        : "vcc");
   }
-  return word;
+}
+
+// Codes of 8 elements. FAST: a in [2^-100, 2^120) and r = RN(1/a).
+// Otherwise x and a are first scaled by 2^sh (exact) with a * 2^sh in [1, 2).
+template <int QT, bool FAST>
+__device__ __forceinline__ uint32_t encode8(const uint32_t d[4], float a, float r,
+                                            const uint2 *lut) {
+  int sh = 0;
+  if (!FAST) {
+    sh = 1 - __builtin_amdgcn_frexp_expf(a);
+    a = __builtin_amdgcn_ldexpf(a, sh);
+    r = (a == 0.0f) ? 0.0f : 1.0f / a;
+  }
+  uint32_t hi, lo;  // codes of the even / odd elements, as high / low nibbles
+#define NF4_ENCODE_PAIR(J)                                     \
+  {                                                            \
+    float x0 = __uint_as_float(d[J] << 16);                    \
+    float x1 = __uint_as_float(d[J] & 0xffff0000u);            \
+    if (!FAST) {                                               \
+      x0 = __builtin_amdgcn_ldexpf(x0, sh);                    \
+      x1 = __builtin_amdgcn_ldexpf(x1, sh);                    \
+    }                                                          \
+    const float s0 = normalise<QT>(x0, a, r);                  \
+    const float s1 = normalise<QT>(x1, a, r);                  \
+    put_code<J, 2>(hi, s0, cell_of(s0, lut));                  \
+    put_code<J, 0>(lo, s1, cell_of(s1, lut));                  \
+  }
+  // d[j] holds elements 2j (low half) and 2j+1 (high half): byte j of the
+  // output is code(2j) << 4 | code(2j+1)
+  NF4_ENCODE_PAIR(0)
+  NF4_ENCODE_PAIR(1)
+  NF4_ENCODE_PAIR(2)
+  NF4_ENCODE_PAIR(3)
+#undef NF4_ENCODE_PAIR
+  return hi | lo;
+}
+
+// RN(1/a) for a block whose absmax has bf16 bits m, from the significand
+// table; true when a lies in [2^-100, 2^120), where that value is exact.
+__device__ __forceinline__ bool block_recip(uint32_t m, const uint32_t *recip, float &r) {
+  r = __uint_as_float(recip[m & 0x7fu] - ((m << 16) & 0x7f800000u));
+  return m - 0x0d80u < 0x6e00u;
 }
 
 __device__ __forceinline__ uint32_t absmax_bits16(const uint32_t d[4]) {
@@ -89,27 +155,160 @@ __device__ __forceinline__ uint32_t absmax_bits16(const uint32_t d[4]) {
   return m.x > m.y ? m.x : m.y;
 }
 
-// Elements per lane of one tile: E = max(32, bs / 64), in E / 8 chunks of 8.
-// Chunk c of a tile is its elements [512 c, 512 c + 512): lane l owns
-// 512 c + 8 l .. +7, so every 16-byte load and 4-byte store instruction covers
-// one contiguous range. A block of bs <= 512 elements is G = bs / 8 lanes of
-// one chunk; a larger block is bs / 512 whole chunks.
-template <int BS>
-constexpr int lane_elems() { return BS / 64 > 32 ? BS / 64 : 32; }
+// Maximum over aligned groups of G lanes, every lane of a group gets it:
+// DPP for partners within a 16-lane row, lane shuffles beyond.
+template <int G>
+__device__ __forceinline__ uint32_t group_max(uint32_t m) {
+  uint32_t o;
+  if (G >= 2) {
+    o = __builtin_amdgcn_update_dpp(0u, m, 0xb1, 0xf, 0xf, false);  // quad_perm 1,0,3,2
+    m = m > o ? m : o;
+  }
+  if (G >= 4) {
+    o = __builtin_amdgcn_update_dpp(0u, m, 0x4e, 0xf, 0xf, false);  // quad_perm 2,3,0,1
+    m = m > o ? m : o;
+  }
+  if (G >= 8) {
+    o = __builtin_amdgcn_update_dpp(0u, m, 0x141, 0xf, 0xf, false);  // row_half_mirror
+    m = m > o ? m : o;
+  }
+  if (G >= 16) {
+    o = __builtin_amdgcn_update_dpp(0u, m, 0x140, 0xf, 0xf, false);  // row_mirror
+    m = m > o ? m : o;
+  }
+#pragma unroll
+  for (int off = 16; off < G; off <<= 1) {
+    o = __shfl_xor(m, off, 64);
+    m = m > o ? m : o;
+  }
+  return m;
+}
 
+// Codes of one lane's 8 elements given the block's absmax bits m.
+template <int QT>
+__device__ __forceinline__ uint32_t encode_lane(const uint32_t d[4], uint32_t m,
+                                                const uint2 *lut, const uint32_t *recip) {
+  float r;
+  const bool fast = block_recip(m, recip, r);
+  const float a = bf16_bits_to_f32(m);
+  if (__builtin_amdgcn_ballot_w64(!fast) == 0) return encode8<QT, true>(d, a, r, lut);
+  return encode8<QT, false>(d, a, 0.0f, lut);
+}
+
+// Packed codes of elements e0 .. e0 + 7; in a ragged tail the nibbles of
+// missing elements are cleared and only the bytes that exist (ceil(n/2) in
+// total) are written.
+__device__ __forceinline__ void store_codes(const QuantArgs &args, int64_t e0, uint32_t word) {
+  if (e0 + 8 <= args.n) {
+    *reinterpret_cast<uint32_t *>(args.packed + e0 / 2) = word;
+  } else if (e0 < args.n) {
+    const int64_t valid = args.n - e0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (2 * b >= valid) break;
+      uint32_t byte = (word >> (8 * b)) & 0xffu;
+      if (2 * b + 1 >= valid) byte &= 0xf0u;
+      args.packed[e0 / 2 + b] = (uint8_t)byte;
+    }
+  }
+}
+
+// Zero the elements at or past n among a lane's 8 (d holds e0 .. e0 + 7).
+__device__ __forceinline__ void clear_tail(uint32_t (&d)[4], int64_t e0, int64_t n) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (e0 + 2 * j >= n) d[j] = 0u;
+    else if (e0 + 2 * j + 1 >= n) d[j] &= 0xffffu;
+  }
+}
+
+__device__ __forceinline__ void load_tables(uint2 *lut, uint32_t *recip, const QuantArgs &args) {
+  if (threadIdx.x < kLutSize) {
+    const int c = threadIdx.x < kCells ? threadIdx.x : kCells - 1;
+    lut[threadIdx.x] = make_uint2(__float_as_uint(args.cell_thr[c]), args.cell_codes[c]);
+  }
+  if (threadIdx.x < 128) recip[threadIdx.x] = args.recip[threadIdx.x];
+  __syncthreads();
+}
+
+// ---- blocks of at most 512 elements: the chunk pipeline ------------------
+constexpr int kInFlight = 4;
+
+// Loads of chunk `chunk` through a buffer resource whose range is the chunk's
+// bytes rounded up to whole 16-byte granules: granules past the end (and
+// every granule of a chunk past the end) read as 0 without touching memory.
+__device__ __forceinline__ void load_chunk(uint32_t (&d)[4], const QuantArgs &args, int64_t chunk,
+                                           int lane) {
+  const int64_t c0 = chunk * 512;
+  const int64_t rem = args.n - c0;
+  const int64_t valid = rem < 512 ? (rem > 0 ? rem : 0) : 512;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(args.w + (c0 < args.n ? c0 : 0)), (short)0,
+      (int)((2 * valid + 15) & ~(int64_t)15), 0x00020000);
+  const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, 0));
+  d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+}
+
+// Absmax bits (returned) and packed codes of one chunk.
+template <int BS, int QT>
+__device__ __forceinline__ uint32_t encode_chunk(uint32_t (&d)[4], const QuantArgs &args,
+                                                 int64_t chunk, int lane, const uint2 *lut,
+                                                 const uint32_t *recip, uint32_t &word) {
+  if (chunk * 512 + 512 > args.n) clear_tail(d, chunk * 512 + 8 * lane, args.n);
+  const uint32_t m = group_max<BS / 8>(absmax_bits16(d));
+  word = encode_lane<QT>(d, m, lut, recip);
+  return m;
+}
+
+// bs <= 512: wave w of the grid takes chunks w, w + nwaves, w + 2 nwaves, ...
+template <int BS, int QT>
+__global__ __launch_bounds__(kThreads) void quantize_chunks_kernel(QuantArgs args) {
+  constexpr int G = BS / 8;
+  __shared__ uint2 lut[kLutSize];
+  __shared__ uint32_t recip[128];
+  load_tables(lut, recip, args);
+  const int lane = threadIdx.x & 63;
+  // wave-uniform (readfirstlane), so chunk addresses and buffer resources
+  // live in scalar registers
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t nchunks = (args.n + 511) / 512;
+  const int64_t nseq = wave < nchunks ? (nchunks - 1 - wave) / nwaves + 1 : 0;
+
+  // Loads are issued unconditionally (a chunk past the end has an empty
+  // range), so the number of loads in flight is the same on every path and
+  // each encode waits for its own chunk only.
+  uint32_t d[kInFlight][4];
+#pragma unroll
+  for (int u = 0; u < kInFlight; ++u) load_chunk(d[u], args, wave + u * nwaves, lane);
+  for (int64_t i0 = 0; i0 < nseq; i0 += kInFlight) {
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int64_t i = i0 + u;
+      if (i >= nseq) break;
+      const int64_t chunk = wave + i * nwaves;
+      uint32_t word;
+      const uint32_t m = encode_chunk<BS, QT>(d[u], args, chunk, lane, lut, recip, word);
+      load_chunk(d[u], args, chunk + kInFlight * nwaves, lane);
+      store_codes(args, chunk * 512 + 8 * lane, word);
+      const int64_t block = (chunk * 512 + 8 * lane) / BS;
+      if (lane % G == 0 && block < args.nb) args.absmax[block] = bf16_bits_to_f32(m);
+    }
+  }
+}
+
+// ---- blocks of more than 512 elements: whole tiles -----------------------
+// A tile is 64 * E elements, E = bs / 64 per lane in E / 8 chunks (chunk c of
+// the tile is its elements [512 c, 512 c + 512)); a block is bs / 512 chunks.
 template <int BS>
 struct TileShape {
-  static constexpr int E = lane_elems<BS>();
+  static constexpr int E = BS / 64;
   static constexpr int CH = E / 8;      // chunks per lane (per tile)
   static constexpr int kTile = 64 * E;  // elements per tile
 };
 
-// Loads of one tile through a buffer resource whose range is the tile's bytes
-// rounded up to whole 16-byte granules (w is 16-byte aligned and so is every
-// tile, so the range never leaves the granule of element n - 1, and a
-// granule never crosses a page): granules past the end read as 0 without a
-// branch. In the last, ragged tile the elements at or past n inside the final
-// granule are then cleared explicitly.
+// Loads of one tile, with the same range rule as load_chunk.
 template <int BS>
 __device__ __forceinline__ void load_tile(uint32_t (&d)[TileShape<BS>::CH][4],
                                           const QuantArgs &args, int64_t tile, int lane) {
@@ -126,136 +325,73 @@ __device__ __forceinline__ void load_tile(uint32_t (&d)[TileShape<BS>::CH][4],
         uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(1024 * c + 16 * lane), 0, 0));
     d[c][0] = v.x; d[c][1] = v.y; d[c][2] = v.z; d[c][3] = v.w;
   }
-  if (valid < kTile) {
-#pragma unroll
-    for (int c = 0; c < CH; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t e = 512 * c + 8 * lane + 2 * j;  // element of the low half
-        if (e >= valid) d[c][j] = 0u;
-        else if (e + 1 >= valid) d[c][j] &= 0xffffu;
-      }
-  }
-}
-
-// Absmax, codes and stores of one tile; mb[c] returns the bf16 bits of the
-// absmax of chunk c's block (every lane of the block holds it).
-template <int BS, int QT, bool kStoreAbsmax = true>
-__device__ __forceinline__ void encode_tile(const uint32_t (&d)[TileShape<BS>::CH][4],
-                                            const QuantArgs &args, int64_t tile, int lane,
-                                            const uint2 *lut,
-                                            uint32_t (&mb)[TileShape<BS>::CH]) {
-  constexpr int CH = TileShape<BS>::CH, kTile = TileShape<BS>::kTile;
-  const int64_t t0 = tile * kTile;
-  // scale of each chunk: the absmax of its block, exact, in bf16 bit space
-  if constexpr (BS <= 512) {
-    constexpr int G = BS / 8;  // lanes per block
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      uint32_t m = absmax_bits16(d[c]);
-#pragma unroll
-      for (int off = 1; off < G; off <<= 1) {
-        const uint32_t o = __shfl_xor(m, off, 64);
-        m = m > o ? m : o;
-      }
-      mb[c] = m;
-      const int64_t block = (t0 + 512 * c + 8 * lane) / BS;
-      if (kStoreAbsmax && lane % G == 0 && block < args.nb) args.absmax[block] = bf16_bits_to_f32(m);
-    }
-  } else {
-    constexpr int CPB = BS / 512;  // chunks per block
-#pragma unroll
-    for (int j = 0; j < CH / CPB; ++j) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int c = j * CPB; c < (j + 1) * CPB; ++c) {
-        const uint32_t mc = absmax_bits16(d[c]);
-        m = m > mc ? m : mc;
-      }
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_xor(m, off, 64);
-        m = m > o ? m : o;
-      }
-#pragma unroll
-      for (int c = j * CPB; c < (j + 1) * CPB; ++c) mb[c] = m;
-      const int64_t block = t0 / BS + j;
-      if (kStoreAbsmax && lane == 0 && block < args.nb) args.absmax[block] = bf16_bits_to_f32(m);
-    }
-  }
-
-  const bool whole_tile = t0 + kTile <= args.n;
-#pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const float a = bf16_bits_to_f32(mb[c]);
-    const bool fast = (a == 0.0f) || (a >= 0x1p-100f && a < 0x1p120f);
-    const float r = (a == 0.0f) ? 0.0f : 1.0f / a;
-    const uint32_t word = encode8<QT>(d[c], a, r, fast, lut);
-    const int64_t e0 = t0 + 512 * c + 8 * lane;
-    if (whole_tile) {
-      *reinterpret_cast<uint32_t *>(args.packed + e0 / 2) = word;
-    } else if (e0 < args.n) {
-      // ragged tail: clear the nibbles of missing elements, store only the
-      // bytes that exist (ceil(n/2) in total)
-      const int64_t valid = args.n - e0;
-      if (valid >= 8) {
-        *reinterpret_cast<uint32_t *>(args.packed + e0 / 2) = word;
-      } else {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          if (2 * b >= valid) break;
-          uint32_t byte = (word >> (8 * b)) & 0xffu;
-          if (2 * b + 1 >= valid) byte &= 0xf0u;
-          args.packed[e0 / 2 + b] = (uint8_t)byte;
-        }
-      }
-    }
-  }
-}
-
-__device__ __forceinline__ void load_lut(uint2 *lut, const QuantArgs &args) {
-  if (threadIdx.x < kLutSize) {
-    const int c = threadIdx.x < kCells ? threadIdx.x : kCells - 1;
-    lut[threadIdx.x] = make_uint2(__float_as_uint(args.cell_thr[c]), args.cell_codes[c]);
-  }
-  __syncthreads();
 }
 
 template <int BS, int QT>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(QuantArgs args) {
+__device__ __forceinline__ void encode_tile(uint32_t (&d)[TileShape<BS>::CH][4],
+                                            const QuantArgs &args, int64_t tile, int lane,
+                                            const uint2 *lut, const uint32_t *recip) {
+  constexpr int CH = TileShape<BS>::CH, kTile = TileShape<BS>::kTile;
+  constexpr int CPB = BS / 512;  // chunks per block
+  const int64_t t0 = tile * kTile;
+  if (t0 + kTile > args.n) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) clear_tail(d[c], t0 + 512 * c + 8 * lane, args.n);
+  }
+#pragma unroll
+  for (int j = 0; j < CH / CPB; ++j) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int c = j * CPB; c < (j + 1) * CPB; ++c) {
+      const uint32_t mc = absmax_bits16(d[c]);
+      m = m > mc ? m : mc;
+    }
+    m = group_max<64>(m);
+    const int64_t block = t0 / BS + j;
+    if (lane == 0 && block < args.nb) args.absmax[block] = bf16_bits_to_f32(m);
+#pragma unroll
+    for (int c = j * CPB; c < (j + 1) * CPB; ++c)
+      store_codes(args, t0 + 512 * c + 8 * lane, encode_lane<QT>(d[c], m, lut, recip));
+  }
+}
+
+template <int BS, int QT>
+__global__ __launch_bounds__(kThreads) void quantize_tiles_kernel(QuantArgs args) {
   constexpr int CH = TileShape<BS>::CH;
   __shared__ uint2 lut[kLutSize];
-  load_lut(lut, args);
+  __shared__ uint32_t recip[128];
+  load_tables(lut, recip, args);
 
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
 
-  // two tiles in flight per wave: the loads of the next tile are issued
-  // before the current one is encoded
-  uint32_t da[CH][4], db[CH][4], mb[CH];
+  uint32_t da[CH][4], db[CH][4];
   int64_t tile = wave;
   if (tile < args.ntiles) load_tile<BS>(da, args, tile, lane);
   for (; tile < args.ntiles; tile += 2 * nwaves) {
     const int64_t t1 = tile + nwaves;
     load_tile<BS>(db, args, t1 < args.ntiles ? t1 : tile, lane);
-    encode_tile<BS, QT>(da, args, tile, lane, lut, mb);
+    encode_tile<BS, QT>(da, args, tile, lane, lut, recip);
     if (t1 >= args.ntiles) break;
     const int64_t t2 = t1 + nwaves;
     load_tile<BS>(da, args, t2 < args.ntiles ? t2 : t1, lane);
-    encode_tile<BS, QT>(db, args, t1, lane, lut, mb);
+    encode_tile<BS, QT>(db, args, t1, lane, lut, recip);
   }
 }
 
-// Quantization with the double quantization of its block scales in the same
-// pass [NF4 page, CSDN "bitsandbytes 是一个用于高效量化和加载大型语言模型（LLM）的开源库",
+// ---- quantization with double quantization in one pass -------------------
+// [NF4 page, CSDN "bitsandbytes 是一个用于高效量化和加载大型语言模型（LLM）的开源库",
 // table 实际性能差异, row 训练稳定性（QLoRA）: the block scales are quantized
-// again with INT8]. A workgroup owns one group of 256 blocks at a time, TPW
-// tiles per wave; the scales of the group meet in LDS, where every wave takes
-// their maximum, and the threads then store the fp32 absmax and the int8 code
-// of one block each, so both stores are coalesced. The arithmetic is that of
-// the separate double-quant kernel: m = fmaxf over the group, s2 = RN(m / 127)
-// (0 for m = 0), q = clamp(rint(RN(a / s2)), -127, 127), ties to even.
+// again with INT8]. A workgroup owns one group of 256 blocks at a time and
+// each of its W waves a contiguous run of CPW chunks of it, walked with the
+// chunk pipeline (the window runs on into the workgroup's next group). The
+// scales of the group meet in LDS, where every wave takes their maximum, and
+// the threads then store the fp32 absmax and the int8 code of one block each,
+// so both stores are coalesced. The arithmetic is that of the separate
+// double-quant kernel: m = fmaxf over the group, s2 = RN(m / 127) (0 for
+// m = 0), q = clamp(rint(RN(a / s2)), -127, 127), ties to even.
 __device__ __forceinline__ int8_t dq_code(float a, float s2) {
   if (s2 == 0.0f) return 0;
   float r = __builtin_rintf(a / s2);
@@ -264,72 +400,67 @@ __device__ __forceinline__ int8_t dq_code(float a, float s2) {
 }
 
 constexpr int kGroupBlocks = 256;
-constexpr int64_t kMaxDqGroups = 256 * 8;  // workgroups of one fused launch
+constexpr int64_t kMaxDqGroups = 256 * 64;  // workgroups of one fused launch
 
-// W waves per group: 4 in general (three workgroups fit a CU), 8 when there
-// are too few groups to give every CU more than one workgroup.
 template <int BS, int W>
 struct DqShape {
-  static constexpr int TPG = kGroupBlocks * BS / TileShape<BS>::kTile;  // tiles per group
-  static constexpr int TPW = TPG / W;                                   // tiles per wave
-  static constexpr int kThreads = 64 * W;
+  static constexpr int CPG = kGroupBlocks * BS / 512;  // chunks per group
+  static constexpr int CPW = CPG / W;                  // chunks per wave
 };
 
 template <int BS, int QT, int W>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(3))) void quantize_dq_kernel(
-    QuantArgs args, int8_t *absmax_q, float *absmax_scale, int64_t ngroups) {
-  constexpr int CH = TileShape<BS>::CH, kTile = TileShape<BS>::kTile;
-  constexpr int TPG = DqShape<BS, W>::TPG, TPW = DqShape<BS, W>::TPW, NT = DqShape<BS, W>::kThreads;
-  static_assert(BS <= 512 && TPW % 2 == 0 && TPG % TPW == 0, "an even number of tiles per wave");
-  constexpr int G = BS / 8;  // lanes per block within a chunk
+__global__ __launch_bounds__(64 * W) void quantize_dq_kernel(QuantArgs args, int8_t *absmax_q,
+                                                            float *absmax_scale, int64_t ngroups) {
+  constexpr int CPG = DqShape<BS, W>::CPG, CPW = DqShape<BS, W>::CPW;
+  static_assert(BS <= 512 && CPW % kInFlight == 0, "whole windows per wave and group");
+  constexpr int G = BS / 8;  // lanes per block
 
   __shared__ uint2 lut[kLutSize];
+  __shared__ uint32_t recip[128];
   __shared__ float sabs[2][kGroupBlocks];
-  if (threadIdx.x < kLutSize) {
-    const int c = threadIdx.x < kCells ? threadIdx.x : kCells - 1;
-    lut[threadIdx.x] = make_uint2(__float_as_uint(args.cell_thr[c]), args.cell_codes[c]);
-  }
-  __syncthreads();
+  load_tables(lut, recip, args);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t first_tile = (int64_t)wave * TPW;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+  // i-th chunk of this wave: group blockIdx.x + (i / CPW) * gridDim.x, chunk
+  // wave * CPW + i % CPW of that group
+  const int64_t my_groups =
+      blockIdx.x < ngroups ? (ngroups - 1 - blockIdx.x) / gridDim.x + 1 : 0;
+  const int64_t nseq = my_groups * CPW;
+  auto chunk_of = [&](int64_t i) -> int64_t {
+    return ((int64_t)blockIdx.x + (i / CPW) * gridDim.x) * CPG + wave * CPW + i % CPW;
+  };
 
-  uint32_t buf[2][CH][4], mb[CH];
-  int64_t group = blockIdx.x;
-  if (group < ngroups) load_tile<BS>(buf[0], args, group * TPG + first_tile, lane);
-  for (int it = 0; group < ngroups; group += gridDim.x, ++it) {
+  // loads are unconditional: past the last group a chunk has an empty range
+  uint32_t d[kInFlight][4];
+#pragma unroll
+  for (int u = 0; u < kInFlight; ++u) load_chunk(d[u], args, chunk_of(u), lane);
+  for (int64_t i0 = 0; i0 < nseq; i0 += kInFlight) {
+    const int64_t it = i0 / CPW;
     float *sa = sabs[it & 1];
-    // tiles in pairs, so that the register buffer of each is known at compile time
-#pragma unroll 1
-    for (int tp = 0; tp < TPW; tp += 2) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int t = tp + u;
-        const int64_t tile = group * TPG + first_tile + t;
-        // the last tile of the group prefetches the first of the next group
-        const int64_t next = t + 1 < TPW ? tile + 1
-                             : (group + gridDim.x < ngroups ? (group + gridDim.x) * TPG + first_tile
-                                                            : tile);
-        load_tile<BS>(buf[u ^ 1], args, next, lane);
-        encode_tile<BS, QT, false>(buf[u], args, tile, lane, lut, mb);
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-          if (lane % G == 0)
-            sa[((first_tile + t) * kTile + 512 * c + 8 * lane) / BS] = bf16_bits_to_f32(mb[c]);
-      }
+    for (int u = 0; u < kInFlight; ++u) {
+      const int64_t i = i0 + u;
+      const int64_t chunk = chunk_of(i);
+      uint32_t word;
+      const uint32_t m = encode_chunk<BS, QT>(d[u], args, chunk, lane, lut, recip, word);
+      load_chunk(d[u], args, chunk_of(i + kInFlight), lane);
+      store_codes(args, chunk * 512 + 8 * lane, word);
+      if (lane % G == 0) sa[((wave * CPW + i % CPW) * 512 + 8 * lane) / BS] = bf16_bits_to_f32(m);
     }
+    if ((i0 + kInFlight) % CPW != 0) continue;
+    // the group is complete: its scale maximum (blocks past n hold 0), taken by every wave
+    const int64_t group = (int64_t)blockIdx.x + it * gridDim.x;
     __syncthreads();
-    // group maximum (blocks past n hold 0), taken by every wave
-    float m = 0.0f;
+    float mx = 0.0f;
 #pragma unroll
-    for (int k = 0; k < kGroupBlocks / 64; ++k) m = fmaxf(m, sa[lane + 64 * k]);
+    for (int k = 0; k < kGroupBlocks / 64; ++k) mx = fmaxf(mx, sa[lane + 64 * k]);
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    const float s2 = (m == 0.0f) ? 0.0f : m / 127.0f;
+    for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+    const float s2 = (mx == 0.0f) ? 0.0f : mx / 127.0f;
     if (threadIdx.x == 0) absmax_scale[group] = s2;
 #pragma unroll
-    for (int i = threadIdx.x; i < kGroupBlocks; i += NT) {
+    for (int i = threadIdx.x; i < kGroupBlocks; i += 64 * W) {
       const int64_t block = group * kGroupBlocks + i;
       if (block < args.nb) {
         const float a = sa[i];
@@ -347,24 +478,32 @@ void launch_qdq_w(int64_t groups, QuantArgs args, int8_t *absmax_q, float *absma
                      stream, args, absmax_q, absmax_scale, ngroups);
 }
 
+// Waves per group: the fewest of 4, 8, 16 that give the launch at least
+// kWantWaves waves (8 per SIMD), while every wave keeps at least one whole
+// window of chunks.
+constexpr int64_t kWantWaves = 256 * 4 * 8;
+
+template <int BS, int QT>
+void launch_qdq_bs(int64_t blocks, QuantArgs args, int8_t *absmax_q, float *absmax_scale,
+                   int64_t ngroups, hipStream_t stream) {
+  constexpr int kMaxW = DqShape<BS, 1>::CPG / kInFlight >= 16 ? 16 : DqShape<BS, 1>::CPG / kInFlight;
+  if (ngroups * 4 >= kWantWaves || kMaxW < 8)
+    launch_qdq_w<BS, QT, 4>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
+  else if (ngroups * 8 >= kWantWaves || kMaxW < 16)
+    launch_qdq_w<BS, QT, (kMaxW < 8 ? 4 : 8)>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
+  else
+    launch_qdq_w<BS, QT, (kMaxW < 8 ? 4 : (kMaxW < 16 ? 8 : 16))>(blocks, args, absmax_q, absmax_scale, ngroups,
+                                                  stream);
+}
+
 template <int QT>
 hipError_t launch_qdq(int blocksize, int64_t blocks, QuantArgs args, int8_t *absmax_q,
                       float *absmax_scale, int64_t ngroups, hipStream_t stream) {
-  const bool wide = ngroups <= 256;
   switch (blocksize) {
-    case 64:
-      launch_qdq_w<64, QT, 4>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
-      break;
-    case 128:
-      if (wide) launch_qdq_w<128, QT, 8>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
-      else launch_qdq_w<128, QT, 4>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
-      break;
-    case 256:
-      if (wide) launch_qdq_w<256, QT, 8>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
-      else launch_qdq_w<256, QT, 4>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 64: launch_qdq_bs<64, QT>(blocks, args, absmax_q, absmax_scale, ngroups, stream); break;
+    case 128: launch_qdq_bs<128, QT>(blocks, args, absmax_q, absmax_scale, ngroups, stream); break;
+    case 256: launch_qdq_bs<256, QT>(blocks, args, absmax_q, absmax_scale, ngroups, stream); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -372,19 +511,24 @@ hipError_t launch_qdq(int blocksize, int64_t blocks, QuantArgs args, int8_t *abs
 template <int QT>
 hipError_t launch_qt(int blocksize, dim3 grid, QuantArgs args, hipStream_t stream) {
   switch (blocksize) {
-#define NF4_QCASE(BSV)                                                                   \
-  case BSV:                                                                              \
-    hipLaunchKernelGGL((quantize_kernel<BSV, QT>), grid, dim3(kThreads), 0, stream, args); \
+#define NF4_QCCASE(BSV)                                                                         \
+  case BSV:                                                                                     \
+    hipLaunchKernelGGL((quantize_chunks_kernel<BSV, QT>), grid, dim3(kThreads), 0, stream, args); \
     break;
-    NF4_QCASE(32)
-    NF4_QCASE(64)
-    NF4_QCASE(128)
-    NF4_QCASE(256)
-    NF4_QCASE(512)
-    NF4_QCASE(1024)
-    NF4_QCASE(2048)
-    NF4_QCASE(4096)
-#undef NF4_QCASE
+#define NF4_QTCASE(BSV)                                                                        \
+  case BSV:                                                                                    \
+    hipLaunchKernelGGL((quantize_tiles_kernel<BSV, QT>), grid, dim3(kThreads), 0, stream, args); \
+    break;
+    NF4_QCCASE(32)
+    NF4_QCCASE(64)
+    NF4_QCCASE(128)
+    NF4_QCCASE(256)
+    NF4_QCCASE(512)
+    NF4_QTCASE(1024)
+    NF4_QTCASE(2048)
+    NF4_QTCASE(4096)
+#undef NF4_QCCASE
+#undef NF4_QTCASE
     default:
       return hipErrorInvalidValue;
   }
@@ -400,12 +544,19 @@ QuantArgs make_args(const uint16_t *w, int64_t n, int blocksize, int quant_type,
   args.absmax = absmax;
   args.n = n;
   args.nb = (n + blocksize - 1) / blocksize;
-  const int E = blocksize / 64 > 32 ? blocksize / 64 : 32;
-  const int64_t tile_elems = 64LL * E;
+  const int64_t tile_elems = blocksize > 512 ? blocksize : 512;
   args.ntiles = (n + tile_elems - 1) / tile_elems;
   for (int i = 0; i < kCells; ++i) {
     args.cell_thr[i] = t.cell_thr[i];
     args.cell_codes[i] = t.cell_codes[i];
+  }
+  for (int k = 0; k < 128; ++k) {
+    // 1 + k/128 is exact in fp32 and the host division is IEEE (correctly rounded)
+    volatile float den = 1.0f + (float)k / 128.0f;
+    const float rk = 1.0f / den;
+    uint32_t bits;
+    __builtin_memcpy(&bits, &rk, 4);
+    args.recip[k] = bits + (127u << 23);
   }
   return args;
 }
@@ -435,9 +586,9 @@ hipError_t launch_quantize(const uint16_t *w, int64_t n, int blocksize, int quan
                            uint8_t *packed, float *absmax, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const QuantArgs args = make_args(w, n, blocksize, quant_type, packed, absmax);
-  // Enough waves to keep every CU's memory pipeline busy; each wave then
-  // strides over the remaining tiles.
-  const int64_t waves_wanted = args.ntiles;
+  // Enough waves to keep every CU's memory pipeline busy (about four chunks
+  // or one tile per wave); each wave then strides over the rest.
+  const int64_t waves_wanted = blocksize <= 512 ? (args.ntiles + 3) / 4 : args.ntiles;
   int64_t blocks = (waves_wanted + (kThreads / 64) - 1) / (kThreads / 64);
   const int64_t max_blocks = 256 * 16;
   if (blocks > max_blocks) blocks = max_blocks;
