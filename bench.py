@@ -6,8 +6,11 @@ double quantization at blocksize 64 by default):
   1. quantize + double-quant every weight (and the prefill weight),
   2. dequantize every weight to bf16,
   3. decode GEMV (M = 1, independent seeded x per matrix) through every weight,
-  4. one prefill GEMM, X[2048, 4096] . W[14336, 4096]^T (NF4 bs 64 + double
-     quant, fp32 accumulation, bf16 output),
+  4. the prefill GEMM, X[2048, 4096] . W[14336, 4096]^T (NF4 bs 64 + double
+     quant, fp32 accumulation, bf16 output), over --gemm-weights distinct
+     seeded weights of that shape back to back (4 by default: a prefill runs
+     its layers' GEMMs in a row, so one isolated launch would mostly time the
+     clock ramp of an idle GPU),
 then the same three stack phases at the other blocksizes of the sweep (128,
 256), and the MLP-shaped decode products one matrix per launch: W [11008, 4096]
 and [4096, 11008], NF4 bs 64 + double quant, M in {1, 4, 8, 16}, each timed
@@ -50,7 +53,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # source the benchmark reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
     "gemv1.hip": ("567298647b500fe76e0e58664b57e622511ba6eb1c221441c73d9a7d0b53ec70", 105795665),
-    "gemm.hip": ("9baba3229fe56ef6578454664ee507889d01c24c6ecf3f90b460d01eee38ba0a", 335843173),
+    "gemm.hip": ("656b93bf13dfda4fc1f6125c152f6d726d1803cdfaeb797536cdf5114cfd0bed", 335046814),
 }
 
 
@@ -70,6 +73,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--bs", type=int, default=64, choices=[32, 64, 128, 256, 512, 1024, 2048, 4096])
     ap.add_argument("--layers", type=int, default=32)
+    ap.add_argument("--gemm-weights", type=int, default=4,
+                    help="distinct [14336, 4096] weights the prefill GEMM phase runs through")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--phases", default="quantize,dequantize,gemv,gemm,sweep,mlp",
@@ -139,7 +144,14 @@ def main():
     pw = gpu_normal((pm.rows, pm.cols), pm.sigma, pm.seed)
     px = gpu_normal((prefill.ms[0], pm.cols), 1.0, prefill.x_seed)
     pqs = nf4.quantize(pw, 64, "nf4", double_quant=True)
-    py = torch.empty((prefill.ms[0], pm.rows), dtype=torch.bfloat16, device=dev)
+    # the GEMM phase's weights: the prefill weight, then seeds pm.seed + 1, ...
+    gemm_w = [pqs]
+    for r in range(1, args.gemm_weights):
+        w = gpu_normal((pm.rows, pm.cols), pm.sigma, pm.seed + r)
+        gemm_w.append(nf4.quantize(w, 64, "nf4", double_quant=True))
+        del w
+    gemm_y = [torch.empty((prefill.ms[0], pm.rows), dtype=torch.bfloat16, device=dev)
+              for _ in gemm_w]
     torch.cuda.synchronize()
 
     def quantize_at(b, with_prefill):
@@ -167,7 +179,8 @@ def main():
         return f
 
     def ph_gemm():
-        nf4.gemm(px, pqs, out=py)
+        for q, y in zip(gemm_w, gemm_y):
+            nf4.gemm(px, q, out=y)
 
     # MLP-shaped products, one matrix per launch, rotating over distinct
     # weights: the stack's [11008, 4096] matrices (bs 64), and 48 seeded
@@ -308,7 +321,7 @@ def main():
         per = N * K // 2 + meta_bytes(N * K, 64) + 2 * m * K + 4 * m * N
         work[key] = dict(bytes=per * len(e["qss"]), launches=len(e["qss"]))
     M = prefill.ms[0]
-    work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols, launches=1)
+    work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols * len(gemm_w), launches=len(gemm_w))
     work["copy"] = dict(bytes=2 * (1 << 30), launches=1)
 
     phase_out = {}
@@ -346,9 +359,11 @@ def main():
         "config": {
             "workload": f"7B-shaped stack: {args.layers} layers x (4 x [4096,4096] + 3 x "
                         f"[11008,4096]) NF4 bs{bs} + double quant (256); decode GEMV M=1 per "
-                        "matrix (the 7 products of a layer in one grouped launch); + prefill GEMM 2048x4096x14336 NF4 bs64 + double quant",
+                        "matrix (the 7 products of a layer in one grouped launch); + prefill GEMM 2048x4096x14336 NF4 bs64 + double quant "
+                        f"over {len(gemm_w)} distinct weights back to back",
             "blocksize": bs, "quant_type": "nf4", "double_quant": True,
             "stack_params": n_stack, "gemv_m": 1, "gemm_mnk": [M, pm.rows, pm.cols],
+            "gemm_weights": len(gemm_w),
             "also_timed": "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
                           "[11008,4096] (up) and [4096,11008] (down) NF4 bs64 + double quant, "
                           "one product per launch over >1 GB of distinct weights, M = 1/4/8/16",
@@ -367,7 +382,7 @@ def main():
         }
     if "gemm" in phase_out:
         us = ms["gemm"] * 1e3 / work["gemm"]["launches"]
-        tf = work["gemm"]["flops"] / us / 1e6
+        tf = work["gemm"]["flops"] / work["gemm"]["launches"] / us / 1e6
         result["roofline_gemm"] = {
             "kernel": "gemm_kernel (NF4 prefill GEMM)", "bound": "mfma", "achieved": round(tf, 1),
             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",

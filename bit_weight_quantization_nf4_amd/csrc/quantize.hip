@@ -213,6 +213,19 @@ __device__ __forceinline__ void store_codes(const QuantArgs &args, int64_t e0, u
   }
 }
 
+// The codes of one chunk: a whole chunk (the test is wave-uniform) stores
+// through the chunk's base address plus a lane offset; the ragged last chunk
+// goes element-wise.
+__device__ __forceinline__ void store_chunk(const QuantArgs &args, int64_t chunk, int lane,
+                                            uint32_t word) {
+  if (chunk * 512 + 512 <= args.n) {
+    uint32_t *base = reinterpret_cast<uint32_t *>(args.packed + chunk * 256);
+    base[lane] = word;
+  } else {
+    store_codes(args, chunk * 512 + 8 * lane, word);
+  }
+}
+
 // Zero the elements at or past n among a lane's 8 (d holds e0 .. e0 + 7).
 __device__ __forceinline__ void clear_tail(uint32_t (&d)[4], int64_t e0, int64_t n) {
 #pragma unroll
@@ -291,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void quantize_chunks_kernel(QuantArgs arg
       uint32_t word;
       const uint32_t m = encode_chunk<BS, QT>(d[u], args, chunk, lane, lut, recip, word);
       load_chunk(d[u], args, chunk + kInFlight * nwaves, lane);
-      store_codes(args, chunk * 512 + 8 * lane, word);
+      store_chunk(args, chunk, lane, word);
       const int64_t block = (chunk * 512 + 8 * lane) / BS;
       if (lane % G == 0 && block < args.nb) args.absmax[block] = bf16_bits_to_f32(m);
     }
@@ -445,7 +458,7 @@ __global__ __launch_bounds__(64 * W) void quantize_dq_kernel(QuantArgs args, int
       uint32_t word;
       const uint32_t m = encode_chunk<BS, QT>(d[u], args, chunk, lane, lut, recip, word);
       load_chunk(d[u], args, chunk_of(i + kInFlight), lane);
-      store_codes(args, chunk * 512 + 8 * lane, word);
+      store_chunk(args, chunk, lane, word);
       if (lane % G == 0) sa[((wave * CPW + i % CPW) * 512 + 8 * lane) / BS] = bf16_bits_to_f32(m);
     }
     if ((i0 + kInFlight) % CPW != 0) continue;
