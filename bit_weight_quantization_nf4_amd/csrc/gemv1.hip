@@ -146,7 +146,9 @@ __attribute__((amdgpu_waves_per_eu(waves_per_simd<J>(), waves_per_simd<J>())))
 void gemv1_kernel(Gemv1Args args) {
   __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
   // x of the workgroup's problem, slice j at 8 KB j; lane l's 16-byte piece
-  // q of a slice sits at index 64 q + l, so each piece read is conflict-free
+  // q of a slice sits at index 64 q + (l + 2 q) mod 64: the 16 lanes of a
+  // piece read (same q) and the 16 threads of a store (8 q's, 2 l's) each
+  // cover all 16 bank groups, so neither conflicts
   __shared__ uint4 xs[J * 512];
 
   const int lane = threadIdx.x & 63;
@@ -362,14 +364,17 @@ void gemv1_kernel(Gemv1Args args) {
     }
     // piece t of a slice belongs to lane t / 8, as its piece t % 8
 #pragma unroll
-    for (int j = 0; j < J; ++j) xs[512 * j + 64 * (threadIdx.x % 8) + threadIdx.x / 8] = xg[j];
+    for (int j = 0; j < J; ++j) {
+      const int q = threadIdx.x % 8, l = threadIdx.x / 8;
+      xs[512 * j + 64 * q + ((l + 2 * q) & 63)] = xg[j];
+    }
     __syncthreads();
     if (!active) return;
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const uint4 v = xs[512 * j + 64 * q + lane];
+        const uint4 v = xs[512 * j + 64 * q + ((lane + 2 * q) & 63)];
         xv[j][4 * q] = v.x;
         xv[j][4 * q + 1] = v.y;
         xv[j][4 * q + 2] = v.z;
