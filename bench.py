@@ -6,6 +6,8 @@ double quantization at blocksize 64 by default):
   1. quantize + double-quant every weight (and the prefill weight),
   2. dequantize every weight to bf16,
   3. decode GEMV (M = 1, independent seeded x per matrix) through every weight,
+     the seven products of a layer in one grouped launch (and, as the separate
+     phase gemv_single, one launch per matrix),
   4. the prefill GEMM, X[2048, 4096] . W[14336, 4096]^T (NF4 bs 64 + double
      quant, fp32 accumulation, bf16 output), over --gemm-weights distinct
      seeded weights of that shape back to back (4 by default: a prefill runs
@@ -52,8 +54,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # for the kernel source it was taken on (its SHA-256); after any change to that
 # source the benchmark reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "gemv1.hip": ("567298647b500fe76e0e58664b57e622511ba6eb1c221441c73d9a7d0b53ec70", 105795665),
-    "gemm.hip": ("656b93bf13dfda4fc1f6125c152f6d726d1803cdfaeb797536cdf5114cfd0bed", 335046814),
+    "gemv1.hip": ("daedb838ffa9d27f523da21c50ed7e277cea3f2985ecd3b6f0186ef123b797cc", 105787460),
+    "gemm.hip": ("656b93bf13dfda4fc1f6125c152f6d726d1803cdfaeb797536cdf5114cfd0bed", 334965651),
 }
 
 
@@ -77,8 +79,9 @@ def parse():
                     help="distinct [14336, 4096] weights the prefill GEMM phase runs through")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemm,sweep,mlp",
-                    help="comma list of quantize, dequantize, gemv, gemm (the stack at --bs), "
+    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemv_single,gemm,sweep,mlp",
+                    help="comma list of quantize, dequantize, gemv (grouped per layer), gemv_single "
+                         "(one launch per matrix), gemm (the stack at --bs), "
                          "sweep (quantize, dequantize and gemv at the other blocksizes of "
                          "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16); "
                          "'copy' adds a plain 1 GiB device copy, the known-size reference "
@@ -178,6 +181,12 @@ def main():
                                  outs=[d["y_bs"][b] for d in grp])
         return f
 
+    def gemv_single():
+        # the same products, one launch per matrix (labelled apart from the
+        # grouped phase)
+        for d in mats:
+            nf4.gemv(d["x"], d["qs"], out=d["y"])
+
     def ph_gemm():
         for q, y in zip(gemm_w, gemm_y):
             nf4.gemm(px, q, out=y)
@@ -217,6 +226,7 @@ def main():
         copy_dst.copy_(copy_src)
 
     fns = dict(quantize=quantize_at(bs, True), dequantize=dequantize_at(bs), gemv=gemv_at(bs),
+               gemv_single=gemv_single,
                gemm=ph_gemm, copy=ph_copy)
     for b in sweep_bs:
         fns[f"quantize_bs{b}"] = quantize_at(b, False)
@@ -312,6 +322,7 @@ def main():
     work["quantize"] = quantize_work(bs, True)
     work["dequantize"] = dequantize_work(bs)
     work["gemv"] = gemv_work(bs)
+    work["gemv_single"] = dict(bytes=work["gemv"]["bytes"], launches=len(mats))
     for b in sweep_bs:
         work[f"quantize_bs{b}"] = quantize_work(b, False)
         work[f"dequantize_bs{b}"] = dequantize_work(b)
@@ -364,7 +375,8 @@ def main():
             "blocksize": bs, "quant_type": "nf4", "double_quant": True,
             "stack_params": n_stack, "gemv_m": 1, "gemm_mnk": [M, pm.rows, pm.cols],
             "gemm_weights": len(gemm_w),
-            "also_timed": "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
+            "also_timed": "phase gemv_single: the same decode products, one launch per matrix; "
+                          "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
                           "[11008,4096] (up) and [4096,11008] (down) NF4 bs64 + double quant, "
                           "one product per launch over >1 GB of distinct weights, M = 1/4/8/16",
         },
