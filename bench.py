@@ -3,8 +3,11 @@
 One step = one pass of the whole path over the 7B-shaped stack (32 layers x
 (4 x [4096, 4096] + 3 x [11008, 4096]) bf16 weights, N(0, 0.02^2), NF4 with
 double quantization at blocksize 64 by default):
-  1. quantize + double-quant every weight (and the prefill weight),
-  2. dequantize every weight to bf16,
+  1. quantize + double-quant every weight (and the prefill weight), one call
+     per weight (and, as the separate phase quantize_grouped, the seven weights
+     of a layer per call),
+  2. dequantize every weight to bf16 (likewise per weight, and per layer as
+     dequantize_grouped),
   3. decode GEMV (M = 1, independent seeded x per matrix) through every weight,
      the seven products of a layer in one grouped launch (and, as the separate
      phase gemv_single, one launch per matrix),
@@ -79,9 +82,11 @@ def parse():
                     help="distinct [14336, 4096] weights the prefill GEMM phase runs through")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
-    ap.add_argument("--phases", default="quantize,dequantize,gemv,gemv_single,gemm,sweep,mlp",
-                    help="comma list of quantize, dequantize, gemv (grouped per layer), gemv_single "
-                         "(one launch per matrix), gemm (the stack at --bs), "
+    ap.add_argument("--phases", default="quantize,quantize_grouped,dequantize,dequantize_grouped,"
+                                        "gemv,gemv_single,gemm,sweep,mlp",
+                    help="comma list of quantize, quantize_grouped, dequantize, dequantize_grouped "
+                         "(per matrix / the seven weights of a layer per call), gemv (grouped per "
+                         "layer), gemv_single (one launch per matrix), gemm (the stack at --bs), "
                          "sweep (quantize, dequantize and gemv at the other blocksizes of "
                          "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16); "
                          "'copy' adds a plain 1 GiB device copy, the known-size reference "
@@ -157,6 +162,9 @@ def main():
               for _ in gemm_w]
     torch.cuda.synchronize()
 
+    # the seven weights of a layer: one grouped launch in the grouped phases
+    layers = [mats[i:i + 7] for i in range(0, len(mats), 7)]
+
     def quantize_at(b, with_prefill):
         def f():
             for d in mats:
@@ -165,14 +173,23 @@ def main():
                 nf4.quantize(pw, 64, "nf4", True, out=pqs)
         return f
 
+    def quantize_grouped():
+        # the same work, the seven weights of a layer in one call
+        for grp in layers:
+            nf4.quantize_grouped([d["w"] for d in grp], bs, "nf4", True,
+                                 outs=[d["qs_bs"][bs] for d in grp])
+        nf4.quantize(pw, 64, "nf4", True, out=pqs)
+
+    def dequantize_grouped():
+        for grp in layers:
+            nf4.dequantize_grouped([d["qs_bs"][bs] for d in grp], outs=[d["wd"] for d in grp])
+
     def dequantize_at(b):
         def f():
             for d in mats:
                 nf4.dequantize(d["qs_bs"][b], out=d["wd"])
         return f
 
-    # decode GEMV: the seven independent products of a layer share one launch
-    layers = [mats[i:i + 7] for i in range(0, len(mats), 7)]
 
     def gemv_at(b):
         def f():
@@ -226,7 +243,8 @@ def main():
         copy_dst.copy_(copy_src)
 
     fns = dict(quantize=quantize_at(bs, True), dequantize=dequantize_at(bs), gemv=gemv_at(bs),
-               gemv_single=gemv_single,
+               gemv_single=gemv_single, quantize_grouped=quantize_grouped,
+               dequantize_grouped=dequantize_grouped,
                gemm=ph_gemm, copy=ph_copy)
     for b in sweep_bs:
         fns[f"quantize_bs{b}"] = quantize_at(b, False)
@@ -321,6 +339,8 @@ def main():
 
     work["quantize"] = quantize_work(bs, True)
     work["dequantize"] = dequantize_work(bs)
+    work["quantize_grouped"] = dict(bytes=work["quantize"]["bytes"], launches=len(layers) + 1)
+    work["dequantize_grouped"] = dict(bytes=work["dequantize"]["bytes"], launches=len(layers))
     work["gemv"] = gemv_work(bs)
     work["gemv_single"] = dict(bytes=work["gemv"]["bytes"], launches=len(mats))
     for b in sweep_bs:
@@ -376,6 +396,8 @@ def main():
             "stack_params": n_stack, "gemv_m": 1, "gemm_mnk": [M, pm.rows, pm.cols],
             "gemm_weights": len(gemm_w),
             "also_timed": "phase gemv_single: the same decode products, one launch per matrix; "
+                          "phases quantize_grouped / dequantize_grouped: the stack's quantize / "
+                          "dequantize with the seven weights of a layer in one call; "
                           "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
                           "[11008,4096] (up) and [4096,11008] (down) NF4 bs64 + double quant, "
                           "one product per launch over >1 GB of distinct weights, M = 1/4/8/16",

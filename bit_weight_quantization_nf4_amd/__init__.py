@@ -65,8 +65,16 @@ _SIGNATURES = [
     ("nf4_device_check", ctypes.c_int32, []),
     ("nf4_quantize", ctypes.c_int32,
      [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P]),
+    ("nf4_quantize_grouped", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_int64),
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+      ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
+      ctypes.POINTER(ctypes.c_void_p), _P]),
     ("nf4_double_quant", ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
     ("nf4_dequantize", ctypes.c_int32, [ctypes.POINTER(QWeightDesc), ctypes.c_int32, _P, _P]),
+    ("nf4_dequantize_grouped", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
+      _P]),
     ("nf4_gemv", ctypes.c_int32,
      [_P, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, _P, _P]),
@@ -212,6 +220,48 @@ def quantize(w: torch.Tensor, blocksize: int = 64, quant_type: str = "nf4",
     return out
 
 
+QUANT_MAX_GROUP = 16
+
+
+def _new_state(w: torch.Tensor, blocksize: int, quant_type: str, double_quant: bool) -> QuantState:
+    n = w.numel()
+    nb = (n + blocksize - 1) // blocksize
+    dev = w.device
+    return QuantState(torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev),
+                      torch.empty(nb, dtype=torch.float32, device=dev),
+                      torch.empty(nb, dtype=torch.int8, device=dev) if double_quant else None,
+                      torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev)
+                      if double_quant else None,
+                      tuple(w.shape), blocksize, quant_type, double_quant, 256)
+
+
+def quantize_grouped(ws, blocksize: int = 64, quant_type: str = "nf4", double_quant: bool = False,
+                     outs=None):
+    """nf4_quantize_grouped: several bf16 device tensors quantized in one call
+    (one launch with double quant at blocksize 64/128/256). Returns their
+    QuantStates (or fills ``outs``)."""
+    count = len(ws)
+    if count > QUANT_MAX_GROUP or (outs is not None and len(outs) != count):
+        raise ValueError("quantize_grouped takes at most 16 tensors (and as many outs)")
+    if count == 0:
+        return []
+    ws2, states = [], []
+    for i, w in enumerate(ws):
+        if w.dtype != torch.bfloat16 or not w.is_cuda:
+            raise TypeError("quantize_grouped expects bf16 tensors on the GPU")
+        w2 = _dev(w)
+        ws2.append(w2)
+        states.append(outs[i] if outs is not None else _new_state(w2, blocksize, quant_type,
+                                                                  double_quant))
+    vp = ctypes.c_void_p * count
+    _check(lib().nf4_quantize_grouped(
+        count, vp(*[_ptr(t) for t in ws2]), (ctypes.c_int64 * count)(*[t.numel() for t in ws2]),
+        blocksize, _qt(quant_type), int(double_quant), vp(*[_ptr(q.packed) for q in states]),
+        vp(*[_ptr(q.absmax) for q in states]), vp(*[_ptr(q.absmax_q) for q in states]),
+        vp(*[_ptr(q.absmax_scale) for q in states]), _stream(ws2[0])), "nf4_quantize_grouped")
+    return states
+
+
 def double_quant(absmax: torch.Tensor, blocksize2: int = 256):
     """nf4_double_quant: returns (absmax_q int8[nb], absmax_scale fp32[ceil(nb/bs2)])."""
     a = _dev(absmax)
@@ -231,6 +281,24 @@ def dequantize(qs: QuantState, out_dtype=torch.bfloat16, out: torch.Tensor | Non
     _check(lib().nf4_dequantize(ctypes.byref(d), _DT[out.dtype], _ptr(out), _stream(qs.packed)),
            "nf4_dequantize")
     return out
+
+
+def dequantize_grouped(qss, out_dtype=torch.bfloat16, outs=None):
+    """nf4_dequantize_grouped: several quantized tensors dequantized in one
+    launch; returns the list of outputs (or fills ``outs``)."""
+    count = len(qss)
+    if count > QUANT_MAX_GROUP or (outs is not None and len(outs) != count):
+        raise ValueError("dequantize_grouped takes at most 16 tensors (and as many outs)")
+    if count == 0:
+        return []
+    ys = [outs[i] if outs is not None else torch.empty(qs.shape, dtype=out_dtype,
+                                                        device=qs.packed.device)
+          for i, qs in enumerate(qss)]
+    _check(lib().nf4_dequantize_grouped(count, (QWeightDesc * count)(*[q.desc() for q in qss]),
+                                        _DT[ys[0].dtype],
+                                        (ctypes.c_void_p * count)(*[_ptr(y) for y in ys]),
+                                        _stream(qss[0].packed)), "nf4_dequantize_grouped")
+    return ys
 
 
 def _product(fn, name, x, qs, out_dtype, out):
@@ -297,5 +365,6 @@ def gemm(x: torch.Tensor, qs: QuantState, out_dtype=torch.bfloat16, out=None) ->
 
 __all__ = [
     "QuantState", "QWeightDesc", "Nf4Error", "lib", "exported_names", "codebook", "packed_bytes",
-    "num_blocks", "quantize", "double_quant", "dequantize", "gemv", "gemv_grouped", "gemm",
+    "num_blocks", "quantize", "quantize_grouped", "double_quant", "dequantize",
+    "dequantize_grouped", "gemv", "gemv_grouped", "gemm",
 ]

@@ -22,14 +22,35 @@ namespace {
 
 constexpr int kThreads = 256;
 
-struct DequantArgs {
+// One tensor of a launch; tile_begin: its first whole tile in the launch's
+// tile numbering.
+struct DTensor {
   const uint8_t *packed;
   void *out;
   int64_t n;
   ScaleArgs sc;
   int32_t log2_bs;
+  int64_t tile_begin;
+};
+
+constexpr int kMaxDGroup = 16;
+
+struct DequantArgs {
+  DTensor t[kMaxDGroup];
+  int32_t count;
+  int64_t total_tiles;  // whole 1024-element tiles over all tensors
   float value[16];
 };
+
+// tensor of launch tile lt and the tile's index within it
+__device__ __forceinline__ const DTensor &locate_tile(const DequantArgs &args, int64_t lt,
+                                                      int64_t &tile) {
+  int t = 0;
+#pragma unroll 1
+  while (t + 1 < args.count && args.t[t + 1].tile_begin <= lt) ++t;
+  tile = lt - args.t[t].tile_begin;
+  return args.t[t];
+}
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -44,18 +65,20 @@ struct TileIn {
 };
 
 template <bool DQ>
-__device__ __forceinline__ TileIn<DQ> load_tile_in(const DequantArgs &args, int64_t tile, int lane) {
+__device__ __forceinline__ TileIn<DQ> load_tile_in(const DequantArgs &args, int64_t lt, int lane) {
+  int64_t tile;
+  const DTensor &T = locate_tile(args, lt, tile);
   TileIn<DQ> t;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int64_t e0 = tile * 1024 + 512 * half + 8 * lane;
-    t.word[half] = *reinterpret_cast<const uint32_t *>(args.packed + e0 / 2);
-    const int64_t b = e0 >> args.log2_bs;
+    t.word[half] = *reinterpret_cast<const uint32_t *>(T.packed + e0 / 2);
+    const int64_t b = e0 >> T.log2_bs;
     if (DQ) {
-      t.q[half] = args.sc.absmax_q[b];
-      t.a[half] = args.sc.absmax_scale[b >> args.sc.log2_bs2];
+      t.q[half] = T.sc.absmax_q[b];
+      t.a[half] = T.sc.absmax_scale[b >> T.sc.log2_bs2];
     } else {
-      t.a[half] = args.sc.absmax[b];
+      t.a[half] = T.sc.absmax[b];
     }
   }
   return t;
@@ -94,13 +117,15 @@ __device__ __forceinline__ void store8(void *out, int64_t e0, const float (&w)[8
 
 template <bool OUT_BF16, bool DQ>
 __device__ __forceinline__ void write_tile(const DequantArgs &args, const TileIn<DQ> &in,
-                                           int64_t t, int lane, const char *tb) {
+                                           int64_t lt, int lane, const char *tb) {
+  int64_t t;
+  const DTensor &T = locate_tile(args, lt, t);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const float ap = DQ ? (float)in.q[half] * in.a[half] : in.a[half];
     float w[8];
     decode8(in.word[half], ap, tb, w);
-    store8<OUT_BF16>(args.out, t * 1024 + 512 * half + 8 * lane, w);
+    store8<OUT_BF16>(T.out, t * 1024 + 512 * half + 8 * lane, w);
   }
 }
 
@@ -115,7 +140,7 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-  const int64_t nfull = args.n >> 10;  // whole 1024-element tiles
+  const int64_t nfull = args.total_tiles;  // whole 1024-element tiles
 
   // whole tiles, two register sets in turn: the inputs of a wave's tile after
   // next are loaded as soon as a set has been decoded, so their latency
@@ -137,27 +162,32 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
     }
   }
 
-  // the ragged last tile, element by element where a piece is cut short
-  if ((args.n & 1023) != 0 && wave == nfull % nwaves) {
+  // the ragged last tile of each tensor, element by element where a piece is
+  // cut short (tensor i's by wave i mod nwaves)
+#pragma unroll 1
+  for (int ti = 0; ti < args.count; ++ti) {
+    const DTensor &T = args.t[ti];
+    if ((T.n & 1023) == 0 || wave != ti % nwaves) continue;
+    const int64_t tl = T.n >> 10;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int64_t e0 = nfull * 1024 + 512 * half + 8 * lane;
-      if (e0 >= args.n) continue;
-      const float ap = block_scale(args.sc, e0 >> args.log2_bs);
-      const int64_t nbytes = (args.n - e0 + 1) / 2;
+      const int64_t e0 = tl * 1024 + 512 * half + 8 * lane;
+      if (e0 >= T.n) continue;
+      const float ap = block_scale(T.sc, e0 >> T.log2_bs);
+      const int64_t nbytes = (T.n - e0 + 1) / 2;
       uint32_t word = 0;
       for (int i = 0; i < 4; ++i)
-        if (i < nbytes) word |= (uint32_t)args.packed[e0 / 2 + i] << (8 * i);
+        if (i < nbytes) word |= (uint32_t)T.packed[e0 / 2 + i] << (8 * i);
       float w[8];
       decode8(word, ap, tb, w);
-      if (e0 + 8 <= args.n) {
-        store8<OUT_BF16>(args.out, e0, w);
+      if (e0 + 8 <= T.n) {
+        store8<OUT_BF16>(T.out, e0, w);
       } else if (OUT_BF16) {
-        uint16_t *o = reinterpret_cast<uint16_t *>(args.out) + e0;
-        for (int i = 0; i < 8 && e0 + i < args.n; ++i) o[i] = (uint16_t)(pack_bf16x2(w[i], 0.0f) & 0xffffu);
+        uint16_t *o = reinterpret_cast<uint16_t *>(T.out) + e0;
+        for (int i = 0; i < 8 && e0 + i < T.n; ++i) o[i] = (uint16_t)(pack_bf16x2(w[i], 0.0f) & 0xffffu);
       } else {
-        float *o = reinterpret_cast<float *>(args.out) + e0;
-        for (int i = 0; i < 8 && e0 + i < args.n; ++i) o[i] = w[i];
+        float *o = reinterpret_cast<float *>(T.out) + e0;
+        for (int i = 0; i < 8 && e0 + i < T.n; ++i) o[i] = w[i];
       }
     }
   }
@@ -165,27 +195,39 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
 
 }  // namespace
 
-hipError_t launch_dequantize(const uint8_t *packed, int64_t n, int blocksize, int quant_type,
-                             const ScaleArgs &sc, bool out_bf16, void *out, hipStream_t stream) {
-  if (n == 0) return hipSuccess;
+int dequantize_max_group() { return kMaxDGroup; }
+
+hipError_t launch_dequantize(int count, const DequantDesc *ds, int quant_type, bool double_quant,
+                             bool out_bf16, hipStream_t stream) {
+  if (count > kMaxDGroup) return hipErrorInvalidValue;
   const CodeTables &t = code_tables(quant_type);
   DequantArgs args;
-  args.packed = packed;
-  args.out = out;
-  args.n = n;
-  args.sc = sc;
-  args.log2_bs = __builtin_ctz((unsigned)blocksize);
+  args.count = 0;
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    if (ds[i].n == 0) continue;
+    DTensor &T = args.t[args.count++];
+    T.packed = ds[i].packed;
+    T.out = ds[i].out;
+    T.n = ds[i].n;
+    T.sc = ds[i].sc;
+    T.log2_bs = __builtin_ctz((unsigned)ds[i].blocksize);
+    T.tile_begin = tiles;
+    tiles += T.n >> 10;
+  }
+  if (args.count == 0) return hipSuccess;
+  args.total_tiles = tiles;
   for (int i = 0; i < 16; ++i) args.value[i] = t.value[i];
-  // about two tiles of 1024 elements per wave, at most 16 workgroups per CU
-  int64_t blocks = ((n + 1023) / 1024 + 4 * 2 - 1) / (4 * 2);
+  // about two tiles of 1024 elements per wave (and a wave for each tensor's
+  // ragged tail), at most 16 workgroups per CU
+  int64_t blocks = (tiles + args.count + 4 * 2 - 1) / (4 * 2);
   if (blocks > 4096) blocks = 4096;
   dim3 grid((unsigned)blocks);
-  const bool dq = sc.double_quant != 0;
-  if (out_bf16 && dq)
+  if (out_bf16 && double_quant)
     hipLaunchKernelGGL((dequantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, args);
   else if (out_bf16)
     hipLaunchKernelGGL((dequantize_kernel<true, false>), grid, dim3(kThreads), 0, stream, args);
-  else if (dq)
+  else if (double_quant)
     hipLaunchKernelGGL((dequantize_kernel<false, true>), grid, dim3(kThreads), 0, stream, args);
   else
     hipLaunchKernelGGL((dequantize_kernel<false, false>), grid, dim3(kThreads), 0, stream, args);

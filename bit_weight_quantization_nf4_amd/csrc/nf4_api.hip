@@ -140,9 +140,12 @@ nf4_status nf4_codebook(int32_t quant_type, float values[16]) {
 
 nf4_status nf4_device_check(void) { return check_device(); }
 
-nf4_status nf4_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_t quant_type,
-                        int32_t double_quant, uint8_t *packed, float *absmax, int8_t *absmax_q,
-                        float *absmax_scale, void *stream) {
+namespace {
+
+// The per-tensor rules of nf4_quantize (no device work).
+nf4_status check_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_t quant_type,
+                          int32_t double_quant, const uint8_t *packed, const float *absmax,
+                          const int8_t *absmax_q, const float *absmax_scale) {
   if (n < 0) return NF4_ERR_INVALID_ARGUMENT;
   if (quant_type != NF4_QUANT_NF4 && quant_type != NF4_QUANT_FP4) return NF4_ERR_INVALID_ARGUMENT;
   if (!is_pow2_in(blocksize, 32, 4096)) return NF4_ERR_INVALID_ARGUMENT;
@@ -153,18 +156,61 @@ nf4_status nf4_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_
     return NF4_ERR_INVALID_ARGUMENT;
   if (!aligned16(w_bf16) || !aligned16(packed) || !aligned16(absmax)) return NF4_ERR_MISALIGNED;
   if (double_quant && (!aligned16(absmax_q) || !aligned16(absmax_scale))) return NF4_ERR_MISALIGNED;
-  if (n == 0) return NF4_OK;
+  return NF4_OK;
+}
+
+// One tensor through the launches that do not share a launch with others.
+nf4_status quantize_one(const QuantTensorDesc &d, int32_t blocksize, int32_t quant_type,
+                        int32_t double_quant, hipStream_t s) {
+  if (d.n == 0) return NF4_OK;
+  nf4_status st =
+      from_hip(launch_quantize(d.w, d.n, blocksize, quant_type, d.packed, d.absmax, s));
+  if (st != NF4_OK || !double_quant) return st;
+  const int64_t nb = (d.n + blocksize - 1) / blocksize;
+  return from_hip(launch_double_quant(d.absmax, nb, 256, d.absmax_q, d.absmax_scale, s));
+}
+
+}  // namespace
+
+nf4_status nf4_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_t quant_type,
+                        int32_t double_quant, uint8_t *packed, float *absmax, int8_t *absmax_q,
+                        float *absmax_scale, void *stream) {
+  return nf4_quantize_grouped(1, &w_bf16, &n, blocksize, quant_type, double_quant, &packed,
+                              &absmax, &absmax_q, &absmax_scale, stream);
+}
+
+nf4_status nf4_quantize_grouped(int32_t count, const void *const *w_bf16, const int64_t *n,
+                                int32_t blocksize, int32_t quant_type, int32_t double_quant,
+                                uint8_t *const *packed, float *const *absmax,
+                                int8_t *const *absmax_q, float *const *absmax_scale,
+                                void *stream) {
+  if (count < 0 || count > NF4_QUANT_MAX_GROUP) return NF4_ERR_INVALID_ARGUMENT;
+  if (count == 0) return NF4_OK;
+  if (w_bf16 == nullptr || n == nullptr || packed == nullptr || absmax == nullptr)
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (double_quant == 1 && (absmax_q == nullptr || absmax_scale == nullptr))
+    return NF4_ERR_INVALID_ARGUMENT;
+  QuantTensorDesc ds[NF4_QUANT_MAX_GROUP];
+  bool any = false;
+  for (int i = 0; i < count; ++i) {
+    int8_t *q = double_quant == 1 ? absmax_q[i] : nullptr;
+    float *s2 = double_quant == 1 ? absmax_scale[i] : nullptr;
+    nf4_status st = check_quantize(w_bf16[i], n[i], blocksize, quant_type, double_quant, packed[i],
+                                   absmax[i], q, s2);
+    if (st != NF4_OK) return st;
+    ds[i] = QuantTensorDesc{static_cast<const uint16_t *>(w_bf16[i]), n[i], packed[i], absmax[i],
+                            q, s2};
+    any = any || n[i] > 0;
+  }
+  if (!any) return NF4_OK;
   nf4_status st = check_device();
   if (st != NF4_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (double_quant && quantize_dq_fused(blocksize, 256))
-    return from_hip(launch_quantize_dq(static_cast<const uint16_t *>(w_bf16), n, blocksize,
-                                       quant_type, packed, absmax, absmax_q, absmax_scale, s));
-  st = from_hip(launch_quantize(static_cast<const uint16_t *>(w_bf16), n, blocksize, quant_type,
-                                packed, absmax, s));
-  if (st != NF4_OK || !double_quant) return st;
-  const int64_t nb = (n + blocksize - 1) / blocksize;
-  return from_hip(launch_double_quant(absmax, nb, 256, absmax_q, absmax_scale, s));
+    return from_hip(launch_quantize_dq(count, ds, blocksize, quant_type, s));
+  for (int i = 0; i < count && st == NF4_OK; ++i)
+    st = quantize_one(ds[i], blocksize, quant_type, double_quant, s);
+  return st;
 }
 
 nf4_status nf4_double_quant(const float *absmax, int64_t nb, int32_t blocksize2, int8_t *absmax_q,
@@ -183,17 +229,33 @@ nf4_status nf4_double_quant(const float *absmax, int64_t nb, int32_t blocksize2,
 }
 
 nf4_status nf4_dequantize(const nf4_qweight *w, int32_t out_dtype, void *out, void *stream) {
-  ScaleArgs sc;
-  nf4_status st = check_qweight(w, &sc);
-  if (st != NF4_OK) return st;
+  return nf4_dequantize_grouped(1, w, out_dtype, &out, stream);
+}
+
+nf4_status nf4_dequantize_grouped(int32_t count, const nf4_qweight *w, int32_t out_dtype,
+                                  void *const *out, void *stream) {
+  if (count < 0 || count > NF4_QUANT_MAX_GROUP) return NF4_ERR_INVALID_ARGUMENT;
+  if (count == 0) return NF4_OK;
+  if (w == nullptr || out == nullptr) return NF4_ERR_INVALID_ARGUMENT;
   if (out_dtype != NF4_DTYPE_BF16 && out_dtype != NF4_DTYPE_FP32) return NF4_ERR_INVALID_ARGUMENT;
-  if (w->n > 0 && out == nullptr) return NF4_ERR_INVALID_ARGUMENT;
-  if (!aligned16(out)) return NF4_ERR_MISALIGNED;
-  if (w->n == 0) return NF4_OK;
-  st = check_device();
+  DequantDesc ds[NF4_QUANT_MAX_GROUP];
+  bool any = false;
+  for (int i = 0; i < count; ++i) {
+    ScaleArgs sc;
+    nf4_status st = check_qweight(&w[i], &sc);
+    if (st != NF4_OK) return st;
+    if (w[i].n > 0 && out[i] == nullptr) return NF4_ERR_INVALID_ARGUMENT;
+    if (!aligned16(out[i])) return NF4_ERR_MISALIGNED;
+    if (w[i].quant_type != w[0].quant_type || w[i].double_quant != w[0].double_quant)
+      return NF4_ERR_UNSUPPORTED;
+    ds[i] = DequantDesc{w[i].packed, w[i].n, w[i].blocksize, sc, out[i]};
+    any = any || w[i].n > 0;
+  }
+  if (!any) return NF4_OK;
+  nf4_status st = check_device();
   if (st != NF4_OK) return st;
-  return from_hip(launch_dequantize(w->packed, w->n, w->blocksize, w->quant_type, sc,
-                                    out_dtype == NF4_DTYPE_BF16, out,
+  return from_hip(launch_dequantize(count, ds, w[0].quant_type, w[0].double_quant != 0,
+                                    out_dtype == NF4_DTYPE_BF16,
                                     reinterpret_cast<hipStream_t>(stream)));
 }
 

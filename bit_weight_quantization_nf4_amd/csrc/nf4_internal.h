@@ -15,16 +15,41 @@ hipError_t launch_quantize(const uint16_t *w, int64_t n, int blocksize, int quan
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int blocksize2, int8_t *q,
                                float *s2, hipStream_t stream);
 
-// Quantization and double quantization (groups of blocksize2 scales) in one
-// launch, for the pairs where quantize_dq_fused() is true; results equal
-// launch_quantize followed by launch_double_quant.
-bool quantize_dq_fused(int blocksize, int blocksize2);
-hipError_t launch_quantize_dq(const uint16_t *w, int64_t n, int blocksize, int quant_type,
-                              uint8_t *packed, float *absmax, int8_t *absmax_q,
-                              float *absmax_scale, hipStream_t stream);
+// One tensor of a quantization launch (absmax_q / absmax_scale used with
+// double quantization only).
+struct QuantTensorDesc {
+  const uint16_t *w;
+  int64_t n;
+  uint8_t *packed;
+  float *absmax;
+  int8_t *absmax_q;
+  float *absmax_scale;
+};
 
-hipError_t launch_dequantize(const uint8_t *packed, int64_t n, int blocksize, int quant_type,
-                             const ScaleArgs &sc, bool out_bf16, void *out, hipStream_t stream);
+// Quantization and double quantization (groups of blocksize2 scales) in one
+// launch, for the pairs where quantize_dq_fused() is true, over up to
+// quantize_max_group() tensors that share blocksize and quant type; each
+// tensor's results equal launch_quantize followed by launch_double_quant.
+bool quantize_dq_fused(int blocksize, int blocksize2);
+int quantize_max_group();
+hipError_t launch_quantize_dq(int count, const QuantTensorDesc *ts, int blocksize, int quant_type,
+                              hipStream_t stream);
+
+// One tensor of a dequantization launch.
+struct DequantDesc {
+  const uint8_t *packed;
+  int64_t n;
+  int blocksize;
+  ScaleArgs sc;
+  void *out;
+};
+
+// Dequantization of up to dequantize_max_group() tensors in one launch; they
+// share the quant type, the double-quant flag and the output dtype. Each
+// tensor's output equals what it gets launched alone.
+int dequantize_max_group();
+hipError_t launch_dequantize(int count, const DequantDesc *ds, int quant_type, bool double_quant,
+                             bool out_bf16, hipStream_t stream);
 
 // One decode product of a group launched together by launch_gemv_grouped.
 struct GemvDesc {

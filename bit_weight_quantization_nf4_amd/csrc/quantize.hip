@@ -42,12 +42,25 @@ namespace {
 
 constexpr int kThreads = 256;
 
-struct QuantArgs {
+// One tensor of a launch. group_begin: its first group of 256 blocks in the
+// launch's group numbering (fused double quantization).
+struct QTensor {
   const uint16_t *w;
   uint8_t *packed;
   float *absmax;
+  int8_t *absmax_q;
+  float *absmax_scale;
   int64_t n;
   int64_t nb;
+  int64_t group_begin;
+};
+
+constexpr int kMaxQGroup = 16;
+
+struct QuantArgs {
+  QTensor t[kMaxQGroup];  // the single-tensor kernels use t[0]
+  int32_t count;
+  int64_t total_groups;
   int64_t ntiles;
   float cell_thr[kCells];
   uint32_t cell_codes[kCells];
@@ -198,17 +211,17 @@ __device__ __forceinline__ uint32_t encode_lane(const uint32_t d[4], uint32_t m,
 // Packed codes of elements e0 .. e0 + 7; in a ragged tail the nibbles of
 // missing elements are cleared and only the bytes that exist (ceil(n/2) in
 // total) are written.
-__device__ __forceinline__ void store_codes(const QuantArgs &args, int64_t e0, uint32_t word) {
-  if (e0 + 8 <= args.n) {
-    *reinterpret_cast<uint32_t *>(args.packed + e0 / 2) = word;
-  } else if (e0 < args.n) {
-    const int64_t valid = args.n - e0;
+__device__ __forceinline__ void store_codes(const QTensor &T, int64_t e0, uint32_t word) {
+  if (e0 + 8 <= T.n) {
+    *reinterpret_cast<uint32_t *>(T.packed + e0 / 2) = word;
+  } else if (e0 < T.n) {
+    const int64_t valid = T.n - e0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       if (2 * b >= valid) break;
       uint32_t byte = (word >> (8 * b)) & 0xffu;
       if (2 * b + 1 >= valid) byte &= 0xf0u;
-      args.packed[e0 / 2 + b] = (uint8_t)byte;
+      T.packed[e0 / 2 + b] = (uint8_t)byte;
     }
   }
 }
@@ -216,13 +229,13 @@ __device__ __forceinline__ void store_codes(const QuantArgs &args, int64_t e0, u
 // The codes of one chunk: a whole chunk (the test is wave-uniform) stores
 // through the chunk's base address plus a lane offset; the ragged last chunk
 // goes element-wise.
-__device__ __forceinline__ void store_chunk(const QuantArgs &args, int64_t chunk, int lane,
+__device__ __forceinline__ void store_chunk(const QTensor &T, int64_t chunk, int lane,
                                             uint32_t word) {
-  if (chunk * 512 + 512 <= args.n) {
-    uint32_t *base = reinterpret_cast<uint32_t *>(args.packed + chunk * 256);
+  if (chunk * 512 + 512 <= T.n) {
+    uint32_t *base = reinterpret_cast<uint32_t *>(T.packed + chunk * 256);
     base[lane] = word;
   } else {
-    store_codes(args, chunk * 512 + 8 * lane, word);
+    store_codes(T, chunk * 512 + 8 * lane, word);
   }
 }
 
@@ -250,13 +263,13 @@ constexpr int kInFlight = 4;
 // Loads of chunk `chunk` through a buffer resource whose range is the chunk's
 // bytes rounded up to whole 16-byte granules: granules past the end (and
 // every granule of a chunk past the end) read as 0 without touching memory.
-__device__ __forceinline__ void load_chunk(uint32_t (&d)[4], const QuantArgs &args, int64_t chunk,
+__device__ __forceinline__ void load_chunk(uint32_t (&d)[4], const QTensor &T, int64_t chunk,
                                            int lane) {
   const int64_t c0 = chunk * 512;
-  const int64_t rem = args.n - c0;
+  const int64_t rem = T.n - c0;
   const int64_t valid = rem < 512 ? (rem > 0 ? rem : 0) : 512;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(args.w + (c0 < args.n ? c0 : 0)), (short)0,
+      (void *)(T.w + (c0 < T.n ? c0 : 0)), (short)0,
       (int)((2 * valid + 15) & ~(int64_t)15), 0x00020000);
   const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, 0, 0));
   d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
@@ -264,10 +277,10 @@ __device__ __forceinline__ void load_chunk(uint32_t (&d)[4], const QuantArgs &ar
 
 // Absmax bits (returned) and packed codes of one chunk.
 template <int BS, int QT>
-__device__ __forceinline__ uint32_t encode_chunk(uint32_t (&d)[4], const QuantArgs &args,
+__device__ __forceinline__ uint32_t encode_chunk(uint32_t (&d)[4], const QTensor &T,
                                                  int64_t chunk, int lane, const uint2 *lut,
                                                  const uint32_t *recip, uint32_t &word) {
-  if (chunk * 512 + 512 > args.n) clear_tail(d, chunk * 512 + 8 * lane, args.n);
+  if (chunk * 512 + 512 > T.n) clear_tail(d, chunk * 512 + 8 * lane, T.n);
   const uint32_t m = group_max<BS / 8>(absmax_bits16(d));
   word = encode_lane<QT>(d, m, lut, recip);
   return m;
@@ -286,7 +299,8 @@ __global__ __launch_bounds__(kThreads) void quantize_chunks_kernel(QuantArgs arg
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-  const int64_t nchunks = (args.n + 511) / 512;
+  const QTensor &T = args.t[0];
+  const int64_t nchunks = (T.n + 511) / 512;
   const int64_t nseq = wave < nchunks ? (nchunks - 1 - wave) / nwaves + 1 : 0;
 
   // Loads are issued unconditionally (a chunk past the end has an empty
@@ -294,7 +308,7 @@ __global__ __launch_bounds__(kThreads) void quantize_chunks_kernel(QuantArgs arg
   // each encode waits for its own chunk only.
   uint32_t d[kInFlight][4];
 #pragma unroll
-  for (int u = 0; u < kInFlight; ++u) load_chunk(d[u], args, wave + u * nwaves, lane);
+  for (int u = 0; u < kInFlight; ++u) load_chunk(d[u], T, wave + u * nwaves, lane);
   for (int64_t i0 = 0; i0 < nseq; i0 += kInFlight) {
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
@@ -302,11 +316,11 @@ __global__ __launch_bounds__(kThreads) void quantize_chunks_kernel(QuantArgs arg
       if (i >= nseq) break;
       const int64_t chunk = wave + i * nwaves;
       uint32_t word;
-      const uint32_t m = encode_chunk<BS, QT>(d[u], args, chunk, lane, lut, recip, word);
-      load_chunk(d[u], args, chunk + kInFlight * nwaves, lane);
-      store_chunk(args, chunk, lane, word);
+      const uint32_t m = encode_chunk<BS, QT>(d[u], T, chunk, lane, lut, recip, word);
+      load_chunk(d[u], T, chunk + kInFlight * nwaves, lane);
+      store_chunk(T, chunk, lane, word);
       const int64_t block = (chunk * 512 + 8 * lane) / BS;
-      if (lane % G == 0 && block < args.nb) args.absmax[block] = bf16_bits_to_f32(m);
+      if (lane % G == 0 && block < T.nb) T.absmax[block] = bf16_bits_to_f32(m);
     }
   }
 }
@@ -324,14 +338,14 @@ struct TileShape {
 // Loads of one tile, with the same range rule as load_chunk.
 template <int BS>
 __device__ __forceinline__ void load_tile(uint32_t (&d)[TileShape<BS>::CH][4],
-                                          const QuantArgs &args, int64_t tile, int lane) {
+                                          const QTensor &T, int64_t tile, int lane) {
   constexpr int CH = TileShape<BS>::CH, kTile = TileShape<BS>::kTile;
   const int64_t t0 = tile * kTile;
-  const int64_t rem = args.n - t0;
+  const int64_t rem = T.n - t0;
   const int64_t valid = rem < kTile ? (rem > 0 ? rem : 0) : kTile;
   const uint32_t bytes = (uint32_t)((2 * valid + 15) & ~(int64_t)15);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(args.w + (t0 < args.n ? t0 : 0)), (short)0, (int)bytes, 0x00020000);
+      (void *)(T.w + (t0 < T.n ? t0 : 0)), (short)0, (int)bytes, 0x00020000);
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const uint4 v = __builtin_bit_cast(
@@ -342,14 +356,14 @@ __device__ __forceinline__ void load_tile(uint32_t (&d)[TileShape<BS>::CH][4],
 
 template <int BS, int QT>
 __device__ __forceinline__ void encode_tile(uint32_t (&d)[TileShape<BS>::CH][4],
-                                            const QuantArgs &args, int64_t tile, int lane,
+                                            const QTensor &T, int64_t tile, int lane,
                                             const uint2 *lut, const uint32_t *recip) {
   constexpr int CH = TileShape<BS>::CH, kTile = TileShape<BS>::kTile;
   constexpr int CPB = BS / 512;  // chunks per block
   const int64_t t0 = tile * kTile;
-  if (t0 + kTile > args.n) {
+  if (t0 + kTile > T.n) {
 #pragma unroll
-    for (int c = 0; c < CH; ++c) clear_tail(d[c], t0 + 512 * c + 8 * lane, args.n);
+    for (int c = 0; c < CH; ++c) clear_tail(d[c], t0 + 512 * c + 8 * lane, T.n);
   }
 #pragma unroll
   for (int j = 0; j < CH / CPB; ++j) {
@@ -361,10 +375,10 @@ __device__ __forceinline__ void encode_tile(uint32_t (&d)[TileShape<BS>::CH][4],
     }
     m = group_max<64>(m);
     const int64_t block = t0 / BS + j;
-    if (lane == 0 && block < args.nb) args.absmax[block] = bf16_bits_to_f32(m);
+    if (lane == 0 && block < T.nb) T.absmax[block] = bf16_bits_to_f32(m);
 #pragma unroll
     for (int c = j * CPB; c < (j + 1) * CPB; ++c)
-      store_codes(args, t0 + 512 * c + 8 * lane, encode_lane<QT>(d[c], m, lut, recip));
+      store_codes(T, t0 + 512 * c + 8 * lane, encode_lane<QT>(d[c], m, lut, recip));
   }
 }
 
@@ -379,18 +393,19 @@ __global__ __launch_bounds__(kThreads) void quantize_tiles_kernel(QuantArgs args
   const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) +
                        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const QTensor &T = args.t[0];
 
   uint32_t da[CH][4], db[CH][4];
   int64_t tile = wave;
-  if (tile < args.ntiles) load_tile<BS>(da, args, tile, lane);
+  if (tile < args.ntiles) load_tile<BS>(da, T, tile, lane);
   for (; tile < args.ntiles; tile += 2 * nwaves) {
     const int64_t t1 = tile + nwaves;
-    load_tile<BS>(db, args, t1 < args.ntiles ? t1 : tile, lane);
-    encode_tile<BS, QT>(da, args, tile, lane, lut, recip);
+    load_tile<BS>(db, T, t1 < args.ntiles ? t1 : tile, lane);
+    encode_tile<BS, QT>(da, T, tile, lane, lut, recip);
     if (t1 >= args.ntiles) break;
     const int64_t t2 = t1 + nwaves;
-    load_tile<BS>(da, args, t2 < args.ntiles ? t2 : t1, lane);
-    encode_tile<BS, QT>(db, args, t1, lane, lut, recip);
+    load_tile<BS>(da, T, t2 < args.ntiles ? t2 : t1, lane);
+    encode_tile<BS, QT>(db, T, t1, lane, lut, recip);
   }
 }
 
@@ -421,9 +436,10 @@ struct DqShape {
   static constexpr int CPW = CPG / W;                  // chunks per wave
 };
 
-template <int BS, int QT, int W>
-__global__ __launch_bounds__(64 * W) void quantize_dq_kernel(QuantArgs args, int8_t *absmax_q,
-                                                            float *absmax_scale, int64_t ngroups) {
+// The launch may hold several tensors (one group numbering over all of
+// them); a group never spans two tensors.
+template <int BS, int QT, int W, bool MULTI>
+__global__ __launch_bounds__(64 * W) void quantize_dq_kernel(QuantArgs args) {
   constexpr int CPG = DqShape<BS, W>::CPG, CPW = DqShape<BS, W>::CPW;
   static_assert(BS <= 512 && CPW % kInFlight == 0, "whole windows per wave and group");
   constexpr int G = BS / 8;  // lanes per block
@@ -435,35 +451,67 @@ __global__ __launch_bounds__(64 * W) void quantize_dq_kernel(QuantArgs args, int
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
-  // i-th chunk of this wave: group blockIdx.x + (i / CPW) * gridDim.x, chunk
-  // wave * CPW + i % CPW of that group
+  const int64_t ngroups = args.total_groups;
+  // i-th chunk of this wave: group blockIdx.x + (i / CPW) * gridDim.x of the
+  // launch, chunk wave * CPW + i % CPW of that group
   const int64_t my_groups =
       blockIdx.x < ngroups ? (ngroups - 1 - blockIdx.x) / gridDim.x + 1 : 0;
   const int64_t nseq = my_groups * CPW;
-  auto chunk_of = [&](int64_t i) -> int64_t {
-    return ((int64_t)blockIdx.x + (i / CPW) * gridDim.x) * CPG + wave * CPW + i % CPW;
+  // tensor of launch group lg and the group's index within it (a group past
+  // the last one maps past the last tensor's end: its loads read nothing).
+  // The tensors' first groups are read once into scalar registers (unused
+  // entries hold INT64_MAX), so a lookup is a short compare chain.
+  // (a launch of one tensor skips all of this: its tensor is fixed, so its
+  // fields load once)
+  constexpr int kT = MULTI ? kMaxQGroup : 1;
+  int64_t gb[kT];
+#pragma unroll
+  for (int k = 0; k < kT; ++k) gb[k] = MULTI ? args.t[k].group_begin : 0;
+  auto locate = [&](int64_t lg, int &ti, int64_t &g) {
+    int t = 0;
+#pragma unroll
+    for (int k = 1; k < kT; ++k) t = gb[k] <= lg ? k : t;
+    ti = t;
+    g = lg - gb[t];
+  };
+  // window i0 (kInFlight chunks, never across two groups): its tensor and the
+  // group's first chunk of this wave
+  auto window = [&](int64_t i0, int &ti) -> int64_t {
+    int64_t g;
+    locate((int64_t)blockIdx.x + (i0 / CPW) * gridDim.x, ti, g);
+    return g * CPG + wave * CPW + i0 % CPW;
   };
 
   // loads are unconditional: past the last group a chunk has an empty range
   uint32_t d[kInFlight][4];
+  int tc;
+  int64_t cc = window(0, tc);
 #pragma unroll
-  for (int u = 0; u < kInFlight; ++u) load_chunk(d[u], args, chunk_of(u), lane);
+  for (int u = 0; u < kInFlight; ++u) load_chunk(d[u], args.t[tc], cc + u, lane);
   for (int64_t i0 = 0; i0 < nseq; i0 += kInFlight) {
     const int64_t it = i0 / CPW;
     float *sa = sabs[it & 1];
+    int tn;
+    const int64_t cn = window(i0 + kInFlight, tn);
+    const QTensor &T = args.t[tc];
+    const QTensor &Tn = args.t[tn];
 #pragma unroll
     for (int u = 0; u < kInFlight; ++u) {
-      const int64_t i = i0 + u;
-      const int64_t chunk = chunk_of(i);
+      const int64_t chunk = cc + u;
       uint32_t word;
-      const uint32_t m = encode_chunk<BS, QT>(d[u], args, chunk, lane, lut, recip, word);
-      load_chunk(d[u], args, chunk_of(i + kInFlight), lane);
-      store_chunk(args, chunk, lane, word);
-      if (lane % G == 0) sa[((wave * CPW + i % CPW) * 512 + 8 * lane) / BS] = bf16_bits_to_f32(m);
+      const uint32_t m = encode_chunk<BS, QT>(d[u], T, chunk, lane, lut, recip, word);
+      load_chunk(d[u], Tn, cn + u, lane);
+      store_chunk(T, chunk, lane, word);
+      if (lane % G == 0)
+        sa[((wave * CPW + (i0 + u) % CPW) * 512 + 8 * lane) / BS] = bf16_bits_to_f32(m);
     }
+    const int t_done = tc;
+    tc = tn;
+    cc = cn;
     if ((i0 + kInFlight) % CPW != 0) continue;
     // the group is complete: its scale maximum (blocks past n hold 0), taken by every wave
-    const int64_t group = (int64_t)blockIdx.x + it * gridDim.x;
+    const QTensor &Td = args.t[t_done];
+    const int64_t group = (int64_t)blockIdx.x + it * gridDim.x - gb[t_done];
     __syncthreads();
     float mx = 0.0f;
 #pragma unroll
@@ -471,24 +519,27 @@ __global__ __launch_bounds__(64 * W) void quantize_dq_kernel(QuantArgs args, int
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
     const float s2 = (mx == 0.0f) ? 0.0f : mx / 127.0f;
-    if (threadIdx.x == 0) absmax_scale[group] = s2;
+    if (threadIdx.x == 0) Td.absmax_scale[group] = s2;
 #pragma unroll
     for (int i = threadIdx.x; i < kGroupBlocks; i += 64 * W) {
       const int64_t block = group * kGroupBlocks + i;
-      if (block < args.nb) {
+      if (block < Td.nb) {
         const float a = sa[i];
-        args.absmax[block] = a;
-        absmax_q[block] = dq_code(a, s2);
+        Td.absmax[block] = a;
+        Td.absmax_q[block] = dq_code(a, s2);
       }
     }
   }
 }
 
 template <int BS, int QT, int W>
-void launch_qdq_w(int64_t groups, QuantArgs args, int8_t *absmax_q, float *absmax_scale,
-                  int64_t ngroups, hipStream_t stream) {
-  hipLaunchKernelGGL((quantize_dq_kernel<BS, QT, W>), dim3((unsigned)groups), dim3(64 * W), 0,
-                     stream, args, absmax_q, absmax_scale, ngroups);
+void launch_qdq_w(int64_t groups, const QuantArgs &args, hipStream_t stream) {
+  if (args.count > 1)
+    hipLaunchKernelGGL((quantize_dq_kernel<BS, QT, W, true>), dim3((unsigned)groups), dim3(64 * W),
+                       0, stream, args);
+  else
+    hipLaunchKernelGGL((quantize_dq_kernel<BS, QT, W, false>), dim3((unsigned)groups),
+                       dim3(64 * W), 0, stream, args);
 }
 
 // Waves per group: the fewest of 4, 8, 16 that give the launch at least
@@ -497,25 +548,23 @@ void launch_qdq_w(int64_t groups, QuantArgs args, int8_t *absmax_q, float *absma
 constexpr int64_t kWantWaves = 256 * 4 * 8;
 
 template <int BS, int QT>
-void launch_qdq_bs(int64_t blocks, QuantArgs args, int8_t *absmax_q, float *absmax_scale,
-                   int64_t ngroups, hipStream_t stream) {
+void launch_qdq_bs(int64_t blocks, const QuantArgs &args, hipStream_t stream) {
   constexpr int kMaxW = DqShape<BS, 1>::CPG / kInFlight >= 16 ? 16 : DqShape<BS, 1>::CPG / kInFlight;
+  const int64_t ngroups = args.total_groups;
   if (ngroups * 4 >= kWantWaves || kMaxW < 8)
-    launch_qdq_w<BS, QT, 4>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
+    launch_qdq_w<BS, QT, 4>(blocks, args, stream);
   else if (ngroups * 8 >= kWantWaves || kMaxW < 16)
-    launch_qdq_w<BS, QT, (kMaxW < 8 ? 4 : 8)>(blocks, args, absmax_q, absmax_scale, ngroups, stream);
+    launch_qdq_w<BS, QT, (kMaxW < 8 ? 4 : 8)>(blocks, args, stream);
   else
-    launch_qdq_w<BS, QT, (kMaxW < 8 ? 4 : (kMaxW < 16 ? 8 : 16))>(blocks, args, absmax_q, absmax_scale, ngroups,
-                                                  stream);
+    launch_qdq_w<BS, QT, (kMaxW < 8 ? 4 : (kMaxW < 16 ? 8 : 16))>(blocks, args, stream);
 }
 
 template <int QT>
-hipError_t launch_qdq(int blocksize, int64_t blocks, QuantArgs args, int8_t *absmax_q,
-                      float *absmax_scale, int64_t ngroups, hipStream_t stream) {
+hipError_t launch_qdq(int blocksize, int64_t blocks, const QuantArgs &args, hipStream_t stream) {
   switch (blocksize) {
-    case 64: launch_qdq_bs<64, QT>(blocks, args, absmax_q, absmax_scale, ngroups, stream); break;
-    case 128: launch_qdq_bs<128, QT>(blocks, args, absmax_q, absmax_scale, ngroups, stream); break;
-    case 256: launch_qdq_bs<256, QT>(blocks, args, absmax_q, absmax_scale, ngroups, stream); break;
+    case 64: launch_qdq_bs<64, QT>(blocks, args, stream); break;
+    case 128: launch_qdq_bs<128, QT>(blocks, args, stream); break;
+    case 256: launch_qdq_bs<256, QT>(blocks, args, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -548,17 +597,31 @@ hipError_t launch_qt(int blocksize, dim3 grid, QuantArgs args, hipStream_t strea
   return hipGetLastError();
 }
 
-QuantArgs make_args(const uint16_t *w, int64_t n, int blocksize, int quant_type, uint8_t *packed,
-                    float *absmax) {
+// Arguments of a launch over `count` tensors that share blocksize and quant type.
+QuantArgs make_args(int count, const QuantTensorDesc *ts, int blocksize, int quant_type) {
   const CodeTables &t = code_tables(quant_type);
   QuantArgs args;
-  args.w = w;
-  args.packed = packed;
-  args.absmax = absmax;
-  args.n = n;
-  args.nb = (n + blocksize - 1) / blocksize;
+  args.count = count;
+  int64_t groups = 0;
+  for (int i = 0; i < count; ++i) {
+    QTensor &T = args.t[i];
+    T.w = ts[i].w;
+    T.packed = ts[i].packed;
+    T.absmax = ts[i].absmax;
+    T.absmax_q = ts[i].absmax_q;
+    T.absmax_scale = ts[i].absmax_scale;
+    T.n = ts[i].n;
+    T.nb = (T.n + blocksize - 1) / blocksize;
+    T.group_begin = groups;
+    groups += (T.nb + kGroupBlocks - 1) / kGroupBlocks;
+  }
+  args.total_groups = groups;
+  for (int i = count; i < kMaxQGroup; ++i) {
+    args.t[i] = args.t[0];
+    args.t[i].group_begin = INT64_MAX;  // never found by a group lookup
+  }
   const int64_t tile_elems = blocksize > 512 ? blocksize : 512;
-  args.ntiles = (n + tile_elems - 1) / tile_elems;
+  args.ntiles = count > 0 ? (args.t[0].n + tile_elems - 1) / tile_elems : 0;
   for (int i = 0; i < kCells; ++i) {
     args.cell_thr[i] = t.cell_thr[i];
     args.cell_codes[i] = t.cell_codes[i];
@@ -580,25 +643,30 @@ bool quantize_dq_fused(int blocksize, int blocksize2) {
   return blocksize2 == 256 && (blocksize == 64 || blocksize == 128 || blocksize == 256);
 }
 
-hipError_t launch_quantize_dq(const uint16_t *w, int64_t n, int blocksize, int quant_type,
-                              uint8_t *packed, float *absmax, int8_t *absmax_q,
-                              float *absmax_scale, hipStream_t stream) {
-  if (!quantize_dq_fused(blocksize, 256)) return hipErrorInvalidValue;
-  if (n == 0) return hipSuccess;
-  const QuantArgs args = make_args(w, n, blocksize, quant_type, packed, absmax);
+int quantize_max_group() { return kMaxQGroup; }
+
+hipError_t launch_quantize_dq(int count, const QuantTensorDesc *ts, int blocksize,
+                              int quant_type, hipStream_t stream) {
+  if (!quantize_dq_fused(blocksize, 256) || count > kMaxQGroup) return hipErrorInvalidValue;
+  QuantTensorDesc live[kMaxQGroup];
+  int nl = 0;
+  for (int i = 0; i < count; ++i)
+    if (ts[i].n > 0) live[nl++] = ts[i];
+  if (nl == 0) return hipSuccess;
+  const QuantArgs args = make_args(nl, live, blocksize, quant_type);
   // a workgroup per group of 256 blocks, at most kMaxDqGroups of them; each
   // then loops over every kMaxDqGroups-th group
-  const int64_t ngroups = (args.nb + 255) / 256;
+  const int64_t ngroups = args.total_groups;
   const int64_t blocks = ngroups < kMaxDqGroups ? ngroups : kMaxDqGroups;
-  return quant_type == kQuantFP4
-             ? launch_qdq<kQuantFP4>(blocksize, blocks, args, absmax_q, absmax_scale, ngroups, stream)
-             : launch_qdq<kQuantNF4>(blocksize, blocks, args, absmax_q, absmax_scale, ngroups, stream);
+  return quant_type == kQuantFP4 ? launch_qdq<kQuantFP4>(blocksize, blocks, args, stream)
+                                 : launch_qdq<kQuantNF4>(blocksize, blocks, args, stream);
 }
 
 hipError_t launch_quantize(const uint16_t *w, int64_t n, int blocksize, int quant_type,
                            uint8_t *packed, float *absmax, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  const QuantArgs args = make_args(w, n, blocksize, quant_type, packed, absmax);
+  const QuantTensorDesc one{w, n, packed, absmax, nullptr, nullptr};
+  const QuantArgs args = make_args(1, &one, blocksize, quant_type);
   // Enough waves to keep every CU's memory pipeline busy (about four chunks
   // or one tile per wave); each wave then strides over the rest.
   const int64_t waves_wanted = blocksize <= 512 ? (args.ntiles + 3) / 4 : args.ntiles;

@@ -141,6 +141,36 @@ nf4_status nf4_double_quant(const float *absmax, int64_t nb, int32_t blocksize2,
  * quant. */
 nf4_status nf4_dequantize(const nf4_qweight *w, int32_t out_dtype, void *out, void *stream);
 
+/* Largest `count` accepted by nf4_quantize_grouped and nf4_dequantize_grouped. */
+#define NF4_QUANT_MAX_GROUP 16
+
+/* Quantization of several tensors in one call -- e.g. the weights of one
+ * transformer layer [NF4 page, table 数学原理对比; repo page 0.49.2]: for
+ * i < count, exactly nf4_quantize(w_bf16[i], n[i], blocksize, quant_type,
+ * double_quant, packed[i], absmax[i], absmax_q[i], absmax_scale[i]), with the
+ * same argument rules per tensor. w_bf16, n, packed, absmax, absmax_q and
+ * absmax_scale are HOST arrays of `count` entries (the buffers they point to are
+ * on the device); absmax_q and absmax_scale may be NULL when double_quant == 0.
+ * With double quantization at blocksize 64, 128 or 256 the tensors share one
+ * launch, so small tensors do not each pay a launch's start-up and tail;
+ * otherwise they are launched one after another. Every output is bitwise what
+ * nf4_quantize writes for that tensor alone. 0 <= count <= NF4_QUANT_MAX_GROUP. */
+nf4_status nf4_quantize_grouped(int32_t count, const void *const *w_bf16, const int64_t *n,
+                                int32_t blocksize, int32_t quant_type, int32_t double_quant,
+                                uint8_t *const *packed, float *const *absmax,
+                                int8_t *const *absmax_q, float *const *absmax_scale,
+                                void *stream);
+
+/* Dequantization of several tensors in one launch [usage page, Configuration:
+ * compute dtype]: for i < count, exactly nf4_dequantize(&w[i], out_dtype,
+ * out[i]). w and out are HOST arrays of `count` entries; all tensors share the
+ * quant type and the double-quant flag (NF4_ERR_UNSUPPORTED otherwise);
+ * sizes and blocksizes may differ. Every output is bitwise what
+ * nf4_dequantize writes for that tensor alone.
+ * 0 <= count <= NF4_QUANT_MAX_GROUP. */
+nf4_status nf4_dequantize_grouped(int32_t count, const nf4_qweight *w, int32_t out_dtype,
+                                  void *const *out, void *stream);
+
 /* Decode product for small batches [repo page 0.50.0: 4-bit GEMV and fused
  * 4-bit dequantize + GEMM for batch 1..64]:
  *   y[m, j] = sum_k bf16(dequant(W)[j, k]) * x[m, k],  fp32 accumulation,

@@ -173,6 +173,59 @@ def test_quantize_with_double_quant_groups(nf4, orc, bs):
             check_dequant(nf4, orc, qs, ref, bs, "nf4", True)
 
 
+@pytest.mark.parametrize("bs,dq,qt", [(64, True, "nf4"), (128, True, "fp4"), (256, True, "nf4"),
+                                      (64, False, "nf4"), (32, True, "nf4"), (1024, True, "fp4")])
+def test_quantize_grouped_matches_single(nf4, bs, dq, qt):
+    """nf4_quantize_grouped writes, for every tensor, exactly what nf4_quantize
+    writes for it alone: layer-sized tensors, a ragged tensor, an empty one,
+    a single element."""
+    sizes = [4096 * 4096, 0, 1000 * 512 + 37, 1, 11008 * 4096, 33 * 160]
+    ws = [workloads.normal_bf16((n,), 0.02, 900 + i) for i, n in enumerate(sizes)]
+    gpu = [dev(w) for w in ws]
+    grouped = nf4.quantize_grouped(gpu, bs, qt, dq)
+    for w, g in zip(gpu, grouped):
+        single = nf4.quantize(w, bs, qt, double_quant=dq)
+        keys = ("packed", "absmax", "absmax_q", "absmax_scale") if dq else ("packed", "absmax")
+        for k in keys:
+            a, b = getattr(g, k), getattr(single, k)
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (w.numel(), k)
+
+
+def test_quantize_grouped_more_groups_than_workgroups(nf4):
+    """A fused grouped launch whose groups of 256 blocks outnumber the
+    launch's workgroup cap (16384): workgroups then walk several groups, of
+    several tensors. Every tensor's output is bitwise its single-call one."""
+    g = torch.Generator(device="cuda").manual_seed(5)
+    n = 4096 * 4096 + 64 * 256  # 1025 groups at blocksize 64
+    ws = [(torch.randn(n, device="cuda", generator=g) * 0.02).to(torch.bfloat16) for _ in range(16)]
+    grouped = nf4.quantize_grouped(ws, 64, "nf4", True)
+    for w, q in zip(ws, grouped):
+        single = nf4.quantize(w, 64, "nf4", double_quant=True)
+        for k in ("packed", "absmax", "absmax_q", "absmax_scale"):
+            assert torch.equal(getattr(q, k).view(torch.uint8), getattr(single, k).view(torch.uint8)), k
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_dequantize_grouped_matches_single(nf4, orc, dq):
+    """nf4_dequantize_grouped: every output bitwise equal to nf4_dequantize of
+    the tensor alone, for tensors of mixed blocksizes and sizes (whole tiles,
+    a ragged tail, an empty tensor, tails only), fp32 and bf16 outputs; one
+    small tensor is also checked against the oracle."""
+    specs = [(4096 * 4096, 64), (0, 64), (1000 * 512 + 37, 128), (77, 32), (11008 * 4096, 64),
+             (2048 + 513, 256)]
+    qss = [nf4.quantize(dev(workloads.normal_bf16((n,), 0.02, 950 + i)), bs, "nf4",
+                        double_quant=dq) for i, (n, bs) in enumerate(specs)]
+    for dtype in (torch.bfloat16, torch.float32):
+        ys = nf4.dequantize_grouped(qss, dtype)
+        for qs, y in zip(qss, ys):
+            assert torch.equal(y, nf4.dequantize(qs, dtype)), (qs.shape, dtype)
+    w = workloads.normal_bf16((1000 * 512 + 37,), 0.02, 952)
+    qs, ref = check_quant(nf4, orc, w, 128, "nf4", dq)
+    _, w16_ref = orc.dequantize(ref["packed"], qs.n, 128, "nf4", **oracle_scales(ref, dq))
+    y = nf4.dequantize_grouped([qss[0], qs], torch.bfloat16)[1]
+    assert np.array_equal(to_u16(y.reshape(-1).cpu()), w16_ref)
+
+
 def test_quantize_empty(nf4):
     qs = nf4.quantize(torch.empty(0, dtype=torch.bfloat16, device="cuda"), 64, "nf4", True)
     assert qs.packed.numel() == 0 and qs.absmax.numel() == 0
