@@ -150,6 +150,7 @@ void gemv1_kernel(Gemv1Args args) {
   // piece read (same q) and the 16 threads of a store (8 q's, 2 l's) each
   // cover all 16 bank groups, so neither conflicts
   __shared__ uint4 xs[J * 512];
+  __shared__ f32x4 vs[4];  // the 16 code values, for the table build
 
   const int lane = threadIdx.x & 63;
   const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
@@ -174,6 +175,11 @@ void gemv1_kernel(Gemv1Args args) {
   for (int i = 0; i < 16; ++i) val[i] = args.value[i];
   // keep these loads in the first batch, ahead of the wave's vector loads
   __builtin_amdgcn_sched_barrier(0);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vs[i] = f32x4{val[4 * i], val[4 * i + 1], val[4 * i + 2], val[4 * i + 3]};
+  }
   int pi = -1, g = 0, ng = 1, nrows = 0;
 #pragma unroll
   for (int i = 0; i < kMaxGroup; ++i) {
@@ -349,18 +355,17 @@ void gemv1_kernel(Gemv1Args args) {
     // Pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy,
     // built while the first loads are in flight, two copies per 16-byte
     // store; consecutive threads write consecutive copies (no bank
-    // conflicts). The 64 stores of a wave cover entries base .. base + 3, so
-    // value[e >> 4] is one scalar and value[e & 15] one of four.
+    // conflicts). Both values are read from the 16 staged in LDS: indexing
+    // the kernel-argument copy with a lane-dependent index would make the
+    // compiler move all 16 into vector registers for every store.
+    __syncthreads();  // code values staged
+    const float *vsf = reinterpret_cast<const float *>(vs);
 #pragma unroll
     for (int k = 0; k < 256 * kCopies / 2 / kThreads; ++k) {
       const int base = (k * kThreads + 64 * wave_in_block) / (kCopies / 2);
-      const int q = lane / (kCopies / 2);
-      const float hi = val[base >> 4];
-      const float l0 = val[base & 15], l1 = val[(base & 15) + 1];
-      const float l2 = val[(base & 15) + 2], l3 = val[(base & 15) + 3];
-      const float lo = q == 0 ? l0 : (q == 1 ? l1 : (q == 2 ? l2 : l3));
-      const f32x4 v = {hi, lo, hi, lo};
-      *reinterpret_cast<f32x4 *>(tbl + 256 * (base + q) + 16 * (lane % (kCopies / 2))) = v;
+      const int e = base + lane / (kCopies / 2);
+      const f32x4 v = {vsf[e >> 4], vsf[e & 15], vsf[e >> 4], vsf[e & 15]};
+      *reinterpret_cast<f32x4 *>(tbl + 256 * e + 16 * (lane % (kCopies / 2))) = v;
     }
     // piece t of a slice belongs to lane t / 8, as its piece t % 8
 #pragma unroll
