@@ -57,8 +57,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # for the kernel source it was taken on (its SHA-256); after any change to that
 # source the benchmark reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "gemv1.hip": ("daedb838ffa9d27f523da21c50ed7e277cea3f2985ecd3b6f0186ef123b797cc", 105787460),
-    "gemm.hip": ("656b93bf13dfda4fc1f6125c152f6d726d1803cdfaeb797536cdf5114cfd0bed", 334965651),
+    "gemv1.hip": ("857aeecec15fcdf5988a2a63637c38cec0d9670e046884201656dd46c5c3158d", 105769158),
+    "gemm.hip": ("656b93bf13dfda4fc1f6125c152f6d726d1803cdfaeb797536cdf5114cfd0bed", 334977641),
 }
 
 
