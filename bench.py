@@ -33,8 +33,10 @@ against HBM with its average launch duration over the timed region (the phase
 time over its launches, so the short gap between two launches is counted in).
 The GEMM's TFLOP/s and each phase's own figures are reported next to it,
 with roofline fractions against MI355X peaks (HBM 8 TB/s, dense bf16 MFMA
-2.5 PFLOP/s). `cpu_baseline` times the CPU oracle on a bounded sample of the
-same workload (test infrastructure, single thread).
+2.5 PFLOP/s). `cpu_baseline` times the CPU oracle's decode GEMV on a bounded
+sample of the same workload (test infrastructure, single thread);
+`cpu_baselines` does the same for its quantize + double quant, dequantize and
+prefill GEMM.
 """
 from __future__ import annotations
 
@@ -427,6 +429,7 @@ def main():
 
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(mats, bs, args.cpu_seconds)
+        result["cpu_baselines"] = cpu_baselines(mats, pw, px, bs, args.cpu_seconds / 2)
     print(json.dumps(result), flush=True)
 
 
@@ -440,7 +443,7 @@ def cpu_baseline(mats, bs, target_s):
     import oracle
     import workloads
 
-    oracle.build(force=False)
+    oracle.ensure_built(force=False)
     done_bytes, done_s, count, worst = 0, 0.0, 0, 0.0
     for d in mats:
         N, K = d["spec"].rows, d["spec"].cols
@@ -464,6 +467,68 @@ def cpu_baseline(mats, bs, target_s):
                   f"stack ({done_bytes / 1e6:.1f} MB algorithmic), {done_s:.1f} s single-threaded; "
                   f"GPU y vs oracle y rel-L2 max {worst:.2e}",
     }
+
+
+def cpu_baselines(mats, pw, px, bs, target_s):
+    """The CPU oracle on bounded samples of the other paths, single-threaded, each
+    for about target_s seconds: quantize + double quant and dequantize (bf16
+    out) over the stack's first matrices, and the prefill GEMM on its first rows
+    (the oracle's GEMM is its dequantize of W, timed apart, then an fp64 product
+    of those rows)."""
+    import oracle
+    import workloads
+
+    oracle.ensure_built(force=False)
+    out = {}
+    q_bytes = q_s = d_bytes = d_s = 0.0
+    qcount = dcount = 0
+    for d in mats:
+        n = d["spec"].rows * d["spec"].cols
+        nb = -(-n // bs)
+        nb2 = -(-nb // 256)
+        w16 = workloads.to_u16(d["w"].cpu().reshape(-1))
+        t = time.perf_counter()
+        p, a = oracle.quantize(w16, bs, "nf4")
+        q, s2 = oracle.double_quant(a, 256)
+        q_s += time.perf_counter() - t
+        q_bytes += 2 * n + (n + 1) // 2 + 4 * nb + nb + 4 * nb2
+        qcount += 1
+        if d_s < target_s:
+            t = time.perf_counter()
+            oracle.dequantize(p, n, bs, "nf4", absmax_q=q, absmax_scale=s2)
+            d_s += time.perf_counter() - t
+            d_bytes += (n + 1) // 2 + nb + 4 * nb2 + 2 * n
+            dcount += 1
+        if q_s >= target_s and d_s >= target_s:
+            break
+    out["quantize"] = {
+        "value": round(q_bytes / q_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"oracle quantize + double quant (NF4 bs {bs}) of the stack's first {qcount} matrices, "
+                  f"{q_bytes / 1e6:.0f} MB algorithmic in {q_s:.1f} s"}
+    out["dequantize"] = {
+        "value": round(d_bytes / d_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"oracle dequantize to bf16 of the stack's first {dcount} matrices, "
+                  f"{d_bytes / 1e6:.0f} MB algorithmic in {d_s:.1f} s"}
+    N, K = pw.shape
+    w16 = workloads.to_u16(pw.cpu().reshape(-1))
+    p, a = oracle.quantize(w16, 64, "nf4")
+    q, s2 = oracle.double_quant(a, 256)
+    t = time.perf_counter()
+    _, wc = oracle.dequantize(p, N * K, 64, "nf4", absmax_q=q, absmax_scale=s2)
+    deq_s = time.perf_counter() - t
+    wc = wc.reshape(N, K)
+    x16 = workloads.to_u16(px.cpu())
+    rows, g_s = 0, 0.0
+    while g_s < target_s and rows < x16.shape[0]:
+        t = time.perf_counter()
+        oracle.matmul_bf16(x16[rows:rows + 1], wc)
+        g_s += time.perf_counter() - t
+        rows += 1
+    out["gemm"] = {
+        "value": round(2.0 * rows * N * K / g_s / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        "sample": f"oracle prefill GEMM (fp64 sums): the first {rows} rows of X [{x16.shape[0]}, {K}] times "
+                  f"W [{N}, {K}] in {g_s:.1f} s, after its dequantize of W ({deq_s:.1f} s, not counted)"}
+    return out
 
 
 if __name__ == "__main__":

@@ -25,9 +25,11 @@ QUANT_TYPES = {"nf4": NF4, "fp4": FP4}
 _lib = None
 
 
-def build(force: bool = True) -> str:
+def ensure_built(force: bool = True) -> str:
     """Compile nf4_oracle.c with gcc into libnf4_oracle.so (IEEE binary32, no
-    contraction, no fast-math)."""
+    contraction, no fast-math); with force=False only when the library is
+    missing or older than the source. (Not named `build`: importing the
+    submodule oracle.build would replace that attribute of the package.)"""
     from oracle.build import build_oracle
 
     return build_oracle(force=force)

@@ -16,5 +16,5 @@ def pytest_configure(config):
 def orc():
     import oracle
 
-    oracle.build(force=False)
+    oracle.ensure_built(force=False)
     return oracle

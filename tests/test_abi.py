@@ -168,3 +168,13 @@ def test_no_device_is_reported(nf4):
     assert L.nf4_quantize(A, 128, 64, 0, 0, A, B, None, None, None) == DEVICE
     d = _desc(nf4, n=64 * 128)
     assert L.nf4_gemv(A, 1, ctypes.byref(d), 64, 128, 0, 1, B, None) == DEVICE
+
+
+def test_oracle_build_callable_after_submodule_import():
+    # importing the build submodule must not shadow the package's build call
+    # (build() and smoke() may run in one process)
+    import oracle
+    import oracle.build  # noqa: F401
+
+    assert oracle.ensure_built(force=False).endswith("libnf4_oracle.so")
+    assert oracle.ensure_built(force=False).endswith("libnf4_oracle.so")
