@@ -204,8 +204,10 @@ void gemv1_kernel(Gemv1Args args) {
     const uint32_t g1 = split((uint32_t)nrows, (uint32_t)g + 1, (uint32_t)ng);
     const uint32_t w0 = g0 + split(g1 - g0, (uint32_t)wave_in_block, kWaves);
     const uint32_t w1 = g0 + split(g1 - g0, (uint32_t)wave_in_block + 1, kWaves);
-    const int64_t first = w0, stride = 1;
-    int64_t cnt = (int64_t)w1 - (int64_t)w0;
+    // row counters in 32 bits (a problem has fewer than 2^31 rows): their
+    // compares stay scalar
+    const int32_t first = (int32_t)w0;
+    int32_t cnt = (int32_t)(w1 - w0);
     if (!has_problem) cnt = 0;
     const bool active = cnt > 0;
     const uint16_t *x = args.p[pi].x;
@@ -346,8 +348,8 @@ void gemv1_kernel(Gemv1Args args) {
     // (clamped to the last row), so the wait before a row counts only that
     // row's own loads.
     // (a wave without rows prefetches a valid row, first, and computes none)
-    const int64_t last = cnt > 0 ? cnt - 1 : 0;
-    auto row_at = [&](int64_t i) { return first + (i < last ? i : last) * stride; };
+    const int32_t last = cnt > 0 ? cnt - 1 : 0;
+    auto row_at = [&](int32_t i) { return (int64_t)(first + (i < last ? i : last)); };
     RowLoads<J, BS32> buf[NBUF];
 #pragma unroll
     for (int b = 0; b + 1 < NBUF; ++b) buf[b] = load_row(row_at(b));
@@ -390,8 +392,8 @@ void gemv1_kernel(Gemv1Args args) {
     // after another and the last runs alone, waiting on memory; with waves
     // that are behind going first they finish together (and late starters
     // catch up).
-    const int64_t q1 = cnt / 4, q2 = cnt / 2, q3 = (3 * cnt) / 4;
-    for (int64_t i = 0; i < cnt; i += NBUF) {
+    const int32_t q1 = cnt / 4, q2 = cnt / 2, q3 = (3 * cnt) / 4;
+    for (int32_t i = 0; i < cnt; i += NBUF) {
       if (i < q1) __builtin_amdgcn_s_setprio(3);
       else if (i < q2) __builtin_amdgcn_s_setprio(2);
       else if (i < q3) __builtin_amdgcn_s_setprio(1);
