@@ -74,7 +74,7 @@ struct Gemv1Args {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Sum over the 64 lanes in a fixed order; the total lands in lane 63.
+// Sum over the 64 lanes in a fixed order; the total lands in lanes 48..63.
 __device__ __forceinline__ float wave_sum(float v) {
   // within quads, then 8- and 16-lane rows (xor-style partners via DPP)
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
@@ -85,11 +85,13 @@ __device__ __forceinline__ float wave_sum(float v) {
                                                             0x141, 0xf, 0xf, false));  // row_half_mirror
   v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
                                                             0x140, 0xf, 0xf, false));  // row_mirror
-  // every lane of a 16-lane row now holds that row's sum; fold the 4 rows
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                            0x142, 0xa, 0xf, false));  // row_bcast:15
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                            0x143, 0xc, 0xf, false));  // row_bcast:31
+  // every lane of a 16-lane row now holds that row's sum r0..r3; a 16-lane
+  // swap gives rows 1 and 3 the sums of rows 0 and 2, a 32-lane swap gives
+  // lanes 32..63 those of lanes 0..31: lanes 48..63 end with (r3 + r2) + (r1 + r0)
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  v += __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_permlane16_swap(u, u, false, false)[0]);
+  const uint32_t t = __builtin_bit_cast(uint32_t, v);
+  v += __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_permlane32_swap(t, t, false, false)[0]);
   return v;
 }
 
