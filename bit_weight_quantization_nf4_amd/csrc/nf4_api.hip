@@ -113,7 +113,7 @@ const char *nf4_status_string(int32_t status) {
     case NF4_ERR_INVALID_ARGUMENT:
       return "NF4_ERR_INVALID_ARGUMENT: null pointer, negative size, unknown enum or shape mismatch";
     case NF4_ERR_UNSUPPORTED:
-      return "NF4_ERR_UNSUPPORTED: request not implemented by this build, or device is not gfx950";
+      return "NF4_ERR_UNSUPPORTED: request this library does not implement, or device is not gfx950";
     case NF4_ERR_MISALIGNED:
       return "NF4_ERR_MISALIGNED: a device pointer is not 16-byte aligned";
     case NF4_ERR_DEVICE:

@@ -64,7 +64,7 @@ extern "C" {
 typedef enum nf4_status {
   NF4_OK = 0,
   NF4_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative size, bad enum, shape mismatch */
-  NF4_ERR_UNSUPPORTED = 2,      /* valid request this build does not implement, or not gfx950 */
+  NF4_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement, or not gfx950 */
   NF4_ERR_MISALIGNED = 3,       /* a device pointer is not 16-byte aligned */
   NF4_ERR_DEVICE = 4            /* no HIP device, or a HIP call / launch failed */
 } nf4_status;
