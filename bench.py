@@ -85,10 +85,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--phases", default="quantize,quantize_grouped,dequantize,dequantize_grouped,"
-                                        "gemv,gemv_single,gemm,sweep,mlp",
+                                        "gemv,gemv_single,linear_bias,gemm,gemm_bias,sweep,mlp",
                     help="comma list of quantize, quantize_grouped, dequantize, dequantize_grouped "
                          "(per matrix / the seven weights of a layer per call), gemv (grouped per "
-                         "layer), gemv_single (one launch per matrix), gemm (the stack at --bs), "
+                         "layer), gemv_single (one launch per matrix), linear_bias (the same "
+                         "through nf4_linear with a bf16 bias), gemm, gemm_bias (the prefill "
+                         "GEMM without / with a fused bias), "
                          "sweep (quantize, dequantize and gemv at the other blocksizes of "
                          "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16); "
                          "'copy' adds a plain 1 GiB device copy, the known-size reference "
@@ -210,6 +212,18 @@ def main():
         for q, y in zip(gemm_w, gemm_y):
             nf4.gemm(px, q, out=y)
 
+    # the same products through nf4_linear with a bf16 bias per output row
+    lin_bias = [gpu_normal((d["spec"].rows,), 0.5, 8000 + i) for i, d in enumerate(mats)]
+    gemm_bias = gpu_normal((pm.rows,), 0.5, 8999)
+
+    def linear_bias():
+        for d, b in zip(mats, lin_bias):
+            nf4.linear(d["x"], d["qs"], b, out_dtype=torch.float32, out=d["y"])
+
+    def ph_gemm_bias():
+        for q, y in zip(gemm_w, gemm_y):
+            nf4.linear(px, q, gemm_bias, out=y)
+
     # MLP-shaped products, one matrix per launch, rotating over distinct
     # weights: the stack's [11008, 4096] matrices (bs 64), and 48 seeded
     # [4096, 11008] ones
@@ -247,7 +261,7 @@ def main():
     fns = dict(quantize=quantize_at(bs, True), dequantize=dequantize_at(bs), gemv=gemv_at(bs),
                gemv_single=gemv_single, quantize_grouped=quantize_grouped,
                dequantize_grouped=dequantize_grouped,
-               gemm=ph_gemm, copy=ph_copy)
+               gemm=ph_gemm, copy=ph_copy, linear_bias=linear_bias, gemm_bias=ph_gemm_bias)
     for b in sweep_bs:
         fns[f"quantize_bs{b}"] = quantize_at(b, False)
         fns[f"dequantize_bs{b}"] = dequantize_at(b)
@@ -355,6 +369,9 @@ def main():
         work[key] = dict(bytes=per * len(e["qss"]), launches=len(e["qss"]))
     M = prefill.ms[0]
     work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols * len(gemm_w), launches=len(gemm_w))
+    work["gemm_bias"] = dict(work["gemm"])
+    work["linear_bias"] = dict(bytes=work["gemv"]["bytes"] + sum(2 * d["spec"].rows for d in mats),
+                               launches=len(mats))
     work["copy"] = dict(bytes=2 * (1 << 30), launches=1)
 
     phase_out = {}
@@ -398,6 +415,8 @@ def main():
             "stack_params": n_stack, "gemv_m": 1, "gemm_mnk": [M, pm.rows, pm.cols],
             "gemm_weights": len(gemm_w),
             "also_timed": "phase gemv_single: the same decode products, one launch per matrix; "
+                          "linear_bias / gemm_bias: those products and the prefill GEMM through "
+                          "nf4_linear with a fused bf16 bias; "
                           "phases quantize_grouped / dequantize_grouped: the stack's quantize / "
                           "dequantize with the seven weights of a layer in one call; "
                           "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "

@@ -85,6 +85,9 @@ _SIGNATURES = [
     ("nf4_gemm", ctypes.c_int32,
      [_P, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    ("nf4_linear", ctypes.c_int32,
+     [_P, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.c_int32, _P,
+      ctypes.c_int32, ctypes.c_int32, _P, _P]),
 ]
 
 _lib = None
@@ -363,8 +366,33 @@ def gemm(x: torch.Tensor, qs: QuantState, out_dtype=torch.bfloat16, out=None) ->
     return _product(lib().nf4_gemm, "nf4_gemm", x, qs, out_dtype, out)
 
 
+def linear(x: torch.Tensor, qs: QuantState, bias: torch.Tensor | None = None,
+           out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
+    """nf4_linear: y[M, N] = x[M, K] . bf16(W)^T (+ bias[N], bf16, added in
+    fp32 before the output rounding); M <= 16 runs the decode kernels, larger M
+    the prefill GEMM."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda:
+        raise TypeError("nf4_linear expects bf16 activations on the GPU")
+    if len(qs.shape) != 2:
+        raise ValueError("nf4_linear expects a quantized [N, K] weight")
+    N, K = (int(s) for s in qs.shape)
+    if bias is not None:
+        if bias.dtype != torch.bfloat16 or not bias.is_cuda or bias.numel() != N:
+            raise ValueError("nf4_linear expects a bf16 GPU bias of N elements")
+        bias = _dev(bias.reshape(-1))
+    x2 = _dev(x.reshape(-1, K))
+    M = x2.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+    d = qs.desc()
+    _check(lib().nf4_linear(_ptr(x2), M, ctypes.byref(d), N, K,
+                            None if bias is None else _ptr(bias), DTYPE_BF16, _DT[out.dtype],
+                            _ptr(out), _stream(x2)), "nf4_linear")
+    return out
+
+
 __all__ = [
     "QuantState", "QWeightDesc", "Nf4Error", "lib", "exported_names", "codebook", "packed_bytes",
     "num_blocks", "quantize", "quantize_grouped", "double_quant", "dequantize",
-    "dequantize_grouped", "gemv", "gemv_grouped", "gemm",
+    "dequantize_grouped", "gemv", "gemv_grouped", "gemm", "linear",
 ]

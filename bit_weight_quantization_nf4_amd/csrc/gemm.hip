@@ -58,6 +58,7 @@ struct GemmArgs {
   const uint16_t *x;
   const uint8_t *packed;
   void *y;
+  const uint16_t *bias;  // [N] bf16 or null
   int32_t M, N, K;
   int32_t log2_bs;
   ScaleArgs sc;
@@ -212,6 +213,21 @@ void gemm_kernel(GemmArgs args) {
     }
   };
 
+  // bias of this lane's output columns n0 + wn * TN + 16 j + lane % 16 (a
+  // column past N reads 0 through the buffer's range check)
+  const bool has_bias = args.bias != nullptr;
+  float bias_n[FN];
+  {
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)args.bias, (short)0, has_bias ? (int)(2u * (uint32_t)N) : 0, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + 16 * j + (lane & 15);
+      bias_n[j] = bf16_bits_to_f32(
+          __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)n), 0, 0));
+    }
+  }
+
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -278,7 +294,8 @@ void gemm_kernel(GemmArgs args) {
 
   // D layout of the 16x16 MFMA: lane l holds column l % 16 and rows
   // 4 (l / 16) + r. Stores go through a buffer resource: rows past M and
-  // columns past N get an out-of-range offset and are dropped.
+  // columns past N get an out-of-range offset and are dropped. The bias of
+  // the lane's columns (loaded before the K walk) is added in fp32.
   constexpr uint32_t kOut = OUT_BF16 ? 2u : 4u;
   const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)((char *)args.y + (int64_t)m0 * N * kOut), (short)0,
@@ -294,7 +311,7 @@ void gemm_kernel(GemmArgs args) {
         const uint32_t off = n < N ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * kOut : kOOB;
         // (a scalar copy first: a bit cast of a vector element directly
         // has been compiled as a cast of element 0)
-        const float v = acc[i][j][r];
+        const float v = has_bias ? acc[i][j][r] + bias_n[j] : acc[i][j][r];
         if (OUT_BF16)
           __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu), yrs,
                                                 (int)off, 0, 0);
@@ -318,13 +335,14 @@ hipError_t launch_cfg(const GemmArgs &args, int grid, bool out_bf16, hipStream_t
 
 hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
                        int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
-                       void *y, hipStream_t stream) {
+                       void *y, const uint16_t *bias, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const CodeTables &t = code_tables(quant_type);
   GemmArgs args;
   args.x = x;
   args.packed = packed;
   args.y = y;
+  args.bias = bias;
   args.M = M;
   args.N = N;
   args.K = K;

@@ -55,6 +55,7 @@ struct GemvProblem {
   const uint16_t *x;
   const uint8_t *packed;
   void *y;
+  const uint16_t *bias;  // [N] bf16 or null
   const float *absmax;
   const int8_t *absmax_q;
   const float *absmax_scale;
@@ -128,6 +129,17 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
     f32x4 acc[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the bias of the one output this thread writes at the end of the item
+    // (NG * 256 <= kThreads), fetched now so its latency is hidden
+    const bool has_bias = P.bias != nullptr;
+    uint32_t bias_bits;
+    {
+      static_assert(NG * 4 * 64 <= kThreads, "one output per thread");
+      const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+          (void *)P.bias, (short)0, has_bias ? 2 * N : 0, kBufferFlags);
+      const int n = row0 + 16 * ((int)threadIdx.x / 256) + ((int)threadIdx.x & 15);
+      bias_bits = __builtin_amdgcn_raw_buffer_load_b16(brs, 2 * n, 0, 0);
+    }
 
     // Activations through a buffer resource: lanes whose row m >= M get an
     // out-of-range offset, which returns zeros without a memory access, so
@@ -210,6 +222,7 @@ __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs args) {
       float sum = 0.0f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) sum += red[((w * NG + g) * 4 + r) * 64 + l];
+      if (has_bias) sum += bf16_bits_to_f32(bias_bits);
       // D layout of the 16x16 MFMA: lane l holds rows 4*(l/16)+r of column l%16.
       const int m = 4 * (l >> 4) + r;
       const int n = row0 + 16 * g + (l & 15);
@@ -348,6 +361,17 @@ __device__ __forceinline__ void x_compute(const GemvArgs &args, const XItem &it,
                                           const XLoads<CPW> &L, const uint4 (&xa)[CPW][4],
                                           const char *tbl, uint32_t lane_base, int lane, int kg,
                                           int wave, float *red) {
+  // the bias of the output this thread writes at the end (threads < 256),
+  // fetched before the item's arithmetic so its latency is hidden
+  const GemvProblem &P = args.p[it.pi];
+  const bool has_bias = P.bias != nullptr;
+  uint32_t bias_bits;
+  {
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)P.bias, (short)0, has_bias ? 2 * P.N : 0, kBufferFlags);
+    bias_bits = __builtin_amdgcn_raw_buffer_load_b16(
+        brs, 2 * (it.row0 + ((int)threadIdx.x & 15)), 0, 0);
+  }
   f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
@@ -372,8 +396,8 @@ __device__ __forceinline__ void x_compute(const GemvArgs &args, const XItem &it,
     float sum = 0.0f;
 #pragma unroll
     for (int w = 0; w < kXWaves; ++w) sum += red[(w * 4 + r) * 64 + l];
+    if (has_bias) sum += bf16_bits_to_f32(bias_bits);
     // D layout of the 16x16 MFMA: lane l holds rows 4*(l/16)+r of column l%16.
-    const GemvProblem &P = args.p[it.pi];
     const int m = 4 * (l >> 4) + r;
     const int n = it.row0 + (l & 15);
     if (m < args.M && n < P.N) {
@@ -489,6 +513,7 @@ hipError_t launch_xreg_group(int count, const GemvDesc *descs, int M, int quant_
     p.x = d.x;
     p.packed = d.packed;
     p.y = d.y;
+    p.bias = d.bias;
     p.absmax = d.sc.absmax;
     p.absmax_q = d.sc.absmax_q;
     p.absmax_scale = d.sc.absmax_scale;
@@ -536,6 +561,7 @@ hipError_t launch_split_group(int count, const GemvDesc *descs, int M, int quant
     p.x = d.x;
     p.packed = d.packed;
     p.y = d.y;
+    p.bias = d.bias;
     p.absmax = d.sc.absmax;
     p.absmax_q = d.sc.absmax_q;
     p.absmax_scale = d.sc.absmax_scale;

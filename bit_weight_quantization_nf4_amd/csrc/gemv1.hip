@@ -52,6 +52,7 @@ struct Gemv1Problem {
   const uint16_t *x;
   const uint8_t *packed;
   void *y;
+  const uint16_t *bias;  // [N] bf16 or null
   const float *absmax;
   const int8_t *absmax_q;
   const float *absmax_scale;
@@ -128,6 +129,7 @@ struct RowLoads {
   uint4 pw[J][2];
   float sf[J][BS32 ? 2 : 1];
   int32_t sq[J][BS32 ? 2 : 1];
+  uint32_t bias;  // bf16 bits of the row's bias (0 without one)
 };
 
 // Waves per SIMD the register budget is sized for: x for J slices lives in
@@ -218,6 +220,10 @@ void gemv1_kernel(Gemv1Args args) {
     const int8_t *absmax_q = args.p[pi].absmax_q;
     const float *absmax_scale = args.p[pi].absmax_scale;
     void *y = args.p[pi].y;
+    const uint16_t *bias = args.p[pi].bias;
+    const bool has_bias = bias != nullptr;
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)bias, (short)0, has_bias ? (int)(2u * (uint32_t)nrows) : 0, kBufferFlags);
     const int K = args.p[pi].K;
     const int log2_bs = args.p[pi].log2_bs, log2_bs2 = args.p[pi].log2_bs2;
     const uint32_t row_bytes = (uint32_t)K >> 1;
@@ -308,6 +314,8 @@ void gemv1_kernel(Gemv1Args args) {
         L.pw[j][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                    prs, (int)(voff[j] + 16u), 0, 0));
       }
+      // the row's bias (a uniform address; no bias: an empty range, reads 0)
+      L.bias = __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)rl), 0, 0);
       // keep the scheduler from hoisting the previous row's arithmetic (and
       // its waits) above these loads
       __builtin_amdgcn_sched_barrier(0);
@@ -327,7 +335,8 @@ void gemv1_kernel(Gemv1Args args) {
           dot32(L.pw[j][p], ap, &xv[j][16 * p], tbl, lane_base, acc0, acc1);
         }
       }
-      const float sum = wave_sum(acc0 + acc1);
+      float sum = wave_sum(acc0 + acc1);
+      if (has_bias) sum += bf16_bits_to_f32(L.bias);
       // Lane 63 holds the total. Every lane issues the store (no branch, so
       // the compiler counts it and its waits for later rows stay exact); the
       // buffer is the one output element, and the other lanes' offsets lie
@@ -488,6 +497,7 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
     p.x = d.x;
     p.packed = d.packed;
     p.y = d.y;
+    p.bias = d.bias;
     p.absmax = d.sc.absmax;
     p.absmax_q = d.sc.absmax_q;
     p.absmax_scale = d.sc.absmax_scale;

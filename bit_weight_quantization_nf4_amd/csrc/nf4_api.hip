@@ -264,10 +264,12 @@ nf4_status nf4_gemv(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t
   return nf4_gemv_grouped(1, &x_bf16, M, w, &N, &K, compute_dtype, out_dtype, &y, stream);
 }
 
-nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
-                            const nf4_qweight *w, const int32_t *N, const int32_t *K,
-                            int32_t compute_dtype, int32_t out_dtype, void *const *y,
-                            void *stream) {
+// the grouped decode products, each with an optional bias (bias == nullptr:
+// none for any product)
+static nf4_status gemv_grouped_impl(int32_t count, const void *const *x_bf16, int32_t M,
+                                    const nf4_qweight *w, const int32_t *N, const int32_t *K,
+                                    const void *const *bias, int32_t compute_dtype,
+                                    int32_t out_dtype, void *const *y, void *stream) {
   if (count < 0 || count > NF4_GEMV_MAX_GROUP) return NF4_ERR_INVALID_ARGUMENT;
   if (count == 0) return NF4_OK;
   if (x_bf16 == nullptr || w == nullptr || N == nullptr || K == nullptr || y == nullptr)
@@ -280,10 +282,12 @@ nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
     if (st != NF4_OK) return st;
     if (w[i].quant_type != w[0].quant_type || w[i].double_quant != w[0].double_quant)
       return NF4_ERR_UNSUPPORTED;
+    const uint16_t *b = bias ? static_cast<const uint16_t *>(bias[i]) : nullptr;
+    if ((reinterpret_cast<uintptr_t>(b) & 1u) != 0) return NF4_ERR_MISALIGNED;
     descs[i] = GemvDesc{static_cast<const uint16_t *>(x_bf16[i]), w[i].packed, y[i], sc, N[i],
-                        K[i], w[i].blocksize};
+                        K[i], w[i].blocksize, b};
   }
-  if (M > 16) return NF4_ERR_INVALID_ARGUMENT;
+  if (M > NF4_GEMV_MAX_M) return NF4_ERR_INVALID_ARGUMENT;
   for (int i = 0; i < count; ++i)
     if (K[i] > (1 << 26)) return NF4_ERR_UNSUPPORTED;  // 31-bit activation offsets
   if (M == 0) return NF4_OK;
@@ -311,11 +315,20 @@ nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
   return st;
 }
 
-nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
-                    int32_t compute_dtype, int32_t out_dtype, void *y, void *stream) {
+nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
+                            const nf4_qweight *w, const int32_t *N, const int32_t *K,
+                            int32_t compute_dtype, int32_t out_dtype, void *const *y,
+                            void *stream) {
+  return gemv_grouped_impl(count, x_bf16, M, w, N, K, nullptr, compute_dtype, out_dtype, y, stream);
+}
+
+static nf4_status gemm_impl(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N,
+                            int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
+                            void *y, void *stream) {
   ScaleArgs sc;
   nf4_status st = check_product(x_bf16, M, w, N, K, compute_dtype, out_dtype, y, &sc);
   if (st != NF4_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(bias) & 1u) != 0) return NF4_ERR_MISALIGNED;
   // a tile's offsets into x, the codes and y are 32-bit
   if (K > (1 << 22) || N > (1 << 21)) return NF4_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return NF4_OK;
@@ -323,7 +336,23 @@ nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t
   if (st != NF4_OK) return st;
   return from_hip(launch_gemm(static_cast<const uint16_t *>(x_bf16), M, w->packed, N, K,
                               w->blocksize, w->quant_type, sc, out_dtype == NF4_DTYPE_BF16, y,
+                              static_cast<const uint16_t *>(bias),
                               reinterpret_cast<hipStream_t>(stream)));
+}
+
+nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+                    int32_t compute_dtype, int32_t out_dtype, void *y, void *stream) {
+  return gemm_impl(x_bf16, M, w, N, K, nullptr, compute_dtype, out_dtype, y, stream);
+}
+
+nf4_status nf4_linear(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+                      const void *bias_bf16, int32_t compute_dtype, int32_t out_dtype, void *y,
+                      void *stream) {
+  // decode shapes take the GEMV kernels, larger batches the prefill GEMM
+  if (M >= 0 && M <= NF4_GEMV_MAX_M)
+    return gemv_grouped_impl(1, &x_bf16, M, w, &N, &K, &bias_bf16, compute_dtype, out_dtype, &y,
+                             stream);
+  return gemm_impl(x_bf16, M, w, N, K, bias_bf16, compute_dtype, out_dtype, y, stream);
 }
 
 }  // extern "C"

@@ -58,6 +58,7 @@ struct GemvDesc {
   void *y;                // [M, N]
   ScaleArgs sc;
   int32_t N, K, blocksize;
+  const uint16_t *bias;   // [N] bf16, added in fp32 before the output rounding; or null
 };
 
 // Largest number of products in one grouped launch.
@@ -77,8 +78,9 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// bias: [N] bf16 added in fp32 before the output rounding, or null
 hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
                        int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
-                       void *y, hipStream_t stream);
+                       void *y, const uint16_t *bias, hipStream_t stream);
 
 }  // namespace nf4

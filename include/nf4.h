@@ -209,6 +209,24 @@ nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
 nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                     int32_t compute_dtype, int32_t out_dtype, void *y, void *stream);
 
+/* Largest M that nf4_linear sends to the decode kernels (nf4_gemv's range). */
+#define NF4_GEMV_MAX_M 16
+
+/* A 4-bit linear layer with an optional fused bias, the kernel picked from the
+ * shape [repo page ossradar.top bitsandbytes, release notes 0.50.0,
+ * "Highlights": the new fused 4-bit kernels take the bias as well, and the
+ * kernel is selected at run time from the shape]:
+ *   y[m, j] = RN_fp32( sum_k bf16(dequant(W)[j, k]) * x[m, k] ) + bias[j]
+ * with the sum accumulated in fp32 exactly as nf4_gemv / nf4_gemm do, then the
+ * bf16 bias added in fp32, then the output rounding (bf16 = RNE of that fp32
+ * value). bias_bf16: device [N] bf16, 2-byte aligned (NF4_ERR_MISALIGNED
+ * otherwise), or NULL for none. 0 <= M <= NF4_GEMV_MAX_M runs nf4_gemv's
+ * kernels, larger M nf4_gemm's, with their layouts, limits and errors. Without
+ * a bias the result is bitwise that of nf4_gemv / nf4_gemm. */
+nf4_status nf4_linear(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+                      const void *bias_bf16, int32_t compute_dtype, int32_t out_dtype, void *y,
+                      void *stream);
+
 #ifdef __cplusplus
 }
 #endif

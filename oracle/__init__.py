@@ -163,6 +163,18 @@ def matmul_bf16(x_bf16: np.ndarray, wc_bf16: np.ndarray) -> np.ndarray:
     return y
 
 
+def linear_bf16(x_bf16: np.ndarray, wc_bf16: np.ndarray, bias_bf16: np.ndarray | None = None):
+    """fp64 y = x @ Wc^T + bias for bf16 x [M, K], Wc [N, K] and bias [N] (or no
+    bias): a linear layer whose bias is part of the product (repo page
+    ossradar.top bitsandbytes, release notes 0.50.0, "Highlights": the fused
+    4-bit kernels take the bias too). The bf16 bias is widened exactly."""
+    y = matmul_bf16(x_bf16, wc_bf16)
+    if bias_bf16 is not None:
+        b = np.ascontiguousarray(bias_bf16, dtype=np.uint16).astype(np.uint32) << 16
+        y = y + b.view(np.float32).astype(np.float64)[None, :]
+    return y
+
+
 def matmul_bf16_sampled(x_bf16: np.ndarray, wc_bf16: np.ndarray, ms, ns) -> np.ndarray:
     """fp64 y[i] = sum_k Wc[ns[i], k] * x[ms[i], k] for the listed positions."""
     x = np.ascontiguousarray(x_bf16, dtype=np.uint16)

@@ -40,7 +40,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(nf4):
     declared = header_functions()
-    assert len(declared) == 14
+    assert len(declared) == 15
     handle = ctypes.CDLL(nf4.LIB_PATH)
     for name in declared:
         assert hasattr(handle, name), name

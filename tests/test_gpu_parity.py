@@ -71,8 +71,10 @@ def check_dequant(nf4, orc, qs, ref, bs, qt, dq):
     return w16_ref
 
 
-def check_product(y32, y16, ref, wc16, x16):
-    """Tolerance bar against the fp64 oracle plus bf16 == RNE(fp32)."""
+def check_product(y32, y16, ref, wc16, x16, bias16=None):
+    """Tolerance bar against the fp64 oracle plus bf16 == RNE(fp32). With a
+    bias, the per-element bound grows by |bias[j]| (the fp32 sum is rounded
+    once more after the bias is added)."""
     y = y32.cpu().numpy().astype(np.float64)
     err = np.abs(y - ref)
     rel = np.linalg.norm(y - ref) / max(np.linalg.norm(ref), 1e-300)
@@ -80,6 +82,8 @@ def check_product(y32, y16, ref, wc16, x16):
     wn = np.linalg.norm(u16_to_f64(wc16), axis=1)
     xn = np.linalg.norm(u16_to_f64(x16), axis=1)
     bound = PER_ELEM * np.outer(xn, wn)
+    if bias16 is not None:
+        bound = bound + PER_ELEM * np.abs(u16_to_f64(bias16))[None, :]
     assert np.all(err <= bound + 1e-30), f"max err/bound {np.max(err / (bound + 1e-30)):.3e}"
     if y16 is not None:
         assert torch.equal(y16.cpu().view(torch.int16), y32.to(torch.bfloat16).cpu().view(torch.int16))
@@ -467,3 +471,51 @@ def test_stack7b_sampled_matrices(nf4, orc, bs):
         y_ref = orc.matmul_bf16(x16, wc16)
         y32 = nf4.gemv(dev(x), qs, torch.float32)
         check_product(y32, None, y_ref, wc16, x16)
+
+
+# ------------------------------------------------------------ linear + bias
+
+
+@pytest.mark.parametrize("M,N,K,bs,dq", [
+    (1, 1000, 512, 64, True),     # single-row kernel
+    (1, 300, 20480, 64, True),    # K > 16384: the K-split kernel at M = 1
+    (4, 1000, 512, 64, True),     # x in registers
+    (4, 130, 8192, 128, False),   # K > 6144: the K-split kernel
+    (16, 257, 1024, 64, True),
+    (17, 300, 512, 64, True),     # past the decode range: the prefill GEMM
+    (64, 1000, 512, 32, False),
+])
+def test_linear_bias_matches_oracle(nf4, orc, M, N, K, bs, dq):
+    """nf4_linear with a bf16 bias against the oracle's linear layer, each path
+    of the dispatch; without a bias it is bitwise nf4_gemv / nf4_gemm, and with
+    one it is bitwise RN_fp32(that result + bias)."""
+    w = workloads.normal_bf16((N, K), 0.02, 7 * M + N + K)
+    x = workloads.normal_bf16((M, K), 1.0, 11 * M + K)
+    b = workloads.normal_bf16((N,), 0.5, 13 * N + M)
+    qs, ref = check_quant(nf4, orc, w, bs, "nf4", dq)
+    _, wc16 = orc.dequantize(ref["packed"], N * K, bs, "nf4", **oracle_scales(ref, dq))
+    x16, b16 = to_u16(x), to_u16(b)
+    y_ref = orc.linear_bf16(x16, wc16.reshape(N, K), b16)
+    xd, bd = dev(x), dev(b)
+    y32 = nf4.linear(xd, qs, bd, torch.float32)
+    y16 = nf4.linear(xd, qs, bd, torch.bfloat16)
+    check_product(y32, y16, y_ref, wc16.reshape(N, K), x16, b16)
+    y_nb = nf4.linear(xd, qs, None, torch.float32)
+    direct = nf4.gemv(xd, qs, torch.float32) if M <= 16 else nf4.gemm(xd, qs, torch.float32)
+    assert torch.equal(y_nb, direct), "without a bias, nf4_linear differs from the direct call"
+    assert torch.equal(y32, y_nb + bd.float()[None, :]), "the bias is not one fp32 add"
+    assert torch.equal(nf4.linear(xd, qs, bd, torch.float32), y32), "not deterministic"
+
+
+def test_linear_rejects_misaligned_bias(nf4):
+    w = workloads.normal_bf16((64, 64), 0.02, 5)
+    qs = nf4.quantize(dev(w), 64, "nf4", double_quant=False)
+    x = dev(workloads.normal_bf16((1, 64), 1.0, 6))
+    y = torch.empty((1, 64), dtype=torch.float32, device="cuda")
+    raw = torch.zeros(65, dtype=torch.uint8, device="cuda")
+    d = qs.desc()
+    import ctypes
+    st = nf4.lib().nf4_linear(ctypes.c_void_p(x.data_ptr()), 1, ctypes.byref(d), 64, 64,
+                              ctypes.c_void_p(raw.data_ptr() + 1), 0, 1,
+                              ctypes.c_void_p(y.data_ptr()), None)
+    assert st == 3, f"status {st}, expected NF4_ERR_MISALIGNED"

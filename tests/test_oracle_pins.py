@@ -419,3 +419,18 @@ def test_7b_storage_accounting():
         total = -(-n // 2) + nb + 4 * (-(-nb // 256))
         assert abs(total / 1e9 - expect_gb) < 0.002
         assert 3.0 < total / 1e9 < 4.0
+
+
+def test_linear_bias_hand_example(orc):
+    """A worked example by hand: x = [[1, 2]], W = [[1, 1], [2, -1]], bias =
+    [0.5, -3] -> y = [[1 + 2 + 0.5, 2 - 2 - 3]] = [[3.5, -3]]; and a zero x
+    gives the bias itself in every row (every value here is exact in bf16)."""
+    bf = lambda v: np.array([orc.f32_to_bf16(float(t)) for t in np.ravel(v)], dtype=np.uint16).reshape(
+        np.shape(v))
+    x = bf([[1.0, 2.0]])
+    w = bf([[1.0, 1.0], [2.0, -1.0]])
+    b = bf([0.5, -3.0])
+    assert np.array_equal(orc.linear_bf16(x, w, b), np.array([[3.5, -3.0]]))
+    assert np.array_equal(orc.linear_bf16(x, w, None), np.array([[3.0, 0.0]]))
+    z = bf(np.zeros((3, 2)))
+    assert np.array_equal(orc.linear_bf16(z, w, b), np.array([[0.5, -3.0]] * 3))
