@@ -59,8 +59,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # for the kernel source it was taken on (its SHA-256); after any change to that
 # source the benchmark reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "gemv1.hip": ("fa8f3ee2184e02442619be55156c575c6d120f89ad83747b9299633f873d9e55", 105663565),
-    "gemm.hip": ("656b93bf13dfda4fc1f6125c152f6d726d1803cdfaeb797536cdf5114cfd0bed", 335017359),
+    "gemv1.hip": ("b7c7f7017cb1d69e7983f32d550aab888f18b4bb71da7cc2e893923f2b24b975", 105748170),
+    "gemm.hip": ("716cea14d23bb31d8facc9fcf26c5a4542dd7a5dc7e19c9d252991b9d3cf89bf", 334951931),
 }
 
 
