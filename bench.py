@@ -85,14 +85,17 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--phases", default="quantize,quantize_grouped,dequantize,dequantize_grouped,"
-                                        "gemv,gemv_single,linear_bias,gemm,gemm_bias,sweep,mlp",
+                                        "gemv,gemv_single,linear_bias,gemm,gemm_bias,sweep,mlp,"
+                                        "batched",
                     help="comma list of quantize, quantize_grouped, dequantize, dequantize_grouped "
                          "(per matrix / the seven weights of a layer per call), gemv (grouped per "
                          "layer), gemv_single (one launch per matrix), linear_bias (the same "
                          "through nf4_linear with a bf16 bias), gemm, gemm_bias (the prefill "
                          "GEMM without / with a fused bias), "
                          "sweep (quantize, dequantize and gemv at the other blocksizes of "
-                         "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16); "
+                         "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16), "
+                         "batched (the stack's decode products at M = 4 and 16, a layer per "
+                         "grouped launch); "
                          "'copy' adds a plain 1 GiB device copy, the known-size reference "
                          "for HBM byte counters")
     ap.add_argument("--no-graph", action="store_true",
@@ -121,7 +124,10 @@ def main():
     requested = args.phases.split(",")
     sweep_bs = [b for b in (64, 128, 256) if b != bs] if "sweep" in requested else []
     mlp_ms = (1, 4, 8, 16) if "mlp" in requested else ()
-    phases = [p for p in requested if p not in ("sweep", "mlp")]
+    batch_ms = (4, 16) if "batched" in requested else ()
+    phases = [p for p in requested if p not in ("sweep", "mlp", "batched")]
+    for m in batch_ms:
+        phases.append(f"gemv_m{m}")
     for b in sweep_bs:
         phases += [f"quantize_bs{b}", f"dequantize_bs{b}", f"gemv_bs{b}"]
     for m in mlp_ms:
@@ -242,6 +248,23 @@ def main():
                 y = torch.empty((m, N), dtype=torch.float32, device=dev)
                 mlp[f"mlp_{name}_m{m}"] = dict(qss=qss, x=x, y=y, N=N, K=K, M=m)
 
+    # the stack's decode products at batch M, a layer's seven per grouped launch
+    # (one activation block per M, shared by the products; an output per product)
+    batch = {}
+    for m in batch_ms:
+        xb = gpu_normal((m, 4096), 1.0, 7300 + m)
+        batch[m] = (xb, [torch.empty((m, d["spec"].rows), dtype=torch.float32, device=dev)
+                         for d in mats])
+
+    def gemv_batched(m):
+        xb, ys = batch[m]
+
+        def f():
+            for li, grp in enumerate(layers):
+                nf4.gemv_grouped([xb] * len(grp), [d["qs"] for d in grp],
+                                 outs=ys[7 * li:7 * li + len(grp)])
+        return f
+
     def mlp_at(key):
         e = mlp[key]
 
@@ -268,6 +291,8 @@ def main():
         fns[f"gemv_bs{b}"] = gemv_at(b)
     for key in mlp:
         fns[key] = mlp_at(key)
+    for m in batch_ms:
+        fns[f"gemv_m{m}"] = gemv_batched(m)
 
     # ---- capture each phase in a graph (after an eager warm-up call)
     graphs = {}
@@ -373,6 +398,11 @@ def main():
     work["linear_bias"] = dict(bytes=work["gemv"]["bytes"] + sum(2 * d["spec"].rows for d in mats),
                                launches=len(mats))
     work["copy"] = dict(bytes=2 * (1 << 30), launches=1)
+    for m in batch_ms:
+        work[f"gemv_m{m}"] = dict(
+            bytes=sum(d["spec"].rows * d["spec"].cols // 2 + meta_bytes(d["spec"].rows * d["spec"].cols, bs)
+                      + 2 * m * d["spec"].cols + 4 * m * d["spec"].rows for d in mats),
+            launches=len(layers))
 
     phase_out = {}
     for p in phases:
@@ -421,7 +451,9 @@ def main():
                           "dequantize with the seven weights of a layer in one call; "
                           "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
                           "[11008,4096] (up) and [4096,11008] (down) NF4 bs64 + double quant, "
-                          "one product per launch over >1 GB of distinct weights, M = 1/4/8/16",
+                          "one product per launch over >1 GB of distinct weights, M = 1/4/8/16; "
+                          "gemv_m4 / gemv_m16: the stack's decode products at M = 4 / 16, a layer "
+                          "per grouped launch",
         },
     }
     if "gemv" in phase_out:
