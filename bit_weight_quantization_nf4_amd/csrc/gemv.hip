@@ -263,7 +263,7 @@ struct XItem {
   int32_t g0;                // first scale group of the item (double quant)
 };
 
-template <bool DQ>
+template <bool DQ, int G>
 __device__ __forceinline__ XItem x_item(const GemvArgs &args, int item, int wave) {
   XItem it;
   int pi = 0;
@@ -272,12 +272,12 @@ __device__ __forceinline__ XItem x_item(const GemvArgs &args, int item, int wave
   const GemvProblem &P = args.p[pi];
   const int N = P.N, K = P.K;
   it.pi = pi;
-  it.row0 = (item - P.item_begin) * 16;
+  it.row0 = (item - P.item_begin) * 16 * G;
   it.nch = (K + kChunk - 1) / kChunk;
   it.c_begin = (wave * it.nch) / kXWaves;
   it.c_end = ((wave + 1) * it.nch) / kXWaves;
   it.kg_last = (K - (it.nch - 1) * kChunk) >> 5;
-  const int rows = item < args.total_items ? (N - it.row0 < 16 ? N - it.row0 : 16) : 0;
+  const int rows = item < args.total_items ? (N - it.row0 < 16 * G ? N - it.row0 : 16 * G) : 0;
   const int64_t e0 = (int64_t)it.row0 * K;  // first element of the item
   const int64_t b0 = e0 >> P.log2_bs;        // its first block (K is a multiple of bs)
   const int nblk = (rows * K) >> P.log2_bs;
@@ -299,19 +299,19 @@ __device__ __forceinline__ XItem x_item(const GemvArgs &args, int item, int wave
   return it;
 }
 
-template <int CPW>
+template <int CPW, int G>
 struct XLoads {
-  uint4 pw[CPW];
-  float sf[CPW];
-  int32_t sq[CPW];
+  uint4 pw[CPW][G];
+  float sf[CPW][G];
+  int32_t sq[CPW][G];
 };
 
 // codes and scale parts of this lane's pieces of an item (a piece past K,
 // last chunk only, reads the chunk start instead; its weights are zeroed later)
-template <int CPW, bool DQ>
-__device__ __forceinline__ XLoads<CPW> x_issue(const GemvArgs &args, const XItem &it, int nl,
-                                               int kg) {
-  XLoads<CPW> L;
+template <int CPW, int G, bool DQ>
+__device__ __forceinline__ XLoads<CPW, G> x_issue(const GemvArgs &args, const XItem &it, int nl,
+                                                  int kg) {
+  XLoads<CPW, G> L;
   const GemvProblem &P = args.p[it.pi];
   const int K = P.K;
 #pragma unroll
@@ -319,16 +319,22 @@ __device__ __forceinline__ XLoads<CPW> x_issue(const GemvArgs &args, const XItem
     int c = it.c_begin + i;
     if (c >= it.c_end) c = it.c_end > it.c_begin ? it.c_end - 1 : 0;
     const int kc = c * kChunk + ((c == it.nch - 1 && kg >= it.kg_last) ? 0 : 32 * kg);
-    const int e = nl * K + kc;  // element of the item
-    L.pw[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(it.wrs, e >> 1, 0, 0));
-    const int b = e >> P.log2_bs;  // block within the item
-    if (DQ) {
-      L.sq[i] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(it.qrs, b, 0, 0);
-      const int g = (int)((((int64_t)it.row0 * K >> P.log2_bs) + b) >> P.log2_bs2) - it.g0;
-      L.sf[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(it.frs, 4 * g, 0, 0));
-    } else {
-      L.sq[i] = 1;
-      L.sf[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(it.frs, 4 * b, 0, 0));
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int e = (16 * g + nl) * K + kc;  // element of the item
+      L.pw[i][g] =
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(it.wrs, e >> 1, 0, 0));
+      const int b = e >> P.log2_bs;  // block within the item
+      if (DQ) {
+        L.sq[i][g] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(it.qrs, b, 0, 0);
+        const int gr = (int)((((int64_t)it.row0 * K >> P.log2_bs) + b) >> P.log2_bs2) - it.g0;
+        L.sf[i][g] =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(it.frs, 4 * gr, 0, 0));
+      } else {
+        L.sq[i][g] = 1;
+        L.sf[i][g] =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(it.frs, 4 * b, 0, 0));
+      }
     }
   }
   return L;
@@ -356,12 +362,12 @@ __device__ __forceinline__ void x_load_x(const GemvArgs &args, const XItem &it, 
   }
 }
 
-template <int CPW, bool DQ, bool OUT_BF16>
+template <int CPW, int G, bool DQ, bool OUT_BF16>
 __device__ __forceinline__ void x_compute(const GemvArgs &args, const XItem &it,
-                                          const XLoads<CPW> &L, const uint4 (&xa)[CPW][4],
+                                          const XLoads<CPW, G> &L, const uint4 (&xa)[CPW][4],
                                           const char *tbl, uint32_t lane_base, int lane, int kg,
                                           int wave, float *red) {
-  // the bias of the output this thread writes at the end (threads < 256),
+  // the bias of the output this thread writes at the end (threads < 256 G),
   // fetched before the item's arithmetic so its latency is hidden
   const GemvProblem &P = args.p[it.pi];
   const bool has_bias = P.bias != nullptr;
@@ -370,36 +376,44 @@ __device__ __forceinline__ void x_compute(const GemvArgs &args, const XItem &it,
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)P.bias, (short)0, has_bias ? 2 * P.N : 0, kBufferFlags);
     bias_bits = __builtin_amdgcn_raw_buffer_load_b16(
-        brs, 2 * (it.row0 + ((int)threadIdx.x & 15)), 0, 0);
+        brs, 2 * (it.row0 + 16 * ((int)threadIdx.x >> 8) + ((int)threadIdx.x & 15)), 0, 0);
   }
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) acc[g] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
     const int c = it.c_begin + i;
     const bool ok = c < it.c_end && (c < it.nch - 1 || kg < it.kg_last);
-    float ap = DQ ? (float)L.sq[i] * L.sf[i] : L.sf[i];
-    ap = ok ? ap : 0.0f;
-    const uint32_t words[4] = {L.pw[i].x, L.pw[i].y, L.pw[i].z, L.pw[i].w};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 b = dequant8(words[s], ap, tbl, lane_base);
-      bf16x8 a = __builtin_bit_cast(bf16x8, xa[i][s]);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    for (int g = 0; g < G; ++g) {
+      float ap = DQ ? (float)L.sq[i][g] * L.sf[i][g] : L.sf[i][g];
+      ap = ok ? ap : 0.0f;
+      const uint32_t words[4] = {L.pw[i][g].x, L.pw[i][g].y, L.pw[i][g].z, L.pw[i][g].w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8 b = dequant8(words[s], ap, tbl, lane_base);
+        bf16x8 a = __builtin_bit_cast(bf16x8, xa[i][s]);
+        acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[g], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) red[(wave * 4 + r) * 64 + lane] = acc[r];
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((wave * G + g) * 4 + r) * 64 + lane] = acc[g][r];
   __syncthreads();
-  // 256 of the threads each add one output over the 16 waves, in wave order
-  if (threadIdx.x < 256) {
-    const int r = threadIdx.x >> 6, l = threadIdx.x & 63;
+  // 256 G of the threads each add one output over the 16 waves, in wave order
+  static_assert(256 * G <= kXThreads, "one output per thread");
+  if (threadIdx.x < 256 * G) {
+    const int g = threadIdx.x >> 8, r = (threadIdx.x >> 6) & 3, l = threadIdx.x & 63;
     float sum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kXWaves; ++w) sum += red[(w * 4 + r) * 64 + l];
+    for (int w = 0; w < kXWaves; ++w) sum += red[((w * G + g) * 4 + r) * 64 + l];
     if (has_bias) sum += bf16_bits_to_f32(bias_bits);
     // D layout of the 16x16 MFMA: lane l holds rows 4*(l/16)+r of column l%16.
     const int m = 4 * (l >> 4) + r;
-    const int n = it.row0 + (l & 15);
+    const int n = it.row0 + 16 * g + (l & 15);
     if (m < args.M && n < P.N) {
       const int64_t o = (int64_t)m * P.N + n;
       if (OUT_BF16)
@@ -410,12 +424,12 @@ __device__ __forceinline__ void x_compute(const GemvArgs &args, const XItem &it,
   }
 }
 
-template <int CPW, bool DQ, bool OUT_BF16>
+template <int CPW, int G, bool DQ, bool OUT_BF16>
 __global__ __launch_bounds__(kXThreads) void gemv_xreg_kernel(GemvArgs args) {
-  __shared__ __attribute__((aligned(16))) char lds[kTableBytes + 2 * kXWaves * 4 * 64 * 4];
+  __shared__ __attribute__((aligned(16))) char lds[kTableBytes + 2 * kXWaves * G * 4 * 64 * 4];
   const char *tbl = lds;
   float *red0 = reinterpret_cast<float *>(lds + kTableBytes);
-  float *red1 = red0 + kXWaves * 4 * 64;
+  float *red1 = red0 + kXWaves * G * 4 * 64;
 
   // pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy
   for (int idx = threadIdx.x; idx < 256 * kCopies; idx += kXThreads) {
@@ -433,26 +447,26 @@ __global__ __launch_bounds__(kXThreads) void gemv_xreg_kernel(GemvArgs args) {
 
   int item = blockIdx.x;
   if (item >= args.total_items) return;  // whole workgroup
-  XItem ia = x_item<DQ>(args, item, wave);
-  XLoads<CPW> la = x_issue<CPW, DQ>(args, ia, nl, kg);
+  XItem ia = x_item<DQ, G>(args, item, wave);
+  XLoads<CPW, G> la = x_issue<CPW, G, DQ>(args, ia, nl, kg);
   uint4 xa[CPW][4];
   int xp = ia.pi;
   x_load_x<CPW>(args, ia, nl, kg, xa);
   __syncthreads();  // table built
   for (;;) {
     // item + step into the second set (an item past the end loads nothing)
-    XItem ib = x_item<DQ>(args, item + step, wave);
-    XLoads<CPW> lb = x_issue<CPW, DQ>(args, ib, nl, kg);
-    x_compute<CPW, DQ, OUT_BF16>(args, ia, la, xa, tbl, lane_base, lane, kg, wave, red0);
+    XItem ib = x_item<DQ, G>(args, item + step, wave);
+    XLoads<CPW, G> lb = x_issue<CPW, G, DQ>(args, ib, nl, kg);
+    x_compute<CPW, G, DQ, OUT_BF16>(args, ia, la, xa, tbl, lane_base, lane, kg, wave, red0);
     item += step;
     if (item >= args.total_items) break;
     if (ib.pi != xp) {
       x_load_x<CPW>(args, ib, nl, kg, xa);
       xp = ib.pi;
     }
-    ia = x_item<DQ>(args, item + step, wave);
-    la = x_issue<CPW, DQ>(args, ia, nl, kg);
-    x_compute<CPW, DQ, OUT_BF16>(args, ib, lb, xa, tbl, lane_base, lane, kg, wave, red1);
+    ia = x_item<DQ, G>(args, item + step, wave);
+    la = x_issue<CPW, G, DQ>(args, ia, nl, kg);
+    x_compute<CPW, G, DQ, OUT_BF16>(args, ib, lb, xa, tbl, lane_base, lane, kg, wave, red1);
     item += step;
     if (item >= args.total_items) break;
     if (ia.pi != xp) {
@@ -462,13 +476,13 @@ __global__ __launch_bounds__(kXThreads) void gemv_xreg_kernel(GemvArgs args) {
   }
 }
 
-template <int CPW, bool DQ>
+template <int CPW, int G, bool DQ>
 hipError_t launch_xreg(const GemvArgs &args, int grid, bool out_bf16, hipStream_t stream) {
   if (out_bf16)
-    hipLaunchKernelGGL((gemv_xreg_kernel<CPW, DQ, true>), dim3(grid), dim3(kXThreads), 0, stream,
-                       args);
+    hipLaunchKernelGGL((gemv_xreg_kernel<CPW, G, DQ, true>), dim3(grid), dim3(kXThreads), 0,
+                       stream, args);
   else
-    hipLaunchKernelGGL((gemv_xreg_kernel<CPW, DQ, false>), dim3(grid), dim3(kXThreads), 0,
+    hipLaunchKernelGGL((gemv_xreg_kernel<CPW, G, DQ, false>), dim3(grid), dim3(kXThreads), 0,
                        stream, args);
   return hipGetLastError();
 }
@@ -502,10 +516,21 @@ namespace {
 hipError_t launch_xreg_group(int count, const GemvDesc *descs, int M, int quant_type,
                              bool double_quant, bool out_bf16, hipStream_t stream) {
   const CodeTables &t = code_tables(quant_type);
+  int rows_total = 0, max_k = 0;
+  for (int i = 0; i < count; ++i) {
+    rows_total += descs[i].N;
+    max_k = descs[i].K > max_k ? descs[i].K : max_k;
+  }
+  const int nch = (max_k + kChunk - 1) / kChunk;
+  const int cpw = (nch + kXWaves - 1) / kXWaves;
+  // 32-row items (two accumulators per wave) put twice the bytes in flight per
+  // item and halve the barriers; taken for short slices (at most 2 chunks per
+  // wave, registers permitting) while every CU still gets several items
+  const int g = (cpw <= 2 && rows_total / 32 >= 4 * device_cu_count()) ? 2 : 1;
   GemvArgs args;
   args.count = 0;
   args.M = M;
-  int items = 0, max_k = 0;
+  int items = 0;
   for (int i = 0; i < count; ++i) {
     const GemvDesc &d = descs[i];
     if (d.N == 0) continue;
@@ -522,24 +547,28 @@ hipError_t launch_xreg_group(int count, const GemvDesc *descs, int M, int quant_
     p.log2_bs = __builtin_ctz((unsigned)d.blocksize);
     p.log2_bs2 = d.sc.log2_bs2;
     p.item_begin = items;
-    items += (d.N + 15) / 16;
-    max_k = d.K > max_k ? d.K : max_k;
+    items += (d.N + 16 * g - 1) / (16 * g);
   }
   if (args.count == 0) return hipSuccess;
   args.total_items = items;
   for (int i = 0; i < 16; ++i) args.value[i] = t.value[i];
-  const int nch = (max_k + kChunk - 1) / kChunk;
-  const int cpw = (nch + kXWaves - 1) / kXWaves;
   const int cap = device_cu_count();
   const int grid = items < cap ? items : cap;
-  if (double_quant) {
-    if (cpw <= 1) return launch_xreg<1, true>(args, grid, out_bf16, stream);
-    if (cpw == 2) return launch_xreg<2, true>(args, grid, out_bf16, stream);
-    return launch_xreg<3, true>(args, grid, out_bf16, stream);
+  if (g == 2) {
+    if (double_quant)
+      return cpw <= 1 ? launch_xreg<1, 2, true>(args, grid, out_bf16, stream)
+                      : launch_xreg<2, 2, true>(args, grid, out_bf16, stream);
+    return cpw <= 1 ? launch_xreg<1, 2, false>(args, grid, out_bf16, stream)
+                    : launch_xreg<2, 2, false>(args, grid, out_bf16, stream);
   }
-  if (cpw <= 1) return launch_xreg<1, false>(args, grid, out_bf16, stream);
-  if (cpw == 2) return launch_xreg<2, false>(args, grid, out_bf16, stream);
-  return launch_xreg<3, false>(args, grid, out_bf16, stream);
+  if (double_quant) {
+    if (cpw <= 1) return launch_xreg<1, 1, true>(args, grid, out_bf16, stream);
+    if (cpw == 2) return launch_xreg<2, 1, true>(args, grid, out_bf16, stream);
+    return launch_xreg<3, 1, true>(args, grid, out_bf16, stream);
+  }
+  if (cpw <= 1) return launch_xreg<1, 1, false>(args, grid, out_bf16, stream);
+  if (cpw == 2) return launch_xreg<2, 1, false>(args, grid, out_bf16, stream);
+  return launch_xreg<3, 1, false>(args, grid, out_bf16, stream);
 }
 
 hipError_t launch_split_group(int count, const GemvDesc *descs, int M, int quant_type,
