@@ -59,8 +59,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # for the kernel source it was taken on (its SHA-256); after any change to that
 # source the benchmark reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "gemv1.hip": ("b7c7f7017cb1d69e7983f32d550aab888f18b4bb71da7cc2e893923f2b24b975", 105748170),
-    "gemm.hip": ("716cea14d23bb31d8facc9fcf26c5a4542dd7a5dc7e19c9d252991b9d3cf89bf", 334951931),
+    "gemv1.hip": ("fcbe1f93273d19cc6b2937644a7bde13195649b866f967babdfa6e636c2ac9a1", 105774357),
+    "gemm.hip": ("c02594d990e55772b2aebc98d40e151be696fd788721fd87ebf7b5efdc0e96d0", 334981229),
 }
 
 

@@ -24,6 +24,8 @@
 // c ^ ((r / 2) mod 8): the operand reads (16 rows, one chunk each) and the
 // row writes then cover every bank once. Staged double-quant scales are held
 // block-column-major, so neighbouring rows read neighbouring bytes.
+// An optional bf16 bias per output column (nf4_linear) is loaded before the
+// K walk and added to the fp32 accumulators before the output rounding.
 // Tile order: consecutive workgroups go to different XCDs (8 of them), so
 // workgroup i takes M tile i % m_tiles and N tile i / m_tiles: with 8 M tiles
 // (M = 2048) each XCD keeps its own X rows hot in its L2 across N tiles.

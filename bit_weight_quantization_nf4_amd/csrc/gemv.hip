@@ -14,7 +14,8 @@
 //  - K <= 6144 (gemv_xreg_kernel): a 16-wave workgroup per CU; wave w owns a
 //    fixed slice of the 128-code chunks of K and holds x of that slice in
 //    registers, loaded once per problem. Persistent workgroups walk work
-//    items of 16 weight rows with two register sets of item loads in turn,
+//    items of 16 weight rows (32, with two accumulators per wave, in big
+//    launches of short rows) with two register sets of item loads in turn,
 //    so the codes and scales of the next item are in flight while the
 //    current one is computed; the 16 partial tiles of an item are added in
 //    wave order through LDS;
@@ -34,7 +35,9 @@
 //    byte 256*e + 8*c): lookups never conflict, and the address is the code
 //    byte moved into bits 15..8 of the lane's base by one v_perm_b32. Per two
 //    weights: 1 perm, 1 LDS read, 2 multiplies by the block scale, 1
-//    v_cvt_pk_bf16_f32 -- the same bf16 weights the dequantize kernel writes.
+//    v_cvt_pk_bf16_f32 -- the same bf16 weights the dequantize kernel writes;
+//  - an optional bf16 bias per output row (nf4_linear) is loaded at the start
+//    of an item by the thread that stores that output, and added to its sum.
 #include "nf4_internal.h"
 
 namespace nf4 {

@@ -31,11 +31,14 @@
 //    per bank pair, address built by one v_perm_b32), times the block scale,
 //    rounded to bf16 pairs with v_cvt_pk_bf16_f32 -- the dequantize kernel's
 //    bf16 weights -- then v_dot2_f32_bf16 with the bf16 activations. This
-//    arithmetic (about 15 VALU cycles per code byte, i.e. per two weights, at
-//    the ~1.9 GHz the chip holds under this load) keeps the SIMDs about 90 %
-//    busy in the main loop: the VALU, not HBM, sets the kernel's pace;
-//  - a row ends with a fixed-order DPP reduction across the wave (no atomics),
-//    so results are bitwise reproducible.
+//    arithmetic (five instructions, about 12 SIMD cycles, per code byte, i.e.
+//    per two weights) keeps the SIMDs busy most of the main loop: it and the
+//    clock the chip holds under it set about half of the kernel's pace;
+//  - a row ends with a fixed-order reduction across the wave (DPP within
+//    16-lane rows, then the 16- and 32-lane swaps; no atomics), so results are
+//    bitwise reproducible;
+//  - an optional bf16 bias per output row (nf4_linear) is loaded with the
+//    row's codes and added to the row's fp32 sum.
 #include "nf4_internal.h"
 
 namespace nf4 {
