@@ -149,9 +149,13 @@ def main():
         w = gpu_normal((m.rows, m.cols), m.sigma, m.seed)
         x = gpu_normal((1, m.cols), 1.0, m.seed + 1000)
         qs = nf4.quantize(w, bs, "nf4", double_quant=True)
+        # y: the grouped gemv phase's output (the one the oracle re-checks);
+        # the per-matrix and bias phases write their own buffers
         mats.append(dict(spec=m, w=w, x=x, qs=qs,
                          wd=torch.empty_like(w),
-                         y=torch.empty((1, m.rows), dtype=torch.float32, device=dev)))
+                         y=torch.empty((1, m.rows), dtype=torch.float32, device=dev),
+                         y_single=torch.empty((1, m.rows), dtype=torch.float32, device=dev),
+                         y_lin=torch.empty((1, m.rows), dtype=torch.float32, device=dev)))
     # the other blocksizes of the sweep share the bf16 weights and outputs
     for d in mats:
         d["qs_bs"] = {b: nf4.quantize(d["w"], b, "nf4", double_quant=True) for b in sweep_bs}
@@ -212,7 +216,7 @@ def main():
         # the same products, one launch per matrix (labelled apart from the
         # grouped phase)
         for d in mats:
-            nf4.gemv(d["x"], d["qs"], out=d["y"])
+            nf4.gemv(d["x"], d["qs"], out=d["y_single"])
 
     def ph_gemm():
         for q, y in zip(gemm_w, gemm_y):
@@ -224,7 +228,7 @@ def main():
 
     def linear_bias():
         for d, b in zip(mats, lin_bias):
-            nf4.linear(d["x"], d["qs"], b, out_dtype=torch.float32, out=d["y"])
+            nf4.linear(d["x"], d["qs"], b, out_dtype=torch.float32, out=d["y_lin"])
 
     def ph_gemm_bias():
         for q, y in zip(gemm_w, gemm_y):
@@ -478,24 +482,38 @@ def main():
         }
     result["phases"] = phase_out
 
+    parity_ok = None
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(mats, bs, args.cpu_seconds)
+        result["cpu_baseline"], parity_ok = cpu_baseline(mats, bs, args.cpu_seconds,
+                                                         check="gemv" in phases)
         result["cpu_baselines"] = cpu_baselines(mats, pw, px, bs, args.cpu_seconds / 2)
+    result["parity_ok"] = parity_ok
     print(json.dumps(result), flush=True)
+    if parity_ok is False:
+        print("bench.py: the GEMV phase's output differs from the oracle beyond the gates",
+              file=sys.stderr)
+        sys.exit(1)
 
 
-def cpu_baseline(mats, bs, target_s):
+REL_L2_GATE = 1e-4     # relative L2 error of a product against the fp64 oracle
+PER_ELEM_GATE = 1e-3   # per element: |y - y_ref| <= gate * ||w_row|| * ||x||
+
+
+def cpu_baseline(mats, bs, target_s, check=True):
     """The CPU oracle's decode GEMV on a bounded sample of the same workload: it
     quantizes the sampled weights itself (from the same bf16 inputs), then its
     timed leg is the GEMV, matrix by matrix until ~target_s seconds of work.
-    Its result is also compared with the GPU's y for those matrices."""
+    With `check`, its result is also compared, element by element, with the
+    output the timed gemv phase left for those matrices (relative L2 <= 1e-4
+    and |y - y_ref| <= 1e-3 ||w_row|| ||x|| with w_row the bf16 dequantized
+    row). Returns (record, parity_ok or None)."""
     import numpy as np
 
     import oracle
     import workloads
 
     oracle.ensure_built(force=False)
-    done_bytes, done_s, count, worst = 0, 0.0, 0, 0.0
+    done_bytes, done_s, count, worst_rel, worst_elem = 0, 0.0, 0, 0.0, 0.0
     for d in mats:
         N, K = d["spec"].rows, d["spec"].cols
         w16 = workloads.to_u16(d["w"].cpu().reshape(-1))
@@ -507,17 +525,29 @@ def cpu_baseline(mats, bs, target_s):
         done_s += time.perf_counter() - t
         nb = -(-(N * K) // bs)
         done_bytes += N * K // 2 + nb + 4 * (-(-nb // 256)) + 2 * K + 4 * N
-        yg = d["y"].cpu().numpy().astype(np.float64)
-        worst = max(worst, float(np.linalg.norm(yg - y) / np.linalg.norm(y)))
+        if check:
+            yg = d["y"].cpu().numpy().astype(np.float64)
+            worst_rel = max(worst_rel, float(np.linalg.norm(yg - y) / np.linalg.norm(y)))
+            _, wc = oracle.dequantize(p, N * K, bs, "nf4", absmax_q=q, absmax_scale=s2)
+            wn = np.linalg.norm((wc.astype(np.uint32) << 16).view(np.float32)
+                                .astype(np.float64).reshape(N, K), axis=1)
+            xn = np.linalg.norm((x16.astype(np.uint32) << 16).view(np.float32)
+                                .astype(np.float64), axis=1)
+            ratio = np.abs(yg - y) / (PER_ELEM_GATE * np.outer(xn, wn) + 1e-300)
+            worst_elem = max(worst_elem, float(ratio.max()))
         count += 1
         if done_s >= target_s:
             break
+    ok = (worst_rel <= REL_L2_GATE and worst_elem <= 1.0) if check else None
+    parity = (f"; GPU gemv-phase y vs oracle y: rel-L2 max {worst_rel:.2e} (gate {REL_L2_GATE:g}), "
+              f"max |err| / (1e-3 ||w|| ||x||) {worst_elem:.2e} (gate 1)" if check else
+              "; gemv phase not run, no parity check")
     return {
         "value": round(done_bytes / done_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": f"oracle decode GEMV (M=1, fp64 sums) over the first {count} matrices of the "
-                  f"stack ({done_bytes / 1e6:.1f} MB algorithmic), {done_s:.1f} s single-threaded; "
-                  f"GPU y vs oracle y rel-L2 max {worst:.2e}",
-    }
+                  f"stack ({done_bytes / 1e6:.1f} MB algorithmic), {done_s:.1f} s single-threaded"
+                  + parity,
+    }, ok
 
 
 def cpu_baselines(mats, pw, px, bs, target_s):

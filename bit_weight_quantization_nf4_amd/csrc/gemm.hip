@@ -355,7 +355,7 @@ hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, i
   for (int i = 0; i < 16; ++i) args.value[i] = t.value[i];
   const int64_t grid = (int64_t)args.m_tiles * args.n_tiles;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (sc.absmax_q == nullptr) return launch_cfg<false, false>(args, (int)grid, out_bf16, stream);
+  if (!sc.double_quant) return launch_cfg<false, false>(args, (int)grid, out_bf16, stream);
   // a tile's scales fit in LDS: at most kQStage blocks, and the groups they
   // touch (one more than they fill, at most) within kGStage
   const int64_t tile_blocks = (int64_t)BN * (K / blocksize);

@@ -63,9 +63,11 @@ nf4_status check_qweight(const nf4_qweight *w, ScaleArgs *sc) {
     if (!aligned16(w->absmax)) return NF4_ERR_MISALIGNED;
   }
   if (!aligned16(w->packed)) return NF4_ERR_MISALIGNED;
-  sc->absmax = w->absmax;
-  sc->absmax_q = w->absmax_q;
-  sc->absmax_scale = w->absmax_scale;
+  // only the scale arrays the flag selects reach the kernels: a caller may
+  // leave stale pointers in the fields the mode does not read
+  sc->absmax = w->double_quant ? nullptr : w->absmax;
+  sc->absmax_q = w->double_quant ? w->absmax_q : nullptr;
+  sc->absmax_scale = w->double_quant ? w->absmax_scale : nullptr;
   sc->double_quant = w->double_quant;
   sc->log2_bs2 = w->double_quant ? __builtin_ctz((unsigned)w->blocksize2) : 0;
   return NF4_OK;

@@ -40,7 +40,7 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        build(force=False)
+        ensure_built(force=False)
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.c_void_p
     i64 = ctypes.c_int64

@@ -519,3 +519,86 @@ def test_linear_rejects_misaligned_bias(nf4):
                               ctypes.c_void_p(raw.data_ptr() + 1), 0, 1,
                               ctypes.c_void_p(y.data_ptr()), None)
     assert st == 3, f"status {st}, expected NF4_ERR_MISALIGNED"
+
+
+# ----------------------------------------------- descriptor scale pointers
+
+
+@pytest.mark.parametrize("M", [17, 64])
+def test_products_read_only_the_scales_the_flag_selects(nf4, orc, M):
+    """A descriptor may carry stale pointers in the scale fields its
+    double-quant flag does not select (the header: absmax is read when
+    double_quant == 0, absmax_q / absmax_scale when it is 1). nf4_gemm and
+    nf4_linear must give bitwise the result of the descriptor with those
+    fields NULL, for both flag values, and match the oracle."""
+    import ctypes
+
+    N, K, bs = 300, 1024, 64
+    w = workloads.normal_bf16((N, K), 0.02, 4400 + M)
+    x = workloads.normal_bf16((M, K), 1.0, 4500 + M)
+    xd = dev(x)
+    x16 = to_u16(x)
+    nb = N * K // bs
+    g = torch.Generator(device="cuda").manual_seed(M)
+    junk_q = torch.randint(-128, 128, (nb,), dtype=torch.int8, device="cuda", generator=g)
+    junk_s = torch.rand((nb + 255) // 256, device="cuda", generator=g) * 100
+    junk_a = torch.rand(nb, device="cuda", generator=g) * 100
+    for dq in (False, True):
+        qs, ref = check_quant(nf4, orc, w, bs, "nf4", dq)
+        _, wc16 = orc.dequantize(ref["packed"], N * K, bs, "nf4", **oracle_scales(ref, dq))
+        y_ref = orc.matmul_bf16(x16, wc16.reshape(N, K))
+        clean = qs.desc()
+        dirty = qs.desc()
+        if dq:
+            clean.absmax = None
+            dirty.absmax = junk_a.data_ptr()
+        else:
+            clean.absmax_q = clean.absmax_scale = None
+            dirty.absmax_q, dirty.absmax_scale = junk_q.data_ptr(), junk_s.data_ptr()
+        outs = {}
+        for name, d in (("clean", clean), ("dirty", dirty)):
+            for fn in ("nf4_gemm", "nf4_linear"):
+                y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+                args = [ctypes.c_void_p(xd.data_ptr()), M, ctypes.byref(d), N, K]
+                if fn == "nf4_linear":
+                    args.append(None)
+                args += [nf4.DTYPE_BF16, nf4.DTYPE_FP32, ctypes.c_void_p(y.data_ptr()), None]
+                assert getattr(nf4.lib(), fn)(*args) == 0, (fn, name, dq)
+                outs[(name, fn)] = y
+        torch.cuda.synchronize()
+        for fn in ("nf4_gemm", "nf4_linear"):
+            assert torch.equal(outs[("clean", fn)], outs[("dirty", fn)]), (fn, dq)
+            check_product(outs[("dirty", fn)], None, y_ref, wc16.reshape(N, K), x16)
+
+
+# ------------------------------------------- a 7B layer, grouped, batched
+
+
+@pytest.mark.parametrize("dq", [False, True])
+def test_gemv_grouped_7b_layer_batched(nf4, orc, dq):
+    """The seven products of one 7B-shaped layer (4 x [4096, 4096],
+    3 x [11008, 4096], NF4 bs 64) in one grouped call at M = 4 and 16: each
+    output bitwise equals the product launched alone and is within tolerance
+    of the oracle. Grouped, the launch holds enough rows for the kernels'
+    large-launch work items, which single products do not reach."""
+    shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 3
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert sum(n for n, _ in shapes) // 32 >= 4 * cu, "the layer no longer reaches big items"
+    qss, refs = [], []
+    for i, (N, K) in enumerate(shapes):
+        w = workloads.normal_bf16((N, K), 0.02, 8800 + i)
+        qs, ref = check_quant(nf4, orc, w, 64, "nf4", dq)
+        qss.append(qs)
+        refs.append(ref)
+    x = workloads.normal_bf16((16, 4096), 1.0, 8899)
+    x16 = to_u16(x)
+    for M in (4, 16):
+        xd = dev(x[:M])
+        ys = nf4.gemv_grouped([xd] * 7, qss, torch.float32)
+        for i, ((N, K), qs, ref, y) in enumerate(zip(shapes, qss, refs, ys)):
+            assert torch.equal(y, nf4.gemv(xd, qs, torch.float32)), (M, i)
+            if i in (0, 4):  # one product of each shape against the oracle
+                y_ref = orc.gemv_quantized(x16[:M], ref["packed"], N, K, 64, "nf4",
+                                           **oracle_scales(ref, dq))
+                _, wc16 = orc.dequantize(ref["packed"], N * K, 64, "nf4", **oracle_scales(ref, dq))
+                check_product(y, None, y_ref, wc16.reshape(N, K), x16[:M])

@@ -17,6 +17,8 @@ import torch
 
 import workloads
 
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 DELTA = 929.0 / 960.0
 
@@ -434,3 +436,28 @@ def test_linear_bias_hand_example(orc):
     assert np.array_equal(orc.linear_bf16(x, w, None), np.array([[3.0, 0.0]]))
     z = bf(np.zeros((3, 2)))
     assert np.array_equal(orc.linear_bf16(z, w, b), np.array([[0.5, -3.0]] * 3))
+
+
+def test_oracle_builds_itself_when_library_missing(tmp_path):
+    """A copy of oracle/ without its compiled library: the first call builds
+    it (gcc) and computes the same codes as the regular build."""
+    import shutil
+    import subprocess
+    import sys
+
+    src = os.path.join(ROOT, "oracle")
+    dst = tmp_path / "oracle"
+    dst.mkdir()
+    for name in os.listdir(src):
+        if name.endswith((".py", ".c")):
+            shutil.copy(os.path.join(src, name), dst / name)
+    assert not (dst / "libnf4_oracle.so").exists()
+    code = ("import numpy as np, oracle\n"
+            "w = np.array([0x3f80, 0xbf00, 0x3e80, 0, 0xbf80, 0x3f33, 0x3dcd, 0xbdb8], np.uint16)\n"
+            "p, a = oracle.quantize(w, 64, 'nf4')\n"
+            "print(bytes(p).hex(), float(a[0]))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=str(tmp_path), capture_output=True,
+                       text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode == 0, r.stderr
+    assert (dst / "libnf4_oracle.so").exists()
+    assert r.stdout.split() == ["f2a70e86", "1.0"]
