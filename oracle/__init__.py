@@ -65,6 +65,22 @@ def _load():
     lib.orc_matmul_bf16_sampled.argtypes = [P, P, i64, P, P, i64, P]
     lib.orc_gemv_quantized.restype = i32
     lib.orc_gemv_quantized.argtypes = [P, i64, P, i64, i64, i32, i32, P, P, P, i32, P]
+    lib.orc_quantize_typed.restype = i32
+    lib.orc_quantize_typed.argtypes = [P, i32, i64, i32, i32, P, P]
+    lib.orc_double_quant_centred.restype = i32
+    lib.orc_double_quant_centred.argtypes = [P, i64, i32, P, P, P]
+    lib.orc_dequantize_typed.restype = i32
+    lib.orc_dequantize_typed.argtypes = [P, i64, i32, i32, P, P, P, P, i32, P, P, P]
+    lib.orc_matmul_typed.restype = i32
+    lib.orc_matmul_typed.argtypes = [P, P, i32, i64, i64, i64, P]
+    lib.orc_gemv_quantized_typed.restype = i32
+    lib.orc_gemv_quantized_typed.argtypes = [P, i32, i64, P, i64, i64, i32, i32, P, P, P, P, i32, P]
+    lib.orc_convert.restype = i32
+    lib.orc_convert.argtypes = [P, i32, i64, P, i32]
+    lib.orc_f32_to_f16.restype = ctypes.c_uint16
+    lib.orc_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.orc_f16_to_f32.restype = ctypes.c_float
+    lib.orc_f16_to_f32.argtypes = [ctypes.c_uint16]
     _lib = lib
     return lib
 
@@ -138,16 +154,25 @@ def double_quant(absmax: np.ndarray, blocksize2: int = 256):
 
 
 def dequantize(packed: np.ndarray, n: int, blocksize: int = 64, quant_type="nf4", absmax=None,
-               absmax_q=None, absmax_scale=None, blocksize2: int = 256):
-    """Dequantize. Returns (fp32[n], bf16 bit patterns uint16[n])."""
+               absmax_q=None, absmax_scale=None, blocksize2: int = 256, absmax_offset=None,
+               half: str = "bf16"):
+    """Dequantize. Returns (fp32[n], 16-bit bit patterns uint16[n]) where the
+    16-bit output is the bf16 (half="bf16") or fp16 (half="fp16") rounding of
+    the fp32 value. absmax_offset: the group offsets of the mean-centred
+    double quant (with absmax_q / absmax_scale)."""
     p = np.ascontiguousarray(packed, dtype=np.uint8)
     out32 = np.zeros(n, dtype=np.float32)
     out16 = np.zeros(n, dtype=np.uint16)
     a = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
     q = None if absmax_q is None else np.ascontiguousarray(absmax_q, dtype=np.int8)
     s2 = None if absmax_scale is None else np.ascontiguousarray(absmax_scale, dtype=np.float32)
-    _check(_load().orc_dequantize(_ptr(p), n, blocksize, _qt(quant_type), _ptr(a), _ptr(q), _ptr(s2),
-                                  blocksize2, _ptr(out32), _ptr(out16)), "dequantize")
+    off = None if absmax_offset is None else np.ascontiguousarray(absmax_offset, dtype=np.float32)
+    if half not in ("bf16", "fp16"):
+        raise ValueError(half)
+    _check(_load().orc_dequantize_typed(
+        _ptr(p), n, blocksize, _qt(quant_type), _ptr(a), _ptr(q), _ptr(s2), _ptr(off), blocksize2,
+        _ptr(out32), _ptr(out16) if half == "bf16" else None,
+        _ptr(out16) if half == "fp16" else None), "dequantize")
     return out32, out16
 
 
@@ -208,4 +233,89 @@ def gemv_quantized(x_bf16: np.ndarray, packed: np.ndarray, N: int, K: int, block
     y = np.zeros((M, N), dtype=np.float64)
     _check(_load().orc_gemv_quantized(_ptr(x), M, _ptr(p), N, K, blocksize, _qt(quant_type), _ptr(a),
                                       _ptr(q), _ptr(s2), blocksize2, _ptr(y)), "gemv")
+    return y
+
+
+# ------------------------------------------------------------ element types
+
+DTYPES = {"bf16": 0, "fp32": 1, "fp16": 2}
+
+
+def _dt(dtype) -> int:
+    return DTYPES[dtype] if isinstance(dtype, str) else int(dtype)
+
+
+def _typed(a: np.ndarray, dtype) -> np.ndarray:
+    """bf16 / fp16 tensors as uint16 bit patterns, fp32 as float32."""
+    if _dt(dtype) == DTYPES["fp32"]:
+        return np.ascontiguousarray(a, dtype=np.float32)
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+def convert(a: np.ndarray, src, dst) -> np.ndarray:
+    """Elementwise conversion between bf16 / fp16 (uint16 bits) and fp32
+    (float32), through the exact fp32 value, rounding to nearest even."""
+    x = _typed(a, src).reshape(-1)
+    out = np.zeros(x.size, dtype=np.float32 if _dt(dst) == DTYPES["fp32"] else np.uint16)
+    _check(_load().orc_convert(_ptr(x), _dt(src), x.size, _ptr(out), _dt(dst)), "convert")
+    return out.reshape(np.shape(a))
+
+
+def quantize_typed(w: np.ndarray, dtype="bf16", blocksize: int = 64, quant_type="nf4"):
+    """Blockwise quantize a flattened tensor of bf16 / fp16 (uint16 bits) or
+    fp32 values, each taken as its exact fp32 value. Returns (packed, absmax)."""
+    x = _typed(w, dtype).reshape(-1)
+    n = x.size
+    packed = np.zeros((n + 1) // 2, dtype=np.uint8)
+    absmax = np.zeros(num_blocks(n, blocksize), dtype=np.float32)
+    _check(_load().orc_quantize_typed(_ptr(x), _dt(dtype), n, blocksize, _qt(quant_type),
+                                      _ptr(packed), _ptr(absmax)), "quantize_typed")
+    return packed, absmax
+
+
+def double_quant_centred(absmax: np.ndarray, blocksize2: int = 256):
+    """Mean-centred second level: per group of bs2 scales, mu = pairwise fp32
+    sum / count, s2 = RN(max |a - mu| / 127), q = clamp(rint((a - mu) / s2)).
+    Returns (q int8[nb], s2 float32[ng], mu float32[ng])."""
+    a = np.ascontiguousarray(absmax.reshape(-1), dtype=np.float32)
+    nb = a.size
+    q = np.zeros(nb, dtype=np.int8)
+    ng = num_blocks(nb, blocksize2)
+    s2 = np.zeros(ng, dtype=np.float32)
+    mu = np.zeros(ng, dtype=np.float32)
+    _check(_load().orc_double_quant_centred(_ptr(a), nb, blocksize2, _ptr(q), _ptr(s2), _ptr(mu)),
+           "double_quant_centred")
+    return q, s2, mu
+
+
+def matmul_typed(x: np.ndarray, wc: np.ndarray, dtype="bf16") -> np.ndarray:
+    """fp64 y = x @ Wc^T for x [M, K] and Wc [N, K] of one compute dtype."""
+    xx = _typed(x, dtype)
+    ww = _typed(wc, dtype)
+    M, K = xx.shape
+    N, K2 = ww.shape
+    assert K == K2
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(_load().orc_matmul_typed(_ptr(xx), _ptr(ww), _dt(dtype), M, N, K, _ptr(y)), "matmul")
+    return y
+
+
+def gemv_quantized_typed(x: np.ndarray, packed: np.ndarray, N: int, K: int, blocksize: int = 64,
+                         quant_type="nf4", absmax=None, absmax_q=None, absmax_scale=None,
+                         absmax_offset=None, blocksize2: int = 256, dtype="bf16") -> np.ndarray:
+    """fp64 y [M, N] = x @ dtype(dequant(W))^T in the compute dtype `dtype`."""
+    xx = _typed(x, dtype)
+    if xx.ndim == 1:
+        xx = xx.reshape(1, -1)
+    M = xx.shape[0]
+    assert xx.shape[1] == K
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    a = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if absmax_q is None else np.ascontiguousarray(absmax_q, dtype=np.int8)
+    s2 = None if absmax_scale is None else np.ascontiguousarray(absmax_scale, dtype=np.float32)
+    off = None if absmax_offset is None else np.ascontiguousarray(absmax_offset, dtype=np.float32)
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(_load().orc_gemv_quantized_typed(_ptr(xx), _dt(dtype), M, _ptr(p), N, K, blocksize,
+                                            _qt(quant_type), _ptr(a), _ptr(q), _ptr(s2), _ptr(off),
+                                            blocksize2, _ptr(y)), "gemv_typed")
     return y

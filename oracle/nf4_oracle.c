@@ -68,6 +68,63 @@ static uint16_t f32_to_bf16_rne(float f) {
 uint16_t orc_f32_to_bf16(float f) { return f32_to_bf16_rne(f); }
 float orc_bf16_to_f32(uint16_t h) { return bf16_to_f32(h); }
 
+/* ------------------------------------------------------------------ fp16 */
+
+/* IEEE binary16 -> binary32, exact: sign, 5-bit exponent (bias 15), 10-bit
+ * fraction; exponent 0 holds zero and the subnormals frac * 2^-24. */
+static float f16_to_f32(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 10) & 31, frac = h & 1023;
+  double v;
+  if (e == 0) v = ldexp((double)frac, -24);
+  else if (e == 31) v = frac ? NAN : INFINITY;
+  else v = ldexp((double)(1024 + frac), e - 25);
+  return (float)(sign ? -v : v); /* exact: at most 11 significant bits */
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, by exact arithmetic
+ * on the value: the result is the multiple of the binary16 spacing at the
+ * input's magnitude (2^-24 for subnormals) nearest to it; magnitudes that
+ * round to 2^16 or beyond give infinity. */
+static uint16_t f32_to_f16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  if (isnan(f)) return (uint16_t)(sign | 0x7e00u);
+  double a = fabs((double)f);
+  if (a == 0.0) return sign;
+  int ex; /* a = m * 2^ex with m in [0.5, 1) */
+  frexp(a, &ex);
+  int q = ex - 11 < -24 ? -24 : ex - 11; /* spacing exponent: 11 significant bits */
+  double scaled = ldexp(a, -q);          /* exact (power-of-two scaling) */
+  double r = floor(scaled);
+  double frac = scaled - r; /* exact */
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  double v = ldexp(r, q); /* the rounded magnitude */
+  if (v >= 65536.0) return (uint16_t)(sign | 0x7c00u);
+  /* encode v: subnormal if below 2^-14 */
+  if (v < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)ldexp(v, 24));
+  int e2;
+  double m = frexp(v, &e2); /* v = m 2^e2, m in [0.5, 1) */
+  uint16_t exp_field = (uint16_t)(e2 - 1 + 15);
+  uint16_t frac_field = (uint16_t)(ldexp(m, 11) - 1024.0);
+  return (uint16_t)(sign | (exp_field << 10) | frac_field);
+}
+
+uint16_t orc_f32_to_f16(float f) { return f32_to_f16_rne(f); }
+float orc_f16_to_f32(uint16_t h) { return f16_to_f32(h); }
+
+/* Element types of tensors passed as raw bits. */
+#define ORC_BF16 0
+#define ORC_FP32 1
+#define ORC_FP16 2
+
+/* Element i of a typed tensor as a binary32 value (exact for every type). */
+static float elem_f32(const void *t, int dtype, int64_t i) {
+  if (dtype == ORC_BF16) return bf16_to_f32(((const uint16_t *)t)[i]);
+  if (dtype == ORC_FP16) return f16_to_f32(((const uint16_t *)t)[i]);
+  return ((const float *)t)[i];
+}
+
 /* ------------------------------------------------- standard normal quantile */
 
 /* Upper tail Q(z) = P(Z > z) = erfc(z / sqrt 2) / 2, using the C library's erfc. */
@@ -202,27 +259,29 @@ int orc_nearest_code(int quant_type, float s) {
  * 16 code values]. Blocks are bs consecutive elements of the flattened tensor
  * (the release notes' 1-D blocksize 64/128/...); the last block may be short
  * and its absmax covers only its real elements [repo page, 0.50.2: mask the
- * absmax store]. Outputs: packed[ceil(n/2)], absmax[ceil(n/bs)]. */
-int orc_quantize(const uint16_t *w, int64_t n, int bs, int quant_type, uint8_t *packed,
-                 float *absmax) {
+ * absmax store]. The input is bf16, fp16 or fp32 (dtype), each element taken
+ * as its exact binary32 value. Outputs: packed[ceil(n/2)], absmax[ceil(n/bs)]. */
+int orc_quantize_typed(const void *w, int dtype, int64_t n, int bs, int quant_type,
+                       uint8_t *packed, float *absmax) {
   float vals[16];
   int cand[16];
   int nc = sorted_candidates(quant_type, vals, cand);
   if (nc == 0 || bs <= 0 || n < 0) return ORC_ERR;
+  if (dtype != ORC_BF16 && dtype != ORC_FP16 && dtype != ORC_FP32) return ORC_ERR;
   for (int64_t i = 0; i < n; ++i)
-    if (!isfinite(bf16_to_f32(w[i]))) return ORC_ERR;
+    if (!isfinite(elem_f32(w, dtype, i))) return ORC_ERR;
   int64_t nb = (n + bs - 1) / bs;
   for (int64_t i = 0; i < (n + 1) / 2; ++i) packed[i] = 0;
   for (int64_t b = 0; b < nb; ++b) {
     int64_t lo = b * bs, hi = lo + bs < n ? lo + bs : n;
     float a = 0.0f;
     for (int64_t i = lo; i < hi; ++i) {
-      float v = fabsf(bf16_to_f32(w[i]));
+      float v = fabsf(elem_f32(w, dtype, i));
       if (v > a) a = v;
     }
     absmax[b] = a;
     for (int64_t i = lo; i < hi; ++i) {
-      float x = bf16_to_f32(w[i]);
+      float x = elem_f32(w, dtype, i);
       float s = (a == 0.0f) ? 0.0f : x / a; /* binary32 division, RN */
       int code = nearest_code(s, vals, cand, nc);
       if (i % 2 == 0)
@@ -232,6 +291,11 @@ int orc_quantize(const uint16_t *w, int64_t n, int bs, int quant_type, uint8_t *
     }
   }
   return ORC_OK;
+}
+
+int orc_quantize(const uint16_t *w, int64_t n, int bs, int quant_type, uint8_t *packed,
+                 float *absmax) {
+  return orc_quantize_typed(w, ORC_BF16, n, bs, quant_type, packed, absmax);
 }
 
 /* ------------------------------------------------------------ double quant */
@@ -268,6 +332,52 @@ int orc_double_quant(const float *absmax, int64_t nb, int bs2, int8_t *q, float 
   return ORC_OK;
 }
 
+/* Mean-centred variant of the second level (a reading: the NF4 page says only
+ * that the scales are quantized again to INT8; centring each group on its
+ * mean lets the int8 codes use both signs). Per group of bs2 consecutive
+ * absmax values a_0 .. a_{L-1} (L = bs2, or fewer in the last group):
+ *   S  = pairwise binary32 sum of the group padded with zeros to bs2 values
+ *        (adjacent pairs first: level by level, element i of a level is
+ *        element 2i plus element 2i+1 of the level below), mu = RN(S / L);
+ *   D  = max_i |RN(a_i - mu)|; s2 = RN(D / 127), or 0 when D = 0;
+ *   q_i = clamp(rint(RN(RN(a_i - mu) / s2)), -127, 127), or 0 when s2 = 0.
+ * Stores q (int8), s2 and mu (fp32 each). The dequantized scale is
+ * a' = RN(RN(q * s2) + mu). bs2 must be a power of two (at most 4096). */
+int orc_double_quant_centred(const float *absmax, int64_t nb, int bs2, int8_t *q, float *s2,
+                             float *offset) {
+  if (bs2 <= 0 || bs2 > 4096 || (bs2 & (bs2 - 1)) != 0 || nb < 0) return ORC_ERR;
+  float buf[4096];
+  int64_t ng = (nb + bs2 - 1) / bs2;
+  for (int64_t g = 0; g < ng; ++g) {
+    int64_t lo = g * bs2, hi = lo + bs2 < nb ? lo + bs2 : nb;
+    int64_t L = hi - lo;
+    for (int i = 0; i < bs2; ++i) buf[i] = (lo + i < hi) ? absmax[lo + i] : 0.0f;
+    for (int w = bs2; w > 1; w >>= 1)
+      for (int i = 0; i < w / 2; ++i) buf[i] = buf[2 * i] + buf[2 * i + 1];
+    float mu = buf[0] / (float)L;
+    float D = 0.0f;
+    for (int64_t i = lo; i < hi; ++i) {
+      float d = fabsf(absmax[i] - mu);
+      if (d > D) D = d;
+    }
+    offset[g] = mu;
+    if (D == 0.0f) {
+      s2[g] = 0.0f;
+      for (int64_t i = lo; i < hi; ++i) q[i] = 0;
+      continue;
+    }
+    float scale = D / 127.0f;
+    s2[g] = scale;
+    for (int64_t i = lo; i < hi; ++i) {
+      float r = rintf((absmax[i] - mu) / scale);
+      if (r > 127.0f) r = 127.0f;
+      if (r < -127.0f) r = -127.0f;
+      q[i] = (int8_t)r;
+    }
+  }
+  return ORC_OK;
+}
+
 /* ---------------------------------------------------------------- dequant */
 
 static int code_at(const uint8_t *packed, int64_t i) {
@@ -275,29 +385,43 @@ static int code_at(const uint8_t *packed, int64_t i) {
   return (i % 2 == 0) ? (byte >> 4) : (byte & 15);
 }
 
-/* Effective block scale a' of block b: the stored fp32 absmax, or with double
- * quant the product of the int8 code and its group's fp32 scale. */
-static float block_scale(int64_t b, const float *absmax, const int8_t *q, const float *s2, int bs2) {
+/* Effective block scale a' of block b: the stored fp32 absmax; with double
+ * quant RN(q * s2) of the int8 code and its group's fp32 scale; with the
+ * mean-centred variant (offset != NULL) RN(RN(q * s2) + mu). */
+static float block_scale(int64_t b, const float *absmax, const int8_t *q, const float *s2,
+                         const float *offset, int bs2) {
   if (q == NULL) return absmax[b];
-  return (float)q[b] * s2[b / bs2];
+  float t = (float)q[b] * s2[b / bs2];
+  if (offset == NULL) return t;
+  return t + offset[b / bs2];
 }
 
-/* Dequantize to the fp32 value w = RN(c[code] * a') and, when out_bf16 is
- * given, to the bf16 compute dtype RNE_bf16(w) [usage page, Configuration:
+/* Dequantize to the fp32 value w = RN(c[code] * a') and, for each 16-bit
+ * output given, to RNE_bf16(w) and RNE_fp16(w) [usage page, Configuration:
  * the compute dtype is the precision used after 4-bit dequantization].
- * q == NULL selects the plain fp32 absmax; otherwise q/s2 are used. */
-int orc_dequantize(const uint8_t *packed, int64_t n, int bs, int quant_type, const float *absmax,
-                   const int8_t *q, const float *s2, int bs2, float *out_f32, uint16_t *out_bf16) {
+ * q == NULL selects the plain fp32 absmax; otherwise q/s2 (and the group
+ * offsets when given) are used. */
+int orc_dequantize_typed(const uint8_t *packed, int64_t n, int bs, int quant_type,
+                         const float *absmax, const int8_t *q, const float *s2,
+                         const float *offset, int bs2, float *out_f32, uint16_t *out_bf16,
+                         uint16_t *out_f16) {
   float vals[16];
   if (orc_codebook(quant_type, vals) != ORC_OK || bs <= 0 || n < 0) return ORC_ERR;
   if (q == NULL && absmax == NULL) return ORC_ERR;
   for (int64_t i = 0; i < n; ++i) {
-    float ap = block_scale(i / bs, absmax, q, s2, bs2);
+    float ap = block_scale(i / bs, absmax, q, s2, offset, bs2);
     float w = vals[code_at(packed, i)] * ap; /* binary32 product, RN */
     if (out_f32) out_f32[i] = w;
     if (out_bf16) out_bf16[i] = f32_to_bf16_rne(w);
+    if (out_f16) out_f16[i] = f32_to_f16_rne(w);
   }
   return ORC_OK;
+}
+
+int orc_dequantize(const uint8_t *packed, int64_t n, int bs, int quant_type, const float *absmax,
+                   const int8_t *q, const float *s2, int bs2, float *out_f32, uint16_t *out_bf16) {
+  return orc_dequantize_typed(packed, n, bs, quant_type, absmax, q, s2, NULL, bs2, out_f32,
+                              out_bf16, NULL);
 }
 
 /* ----------------------------------------------------------------- matmul */
@@ -346,11 +470,70 @@ int orc_gemv_quantized(const uint16_t *x, int64_t M, const uint8_t *packed, int6
     for (int64_t m = 0; m < M; ++m) y[m * N + n] = 0.0;
     for (int64_t k = 0; k < K; ++k) {
       int64_t i = n * K + k;
-      float ap = block_scale(i / bs, absmax, q, s2, bs2);
+      float ap = block_scale(i / bs, absmax, q, s2, NULL, bs2);
       float w = vals[code_at(packed, i)] * ap;
       double wc = (double)bf16_to_f32(f32_to_bf16_rne(w));
       for (int64_t m = 0; m < M; ++m) y[m * N + n] += wc * (double)bf16_to_f32(x[m * K + k]);
     }
+  }
+  return ORC_OK;
+}
+
+/* y[m, n] = sum_k Wc[n, k] * x[m, k] in fp64 for operands of one element type
+ * (bf16, fp16 or fp32 -- the compute dtype; every product of two such values
+ * is exact in fp64), summed in k order. */
+int orc_matmul_typed(const void *x, const void *wc, int dtype, int64_t M, int64_t N, int64_t K,
+                     double *y) {
+  if (M < 0 || N < 0 || K < 0) return ORC_ERR;
+  if (dtype != ORC_BF16 && dtype != ORC_FP16 && dtype != ORC_FP32) return ORC_ERR;
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        acc += (double)elem_f32(wc, dtype, n * K + k) * (double)elem_f32(x, dtype, m * K + k);
+      y[m * N + n] = acc;
+    }
+  return ORC_OK;
+}
+
+/* The decode product straight from the quantized form in a compute dtype:
+ * each weight is dequantized (block_scale, then RN(c * a')), rounded to the
+ * compute dtype (bf16 or fp16 RNE; fp32 kept as is), and its fp64 product
+ * with the activation (of the same dtype) summed in k order. */
+int orc_gemv_quantized_typed(const void *x, int dtype, int64_t M, const uint8_t *packed,
+                             int64_t N, int64_t K, int bs, int quant_type, const float *absmax,
+                             const int8_t *q, const float *s2, const float *offset, int bs2,
+                             double *y) {
+  float vals[16];
+  if (orc_codebook(quant_type, vals) != ORC_OK || bs <= 0 || M < 0 || N < 0 || K < 0)
+    return ORC_ERR;
+  if (dtype != ORC_BF16 && dtype != ORC_FP16 && dtype != ORC_FP32) return ORC_ERR;
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t m = 0; m < M; ++m) y[m * N + n] = 0.0;
+    for (int64_t k = 0; k < K; ++k) {
+      int64_t i = n * K + k;
+      float ap = block_scale(i / bs, absmax, q, s2, offset, bs2);
+      float w = vals[code_at(packed, i)] * ap;
+      double wc;
+      if (dtype == ORC_BF16) wc = (double)bf16_to_f32(f32_to_bf16_rne(w));
+      else if (dtype == ORC_FP16) wc = (double)f16_to_f32(f32_to_f16_rne(w));
+      else wc = (double)w;
+      for (int64_t m = 0; m < M; ++m) y[m * N + n] += wc * (double)elem_f32(x, dtype, m * K + k);
+    }
+  }
+  return ORC_OK;
+}
+
+/* Elementwise conversion of n values between the element types (via the
+ * exact binary32 value; to bf16 / fp16 with RNE). */
+int orc_convert(const void *in, int in_dtype, int64_t n, void *out, int out_dtype) {
+  if (n < 0) return ORC_ERR;
+  for (int64_t i = 0; i < n; ++i) {
+    float f = elem_f32(in, in_dtype, i);
+    if (out_dtype == ORC_BF16) ((uint16_t *)out)[i] = f32_to_bf16_rne(f);
+    else if (out_dtype == ORC_FP16) ((uint16_t *)out)[i] = f32_to_f16_rne(f);
+    else if (out_dtype == ORC_FP32) ((float *)out)[i] = f;
+    else return ORC_ERR;
   }
   return ORC_OK;
 }

@@ -461,3 +461,213 @@ def test_oracle_builds_itself_when_library_missing(tmp_path):
     assert r.returncode == 0, r.stderr
     assert (dst / "libnf4_oracle.so").exists()
     assert r.stdout.split() == ["f2a70e86", "1.0"]
+
+
+# ----------------------------------------------------- fp16 and fp32 types
+
+
+def test_fp16_decode_all_patterns(orc):
+    """Every finite fp16 bit pattern decodes to numpy's float16 value."""
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    ref = h.view(np.float16).astype(np.float32)
+    fin = np.isfinite(ref)
+    got = orc.convert(h, "fp16", "fp32")
+    assert np.array_equal(got[fin].view(np.uint32), ref[fin].view(np.uint32))
+
+
+def test_fp16_rounding_matches_numpy(orc):
+    """fp32 -> fp16 round-to-nearest-even against numpy's conversion: every
+    fp32 whose low 13 bits (the ones fp16 drops from a normal value) are one
+    of the rounding-boundary patterns, over all sign/exponent/high-mantissa
+    combinations in fp16's range and beyond it, plus random values and the
+    whole subnormal range at a stride."""
+    hi = np.arange(0, 1 << 19, dtype=np.uint32) << 13
+    lows = np.array([0, 1, 0x0FFF, 0x1000, 0x1001, 0x1FFF], dtype=np.uint32)
+    u = (hi[:, None] | lows[None, :]).reshape(-1)
+    # keep |f| below 2^17 (beyond: infinity on both sides, checked separately)
+    f = u.view(np.float32)
+    f = f[np.isfinite(f) & (np.abs(f) < 2.0 ** 17)]
+    rng = np.random.default_rng(3)
+    f = np.concatenate([f, rng.standard_normal(1 << 20).astype(np.float32) * 1000,
+                        (np.arange(1 << 20, dtype=np.float32) * 2.0 ** -34),
+                        np.array([65504.0, 65519.99, 65520.0, 1e6, -1e6, 2.0 ** -25,
+                                  np.nextafter(np.float32(2.0 ** -25), np.float32(1))],
+                                 np.float32)])
+    with np.errstate(over="ignore"):
+        ref = f.astype(np.float16).view(np.uint16)
+    got = orc.convert(f, "fp32", "fp16")
+    assert np.array_equal(got, ref), int(np.sum(got != ref))
+
+
+def _thr_codes(orc, qt, xf, absmax, bs):
+    """Independent threshold formulation of the code function on fp32 values:
+    numpy IEEE fp32 division, then the rank among round-down fp32 midpoints."""
+    cb, codes = _sorted_candidates(orc, qt)
+    thr = _rd_thresholds(cb, codes)
+    a = np.repeat(absmax, bs)[: xf.size]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        s = np.where(a == 0, np.float32(0), xf / a).astype(np.float32)
+    return np.array(codes)[np.searchsorted(thr, s, side="left")]
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_quantize_fp32_inputs(orc, qt):
+    """fp32 inputs (no bf16 rounding): the absmax is numpy's max |x| per block
+    and every code agrees with the independent threshold formulation, on
+    random blocks and on blocks built to put x / a on both sides of every
+    decision midpoint; the exact-rational brute force agrees on a sample."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal(64 * 400) * 0.02).astype(np.float32)
+    cb, codes = _sorted_candidates(orc, qt)
+    thr = _rd_thresholds(cb, codes)
+    near = []
+    for t in thr:  # s = t - 2 ulp .. t + 2 ulp, with a = 1 in element 0
+        v = np.float32(t)
+        for _ in range(2):
+            v = np.nextafter(v, np.float32(-2))
+        for _ in range(5):
+            near.append(v)
+            v = np.nextafter(v, np.float32(2))
+    near = np.array(near, np.float32)
+    pad = (-(near.size + 1)) % 64
+    blk = np.concatenate([[np.float32(1.0)], near, np.zeros(pad, np.float32)]).astype(np.float32)
+    w = np.concatenate([w, blk, blk * np.float32(3.0e-5)]).astype(np.float32)
+    p, a = orc.quantize_typed(w, "fp32", 64, qt)
+    assert np.array_equal(a, np.abs(w).reshape(-1, 64).max(axis=1))
+    got = _codes(p, w.size)
+    assert np.array_equal(got, _thr_codes(orc, qt, w, a, 64))
+    idx = np.random.default_rng(2).integers(0, w.size, 300)
+    for i in idx:
+        s = np.float32(w[i] / a[i // 64]) if a[i // 64] != 0 else np.float32(0)
+        assert got[i] == _brute_nearest(s, cb, codes)
+
+
+@pytest.mark.parametrize("qt", ["nf4", "fp4"])
+def test_quantize_fp16_inputs_every_value(orc, qt):
+    """Every finite fp16 value, in blocks whose absmax is fixed by a leading
+    element, against the independent threshold formulation."""
+    h = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    v = h.view(np.float16)
+    h = h[np.isfinite(v) & (np.abs(v.astype(np.float32)) <= 1.5)]
+    one_half = np.float16(1.5).view(np.uint16)
+    rows = h[: h.size - h.size % 63].reshape(-1, 63)
+    w = np.concatenate([np.full((rows.shape[0], 1), one_half, np.uint16), rows], axis=1).reshape(-1)
+    p, a = orc.quantize_typed(w, "fp16", 64, qt)
+    xf = w.view(np.float16).astype(np.float32)
+    assert np.all(a == np.float32(1.5))
+    assert np.array_equal(_codes(p, w.size), _thr_codes(orc, qt, xf, a, 64))
+
+
+def test_quantize_typed_bf16_is_the_bf16_path(orc):
+    w = workloads.to_u16(workloads.normal_bf16((64 * 50 + 17,), 0.02, 41))
+    p1, a1 = orc.quantize(w, 64, "nf4")
+    p2, a2 = orc.quantize_typed(w, "bf16", 64, "nf4")
+    assert np.array_equal(p1, p2) and np.array_equal(a1, a2)
+
+
+# ------------------------------------------------ mean-centred double quant
+
+
+def test_centred_double_quant_worked_examples(orc):
+    """Hand-worked, every value exact in fp32 (bs2 = 4):
+    a = [254, 0, 190.5, 63.5]: S = (254 + 0) + (190.5 + 63.5) = 508, mu = 127,
+      a - mu = [127, -127, 63.5, -63.5], s2 = 127 / 127 = 1, q = [127, -127, 64, -64]
+      (half to even), a' = [254, 0, 191, 63];
+    a = [254, 0, 190.5, 127]: S = 571.5, mu = 142.875, a - mu = [111.125,
+      -142.875, 47.625, -15.875], s2 = 142.875 / 127 = 1.125, q = [99, -127, 42, -14];
+    a = [3, 1, 2] (a short last group: padded with a zero for the sum, divided
+      by 3): S = (3 + 1) + (2 + 0) = 6, mu = 2, s2 = RN(1/127), q = [127, -127, 0]."""
+    q, s2, mu = orc.double_quant_centred(np.array([254, 0, 190.5, 63.5], np.float32), 4)
+    assert q.tolist() == [127, -127, 64, -64] and s2.tolist() == [1.0] and mu.tolist() == [127.0]
+    q, s2, mu = orc.double_quant_centred(np.array([254, 0, 190.5, 127], np.float32), 4)
+    assert q.tolist() == [99, -127, 42, -14] and s2.tolist() == [1.125]
+    assert mu.tolist() == [142.875]
+    q, s2, mu = orc.double_quant_centred(np.array([3, 1, 2], np.float32), 4)
+    assert q.tolist() == [127, -127, 0] and mu.tolist() == [2.0]
+    assert s2[0] == f32(1) / f32(127)
+    # the dequantized scales a' = RN(RN(q s2) + mu) of the first example
+    p = np.array([0xFF, 0xFF], np.uint8)  # code 15 = +1: w = a'
+    w32, _ = orc.dequantize(p, 4, 1, "nf4", absmax_q=np.array([127, -127, 64, -64], np.int8),
+                            absmax_scale=np.array([1.0], np.float32),
+                            absmax_offset=np.array([127.0], np.float32), blocksize2=4)
+    assert w32.tolist() == [254.0, 0.0, 191.0, 63.0]
+
+
+def test_centred_double_quant_invariants(orc):
+    """Groups of 256 scales: q in [-127, 127]; the scale farthest from the
+    centre maps to +-127; |a' - a| <= s2 / 2 plus the two roundings of a';
+    an all-equal group keeps its value exactly (q = 0, a' = mu = a); the
+    pairwise sum is within the pairwise-summation bound of the exact sum."""
+    from fractions import Fraction as Fr
+
+    rng = np.random.default_rng(8)
+    nb = 256 * 4 + 99
+    a = (np.abs(rng.standard_normal(nb)) * 0.05).astype(np.float32)
+    a[256:512] = np.float32(0.0371)
+    q, s2, mu = orc.double_quant_centred(a, 256)
+    assert q.dtype == np.int8 and s2.size == mu.size == 5
+    for g in range(5):
+        blk = a[g * 256:(g + 1) * 256]
+        qb = q[g * 256:(g + 1) * 256].astype(np.int64)
+        assert np.all((qb >= -127) & (qb <= 127))
+        exact = sum(Fr(float(v)) for v in blk)
+        bound = 8 * 2.0 ** -24 * float(np.sum(blk)) + 1e-45  # log2(256) levels
+        assert abs(float(Fr(float(mu[g])) * len(blk) - exact)) <= bound + len(blk) * float(mu[g]) * 2.0 ** -24
+        if g == 1:
+            assert mu[g] == np.float32(0.0371) and s2[g] == 0 and np.all(qb == 0)
+            continue
+        d = np.abs(blk.astype(np.float64) - float(mu[g]))
+        assert abs(qb[int(np.argmax(d))]) == 127
+        ap = ((qb.astype(np.float32) * s2[g]).astype(np.float32) + mu[g]).astype(np.float32)
+        err = np.abs(ap.astype(np.float64) - blk)
+        assert np.all(err <= float(s2[g]) / 2 * (1 + 2 ** -14) + 4 * 2.0 ** -24 * float(blk.max()))
+
+
+# ------------------------------------------------- typed products and dequant
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+def test_matmul_typed_matches_blas(orc, dtype):
+    M, N, K = 3, 29, 160
+    rng = np.random.default_rng(5)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    wf = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    if dtype == "fp16":
+        x, wc = xf.astype(np.float16).view(np.uint16), wf.astype(np.float16).view(np.uint16)
+        xd, wd = x.view(np.float16).astype(np.float64), wc.view(np.float16).astype(np.float64)
+    else:
+        x, wc, xd, wd = xf, wf, xf.astype(np.float64), wf.astype(np.float64)
+    y = orc.matmul_typed(x, wc, dtype)
+    ref = xd @ wd.T
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16", "fp32"])
+@pytest.mark.parametrize("dq", [0, 1, 2])
+def test_gemv_typed_equals_dequant_then_matmul(orc, dtype, dq):
+    """The direct decode product in each compute dtype equals the oracle's
+    dequantize (fp32, or its bf16 / fp16 rounding) followed by its matmul;
+    dequantize's fp16 output is numpy's fp16 rounding of the fp32 output."""
+    N, K, M = 20, 320, 3
+    w = workloads.to_u16(workloads.normal_bf16((N, K), 0.02, 51))
+    p, a = orc.quantize(w, 64, "nf4")
+    kw = dict(absmax=a)
+    if dq == 1:
+        q, s2 = orc.double_quant(a, 256)
+        kw = dict(absmax_q=q, absmax_scale=s2)
+    elif dq == 2:
+        q, s2, mu = orc.double_quant_centred(a, 64)
+        kw = dict(absmax_q=q, absmax_scale=s2, absmax_offset=mu, blocksize2=64)
+    rng = np.random.default_rng(6)
+    xf = rng.standard_normal((M, K)).astype(np.float32)
+    if dtype == "fp32":
+        x = xf
+        wc, _ = orc.dequantize(p, N * K, 64, "nf4", **kw)
+    else:
+        x = orc.convert(xf, "fp32", dtype)
+        w32, wc = orc.dequantize(p, N * K, 64, "nf4", half=dtype, **kw)
+        if dtype == "fp16":
+            assert np.array_equal(wc, w32.astype(np.float16).view(np.uint16))
+    y = orc.gemv_quantized_typed(x, p, N, K, 64, "nf4", dtype=dtype, **kw)
+    ref = orc.matmul_typed(x, wc.reshape(N, K), dtype)
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
