@@ -6,11 +6,12 @@ declared in ``include/nf4.h``; PyTorch supplies device memory and the current
 stream. There is no fallback: if ``libnf4.so`` is not built, importing the
 low-level handle raises.
 
-Functions mirror the C entry points: ``quantize``, ``double_quant``,
-``dequantize``, ``gemv``, ``gemm``, plus ``codebook`` (host) and the size
-helpers. A quantized tensor is described by :class:`QuantState`, the
-counterpart of the pages' 4-bit configuration (quant_type, use_double_quant,
-compute dtype bf16) plus the blocksizes.
+Functions mirror the C entry points: ``quantize`` (nf4_quantize /
+nf4_quantize_ex), ``double_quant``, ``dequantize``, ``gemv``, ``gemm``,
+``linear`` (nf4_linear / nf4_linear_ex), the grouped forms, plus ``codebook``
+(host) and the size helpers. A quantized tensor is described by
+:class:`QuantState`, the counterpart of the pages' 4-bit configuration
+(quant_type, use_double_quant, compute dtype) plus the blocksizes.
 """
 from __future__ import annotations
 
@@ -33,9 +34,22 @@ QUANT_NF4 = 0
 QUANT_FP4 = 1
 DTYPE_BF16 = 0
 DTYPE_FP32 = 1
+DTYPE_FP16 = 2
+DQ_NONE = 0
+DQ_SYMMETRIC = 1
+DQ_CENTRED = 2
+ABI_VERSION = 2
+GEMV_MAX_M = 64
 
 _QT = {"nf4": QUANT_NF4, "fp4": QUANT_FP4}
-_DT = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32}
+_DT = {torch.bfloat16: DTYPE_BF16, torch.float32: DTYPE_FP32, torch.float16: DTYPE_FP16}
+
+
+def _dq(mode) -> int:
+    """Double-quant mode: False / 0 none, True / 1 / "symmetric", 2 / "centred"."""
+    if isinstance(mode, str):
+        return {"none": DQ_NONE, "symmetric": DQ_SYMMETRIC, "centred": DQ_CENTRED}[mode]
+    return int(mode)
 
 
 class QWeightDesc(ctypes.Structure):
@@ -51,6 +65,7 @@ class QWeightDesc(ctypes.Structure):
         ("quant_type", ctypes.c_int32),
         ("double_quant", ctypes.c_int32),
         ("blocksize2", ctypes.c_int32),
+        ("absmax_offset", ctypes.c_void_p),
     ]
 
 
@@ -70,7 +85,12 @@ _SIGNATURES = [
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
       ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(ctypes.c_void_p),
       ctypes.POINTER(ctypes.c_void_p), _P]),
+    ("nf4_quantize_ex", ctypes.c_int32,
+     [_P, ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P, _P, _P]),
     ("nf4_double_quant", ctypes.c_int32, [_P, ctypes.c_int64, ctypes.c_int32, _P, _P, _P]),
+    ("nf4_double_quant_ex", ctypes.c_int32,
+     [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P, _P]),
     ("nf4_dequantize", ctypes.c_int32, [ctypes.POINTER(QWeightDesc), ctypes.c_int32, _P, _P]),
     ("nf4_dequantize_grouped", ctypes.c_int32,
      [ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p),
@@ -88,6 +108,9 @@ _SIGNATURES = [
     ("nf4_linear", ctypes.c_int32,
      [_P, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32, ctypes.c_int32, _P,
       ctypes.c_int32, ctypes.c_int32, _P, _P]),
+    ("nf4_linear_ex", ctypes.c_int32,
+     [_P, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32,
+      ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P]),
 ]
 
 _lib = None
@@ -107,7 +130,7 @@ def lib() -> ctypes.CDLL:
         fn = getattr(h, name)
         fn.restype = res
         fn.argtypes = args
-    if h.nf4_abi_version() != 1:
+    if h.nf4_abi_version() != ABI_VERSION:
         raise RuntimeError("libnf4.so ABI version mismatch")
     _lib = h
     return h
@@ -167,7 +190,9 @@ def codebook(quant_type="nf4") -> list[float]:
 
 @dataclass
 class QuantState:
-    """A quantized tensor: packed codes plus block scales (device tensors)."""
+    """A quantized tensor: packed codes plus block scales (device tensors).
+    double_quant is the mode: 0 none, 1 symmetric, 2 mean-centred (True / False
+    are accepted as 1 / 0)."""
 
     packed: torch.Tensor
     absmax: torch.Tensor
@@ -176,8 +201,9 @@ class QuantState:
     shape: tuple
     blocksize: int
     quant_type: str
-    double_quant: bool
+    double_quant: int
     blocksize2: int = 256
+    absmax_offset: torch.Tensor | None = None
 
     @property
     def n(self) -> int:
@@ -189,56 +215,73 @@ class QuantState:
     def desc(self) -> QWeightDesc:
         return QWeightDesc(
             _ptr(self.packed), _ptr(self.absmax), _ptr(self.absmax_q), _ptr(self.absmax_scale),
-            self.n, self.blocksize, _QT[self.quant_type], int(self.double_quant), self.blocksize2)
+            self.n, self.blocksize, _QT[self.quant_type], _dq(self.double_quant), self.blocksize2,
+            _ptr(self.absmax_offset))
 
     def nbytes(self) -> int:
         b = self.packed.numel()
-        if self.double_quant:
+        if _dq(self.double_quant):
             b += self.absmax_q.numel() + 4 * self.absmax_scale.numel()
+            if self.absmax_offset is not None:
+                b += 4 * self.absmax_offset.numel()
         else:
             b += 4 * self.absmax.numel()
         return b
 
 
-def quantize(w: torch.Tensor, blocksize: int = 64, quant_type: str = "nf4",
-             double_quant: bool = False, out: QuantState | None = None) -> QuantState:
-    """nf4_quantize on a bf16 device tensor (flattened row-major). With
-    ``out`` the result is written into its buffers instead of new ones."""
-    if w.dtype != torch.bfloat16 or not w.is_cuda:
-        raise TypeError("quantize expects a bf16 tensor on the GPU")
-    w = _dev(w)
-    n = w.numel()
+def _new_state(shape, n: int, dev, blocksize: int, quant_type: str, mode: int) -> QuantState:
     nb = (n + blocksize - 1) // blocksize
+    ng = (nb + 255) // 256
+    return QuantState(torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev),
+                      torch.empty(nb, dtype=torch.float32, device=dev),
+                      torch.empty(nb, dtype=torch.int8, device=dev) if mode else None,
+                      torch.empty(ng, dtype=torch.float32, device=dev) if mode else None,
+                      tuple(shape), blocksize, quant_type, mode, 256,
+                      torch.empty(ng, dtype=torch.float32, device=dev)
+                      if mode == DQ_CENTRED else None)
+
+
+def _rows_view(w: torch.Tensor):
+    """(tensor, rows, cols, ld): a row-strided 2-D view of w passed as is (unit
+    element stride, any row stride), anything else as a contiguous copy."""
+    es = w.element_size()
+    if (w.dim() == 2 and w.stride(1) == 1 and w.stride(0) >= w.shape[1]
+            and w.data_ptr() % 16 == 0 and (w.is_contiguous() or (
+                w.shape[1] % 8 == 0 and (w.stride(0) * es) % 16 == 0))):
+        return w, w.shape[0], w.shape[1], w.stride(0)
+    w = _dev(w)
+    return w, 1, w.numel(), w.numel()
+
+
+def quantize(w: torch.Tensor, blocksize: int = 64, quant_type: str = "nf4",
+             double_quant=False, out: QuantState | None = None) -> QuantState:
+    """Quantize a bf16 / fp16 / fp32 device tensor (flattened row-major; a 2-D
+    view with a row stride is read in place). nf4_quantize for contiguous bf16
+    without the centred mode, nf4_quantize_ex otherwise. With ``out`` the
+    result is written into its buffers instead of new ones."""
+    if w.dtype not in _DT or not w.is_cuda:
+        raise TypeError("quantize expects a bf16, fp16 or fp32 tensor on the GPU")
+    mode = _dq(double_quant)
     if out is None:
-        dev = w.device
-        packed = torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev)
-        absmax = torch.empty(nb, dtype=torch.float32, device=dev)
-        q = torch.empty(nb, dtype=torch.int8, device=dev) if double_quant else None
-        s2 = torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev) if double_quant else None
-        out = QuantState(packed, absmax, q, s2, tuple(w.shape), blocksize, quant_type,
-                         double_quant, 256)
-    _check(lib().nf4_quantize(_ptr(w), n, blocksize, _qt(quant_type), int(double_quant),
-                              _ptr(out.packed), _ptr(out.absmax), _ptr(out.absmax_q),
-                              _ptr(out.absmax_scale), _stream(w)), "nf4_quantize")
+        out = _new_state(w.shape, w.numel(), w.device, blocksize, quant_type, mode)
+    if w.dtype == torch.bfloat16 and w.is_contiguous() and mode != DQ_CENTRED:
+        w = _dev(w)
+        _check(lib().nf4_quantize(_ptr(w), w.numel(), blocksize, _qt(quant_type), mode,
+                                  _ptr(out.packed), _ptr(out.absmax), _ptr(out.absmax_q),
+                                  _ptr(out.absmax_scale), _stream(w)), "nf4_quantize")
+        return out
+    src, rows, cols, ld = _rows_view(w)
+    _check(lib().nf4_quantize_ex(_ptr(src), _DT[w.dtype], rows, cols, ld, blocksize,
+                                 _qt(quant_type), mode, _ptr(out.packed), _ptr(out.absmax),
+                                 _ptr(out.absmax_q), _ptr(out.absmax_scale),
+                                 _ptr(out.absmax_offset), _stream(src)), "nf4_quantize_ex")
     return out
 
 
 QUANT_MAX_GROUP = 16
 
 
-def _new_state(w: torch.Tensor, blocksize: int, quant_type: str, double_quant: bool) -> QuantState:
-    n = w.numel()
-    nb = (n + blocksize - 1) // blocksize
-    dev = w.device
-    return QuantState(torch.empty((n + 1) // 2, dtype=torch.uint8, device=dev),
-                      torch.empty(nb, dtype=torch.float32, device=dev),
-                      torch.empty(nb, dtype=torch.int8, device=dev) if double_quant else None,
-                      torch.empty((nb + 255) // 256, dtype=torch.float32, device=dev)
-                      if double_quant else None,
-                      tuple(w.shape), blocksize, quant_type, double_quant, 256)
-
-
-def quantize_grouped(ws, blocksize: int = 64, quant_type: str = "nf4", double_quant: bool = False,
+def quantize_grouped(ws, blocksize: int = 64, quant_type: str = "nf4", double_quant=False,
                      outs=None):
     """nf4_quantize_grouped: several bf16 device tensors quantized in one call
     (one launch with double quant at blocksize 64/128/256). Returns their
@@ -248,36 +291,41 @@ def quantize_grouped(ws, blocksize: int = 64, quant_type: str = "nf4", double_qu
         raise ValueError("quantize_grouped takes at most 16 tensors (and as many outs)")
     if count == 0:
         return []
+    mode = _dq(double_quant)
     ws2, states = [], []
     for i, w in enumerate(ws):
         if w.dtype != torch.bfloat16 or not w.is_cuda:
             raise TypeError("quantize_grouped expects bf16 tensors on the GPU")
         w2 = _dev(w)
         ws2.append(w2)
-        states.append(outs[i] if outs is not None else _new_state(w2, blocksize, quant_type,
-                                                                  double_quant))
+        states.append(outs[i] if outs is not None else
+                      _new_state(w2.shape, w2.numel(), w2.device, blocksize, quant_type, mode))
     vp = ctypes.c_void_p * count
     _check(lib().nf4_quantize_grouped(
         count, vp(*[_ptr(t) for t in ws2]), (ctypes.c_int64 * count)(*[t.numel() for t in ws2]),
-        blocksize, _qt(quant_type), int(double_quant), vp(*[_ptr(q.packed) for q in states]),
+        blocksize, _qt(quant_type), mode, vp(*[_ptr(q.packed) for q in states]),
         vp(*[_ptr(q.absmax) for q in states]), vp(*[_ptr(q.absmax_q) for q in states]),
         vp(*[_ptr(q.absmax_scale) for q in states]), _stream(ws2[0])), "nf4_quantize_grouped")
     return states
 
 
-def double_quant(absmax: torch.Tensor, blocksize2: int = 256):
-    """nf4_double_quant: returns (absmax_q int8[nb], absmax_scale fp32[ceil(nb/bs2)])."""
+def double_quant(absmax: torch.Tensor, blocksize2: int = 256, mode=DQ_SYMMETRIC):
+    """nf4_double_quant_ex: returns (absmax_q int8[nb], absmax_scale fp32[ng])
+    and, in the centred mode, also absmax_offset fp32[ng]."""
     a = _dev(absmax)
     nb = a.numel()
+    mode = _dq(mode)
+    ng = (nb + blocksize2 - 1) // blocksize2
     q = torch.empty(nb, dtype=torch.int8, device=a.device)
-    s2 = torch.empty((nb + blocksize2 - 1) // blocksize2, dtype=torch.float32, device=a.device)
-    _check(lib().nf4_double_quant(_ptr(a), nb, blocksize2, _ptr(q), _ptr(s2), _stream(a)),
-           "nf4_double_quant")
-    return q, s2
+    s2 = torch.empty(ng, dtype=torch.float32, device=a.device)
+    mu = torch.empty(ng, dtype=torch.float32, device=a.device) if mode == DQ_CENTRED else None
+    _check(lib().nf4_double_quant_ex(_ptr(a), nb, blocksize2, mode, _ptr(q), _ptr(s2), _ptr(mu),
+                                     _stream(a)), "nf4_double_quant_ex")
+    return (q, s2) if mode != DQ_CENTRED else (q, s2, mu)
 
 
 def dequantize(qs: QuantState, out_dtype=torch.bfloat16, out: torch.Tensor | None = None):
-    """nf4_dequantize to bf16 (compute dtype) or fp32, shaped like the source."""
+    """nf4_dequantize to bf16 / fp16 (compute dtypes) or fp32, shaped like the source."""
     if out is None:
         out = torch.empty(qs.shape, dtype=out_dtype, device=qs.packed.device)
     d = qs.desc()
@@ -304,9 +352,19 @@ def dequantize_grouped(qss, out_dtype=torch.bfloat16, outs=None):
     return ys
 
 
+def _rows2d(t: torch.Tensor, cols: int):
+    """(tensor, ld) for a [rows, cols] operand: a 2-D view with unit element
+    stride is kept with its row stride, anything else flattened contiguously."""
+    if t.dim() == 2 and t.shape[1] == cols and t.stride(1) == 1 and t.data_ptr() % 16 == 0 \
+            and (t.shape[0] <= 1 or t.stride(0) >= cols):
+        return t, (t.stride(0) if t.shape[0] > 1 else cols)
+    t = _dev(t.reshape(-1, cols))
+    return t, cols
+
+
 def _product(fn, name, x, qs, out_dtype, out):
-    if x.dtype != torch.bfloat16 or not x.is_cuda:
-        raise TypeError(f"{name} expects bf16 activations on the GPU")
+    if x.dtype not in _DT or not x.is_cuda:
+        raise TypeError(f"{name} expects bf16 / fp16 / fp32 activations on the GPU")
     if len(qs.shape) != 2:
         raise ValueError(f"{name} expects a quantized [N, K] weight")
     N, K = (int(s) for s in qs.shape)
@@ -315,13 +373,14 @@ def _product(fn, name, x, qs, out_dtype, out):
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=x.device)
     d = qs.desc()
-    _check(fn(_ptr(x2), M, ctypes.byref(d), N, K, DTYPE_BF16, _DT[out.dtype], _ptr(out),
+    _check(fn(_ptr(x2), M, ctypes.byref(d), N, K, _DT[x.dtype], _DT[out.dtype], _ptr(out),
               _stream(x2)), name)
     return out
 
 
 def gemv(x: torch.Tensor, qs: QuantState, out_dtype=torch.float32, out=None) -> torch.Tensor:
-    """nf4_gemv: y[M, N] = x[M, K] . bf16(W)^T for M <= 16."""
+    """nf4_gemv: y[M, N] = x[M, K] . cd(W)^T for M <= 64; the compute dtype
+    cd is x's dtype (bf16, fp16 or fp32)."""
     return _product(lib().nf4_gemv, "nf4_gemv", x, qs, out_dtype, out)
 
 
@@ -329,9 +388,9 @@ GEMV_MAX_GROUP = 16
 
 
 def gemv_grouped(xs, qss, out_dtype=torch.float32, outs=None):
-    """nf4_gemv_grouped: several independent decode products in one launch.
-    xs[i] is [M, K_i] bf16 (same M for all), qss[i] the quantized [N_i, K_i]
-    weight. Returns the list of y_i [M, N_i]."""
+    """nf4_gemv_grouped: several independent decode products in one call.
+    xs[i] is [M, K_i] (same M and dtype for all), qss[i] the quantized
+    [N_i, K_i] weight. Returns the list of y_i [M, N_i]."""
     count = len(xs)
     if count != len(qss) or count > GEMV_MAX_GROUP:
         raise ValueError("gemv_grouped takes matching lists of at most 16 problems")
@@ -339,8 +398,8 @@ def gemv_grouped(xs, qss, out_dtype=torch.float32, outs=None):
         return []
     xs2, ys, descs, Ns, Ks = [], [], [], [], []
     for i, (x, qs) in enumerate(zip(xs, qss)):
-        if x.dtype != torch.bfloat16 or not x.is_cuda or len(qs.shape) != 2:
-            raise TypeError("gemv_grouped expects bf16 GPU activations and [N, K] weights")
+        if x.dtype not in _DT or not x.is_cuda or len(qs.shape) != 2:
+            raise TypeError("gemv_grouped expects GPU activations and [N, K] weights")
         N, K = (int(v) for v in qs.shape)
         x2 = _dev(x.reshape(-1, K))
         y = outs[i] if outs is not None else torch.empty((x2.shape[0], N), dtype=out_dtype,
@@ -356,38 +415,44 @@ def gemv_grouped(xs, qss, out_dtype=torch.float32, outs=None):
     Darr = (QWeightDesc * count)(*descs)
     Narr = (ctypes.c_int32 * count)(*Ns)
     Karr = (ctypes.c_int32 * count)(*Ks)
-    _check(lib().nf4_gemv_grouped(count, Xarr, M, Darr, Narr, Karr, DTYPE_BF16, _DT[ys[0].dtype],
-                                  Yarr, _stream(xs2[0])), "nf4_gemv_grouped")
+    _check(lib().nf4_gemv_grouped(count, Xarr, M, Darr, Narr, Karr, _DT[xs2[0].dtype],
+                                  _DT[ys[0].dtype], Yarr, _stream(xs2[0])), "nf4_gemv_grouped")
     return ys
 
 
 def gemm(x: torch.Tensor, qs: QuantState, out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
-    """nf4_gemm: y[M, N] = x[M, K] . bf16(W)^T for any M."""
+    """nf4_gemm: y[M, N] = x[M, K] . cd(W)^T for any M (compute dtype = x's)."""
     return _product(lib().nf4_gemm, "nf4_gemm", x, qs, out_dtype, out)
 
 
 def linear(x: torch.Tensor, qs: QuantState, bias: torch.Tensor | None = None,
-           out_dtype=torch.bfloat16, out=None) -> torch.Tensor:
-    """nf4_linear: y[M, N] = x[M, K] . bf16(W)^T (+ bias[N], bf16, added in
-    fp32 before the output rounding); M <= 16 runs the decode kernels, larger M
-    the prefill GEMM."""
-    if x.dtype != torch.bfloat16 or not x.is_cuda:
-        raise TypeError("nf4_linear expects bf16 activations on the GPU")
+           out_dtype=None, out=None) -> torch.Tensor:
+    """nf4_linear_ex: y[M, N] = x[M, K] . cd(W)^T (+ bias[N] in the compute
+    dtype, added in fp32 before the output rounding); the compute dtype is x's
+    dtype; M <= 64 runs the decode kernels, larger M the prefill GEMM. A 2-D x
+    (or ``out``) with a row stride is passed in place. out_dtype defaults to
+    the compute dtype."""
+    if x.dtype not in _DT or not x.is_cuda:
+        raise TypeError("nf4_linear expects bf16 / fp16 / fp32 activations on the GPU")
     if len(qs.shape) != 2:
         raise ValueError("nf4_linear expects a quantized [N, K] weight")
     N, K = (int(s) for s in qs.shape)
     if bias is not None:
-        if bias.dtype != torch.bfloat16 or not bias.is_cuda or bias.numel() != N:
-            raise ValueError("nf4_linear expects a bf16 GPU bias of N elements")
+        if bias.dtype != x.dtype or not bias.is_cuda or bias.numel() != N:
+            raise ValueError("nf4_linear expects a GPU bias of N elements in x's dtype")
         bias = _dev(bias.reshape(-1))
-    x2 = _dev(x.reshape(-1, K))
+    x2, ldx = _rows2d(x, K)
     M = x2.shape[0]
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=x.device)
+        out = torch.empty((M, N), dtype=out_dtype or x.dtype, device=x.device)
+    if out.dim() != 2 or out.shape != (M, N) or out.stride(1) != 1 or \
+            (M > 1 and out.stride(0) < N) or out.data_ptr() % 16:
+        raise ValueError("nf4_linear: out must be an [M, N] view with unit column stride")
+    ldy = out.stride(0) if M > 1 else N
     d = qs.desc()
-    _check(lib().nf4_linear(_ptr(x2), M, ctypes.byref(d), N, K,
-                            None if bias is None else _ptr(bias), DTYPE_BF16, _DT[out.dtype],
-                            _ptr(out), _stream(x2)), "nf4_linear")
+    _check(lib().nf4_linear_ex(_ptr(x2), ldx, M, ctypes.byref(d), N, K,
+                               None if bias is None else _ptr(bias), _DT[x.dtype], _DT[out.dtype],
+                               _ptr(out), ldy, _stream(x2)), "nf4_linear_ex")
     return out
 
 

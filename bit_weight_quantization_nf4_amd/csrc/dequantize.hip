@@ -3,7 +3,8 @@
 // [usage page icman.com.cn/news/48546, "Configuration": the compute dtype is
 //  the precision used after 4-bit dequantization, bf16 preferred; NF4 page,
 //  table 数学原理对比, row 缩放机制: value = code value x block scale.]
-// w = RN(c[code] * a'), a' = absmax or RN(q * s2); bf16 output = RNE(w).
+// w = RN(c[code] * a'), a' = absmax, RN(q * s2) or RN(RN(q * s2) + mu) (the
+// double-quant modes); bf16 / fp16 output = RNE(w).
 //
 // Layout: a wave owns tiles of 1024 consecutive elements and a lane owns
 // elements 8l..8l+7 and 512+8l..512+8l+7 of each (one 4-byte code load per
@@ -57,14 +58,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // The raw inputs of one lane for one whole tile: the packed codes of its two
 // 8-element pieces and what their block scales are made of.
-template <bool DQ>
+template <int DQ>
 struct TileIn {
   uint32_t word[2];
   float a[2];      // fp32 absmax (no double quant) or absmax_scale
   int32_t q[2];    // int8 absmax code (double quant)
+  float mu[2];     // group offset (mean-centred double quant)
 };
 
-template <bool DQ>
+template <int DQ>
 __device__ __forceinline__ TileIn<DQ> load_tile_in(const DequantArgs &args, int64_t lt, int lane) {
   int64_t tile;
   const DTensor &T = locate_tile(args, lt, tile);
@@ -77,8 +79,11 @@ __device__ __forceinline__ TileIn<DQ> load_tile_in(const DequantArgs &args, int6
     if (DQ) {
       t.q[half] = T.sc.absmax_q[b];
       t.a[half] = T.sc.absmax_scale[b >> T.sc.log2_bs2];
+      t.mu[half] = DQ == kDqCentred ? T.sc.absmax_offset[b >> T.sc.log2_bs2] : 0.0f;
     } else {
+      t.q[half] = 1;
       t.a[half] = T.sc.absmax[b];
+      t.mu[half] = 0.0f;
     }
   }
   return t;
@@ -96,14 +101,14 @@ __device__ __forceinline__ void decode8(uint32_t word, float ap, const char *tb,
   }
 }
 
-template <bool OUT_BF16>
+template <int OUT>
 __device__ __forceinline__ void store8(void *out, int64_t e0, const float (&w)[8]) {
-  if (OUT_BF16) {
+  if (OUT != kFP32) {
     u32x4 v;
-    v.x = pack_bf16x2(w[0], w[1]);
-    v.y = pack_bf16x2(w[2], w[3]);
-    v.z = pack_bf16x2(w[4], w[5]);
-    v.w = pack_bf16x2(w[6], w[7]);
+    v.x = pack2<OUT>(w[0], w[1]);
+    v.y = pack2<OUT>(w[2], w[3]);
+    v.z = pack2<OUT>(w[4], w[5]);
+    v.w = pack2<OUT>(w[6], w[7]);
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(reinterpret_cast<uint16_t *>(out) + e0));
   } else {
     f32x4 v0, v1;
@@ -115,21 +120,21 @@ __device__ __forceinline__ void store8(void *out, int64_t e0, const float (&w)[8
   }
 }
 
-template <bool OUT_BF16, bool DQ>
+template <int OUT, int DQ>
 __device__ __forceinline__ void write_tile(const DequantArgs &args, const TileIn<DQ> &in,
                                            int64_t lt, int lane, const char *tb) {
   int64_t t;
   const DTensor &T = locate_tile(args, lt, t);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const float ap = DQ ? (float)in.q[half] * in.a[half] : in.a[half];
+    const float ap = scale_from<DQ>(in.q[half], in.a[half], in.mu[half]);
     float w[8];
     decode8(in.word[half], ap, tb, w);
-    store8<OUT_BF16>(T.out, t * 1024 + 512 * half + 8 * lane, w);
+    store8<OUT>(T.out, t * 1024 + 512 * half + 8 * lane, w);
   }
 }
 
-template <bool OUT_BF16, bool DQ>
+template <int OUT, int DQ>
 __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) {
   __shared__ float table[16];
   if (threadIdx.x < 16) table[threadIdx.x] = args.value[threadIdx.x];
@@ -152,10 +157,10 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
     TileIn<DQ> a = load_tile_in<DQ>(args, t, lane);
     TileIn<DQ> b = load_tile_in<DQ>(args, clampt(t + nwaves), lane);
     for (;;) {
-      write_tile<OUT_BF16, DQ>(args, a, t, lane, tb);
+      write_tile<OUT, DQ>(args, a, t, lane, tb);
       a = load_tile_in<DQ>(args, clampt(t + 2 * nwaves), lane);
       if (t + nwaves >= nfull) break;
-      write_tile<OUT_BF16, DQ>(args, b, t + nwaves, lane, tb);
+      write_tile<OUT, DQ>(args, b, t + nwaves, lane, tb);
       b = load_tile_in<DQ>(args, clampt(t + 3 * nwaves), lane);
       if (t + 2 * nwaves >= nfull) break;
       t += 2 * nwaves;
@@ -173,7 +178,12 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
     for (int half = 0; half < 2; ++half) {
       const int64_t e0 = tl * 1024 + 512 * half + 8 * lane;
       if (e0 >= T.n) continue;
-      const float ap = block_scale(T.sc, e0 >> T.log2_bs);
+      const int64_t b = e0 >> T.log2_bs;
+      const int64_t g = DQ ? b >> T.sc.log2_bs2 : 0;
+      const float ap =
+          DQ ? scale_from<DQ>(T.sc.absmax_q[b], T.sc.absmax_scale[g],
+                              DQ == kDqCentred ? T.sc.absmax_offset[g] : 0.0f)
+             : T.sc.absmax[b];
       const int64_t nbytes = (T.n - e0 + 1) / 2;
       uint32_t word = 0;
       for (int i = 0; i < 4; ++i)
@@ -181,10 +191,10 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
       float w[8];
       decode8(word, ap, tb, w);
       if (e0 + 8 <= T.n) {
-        store8<OUT_BF16>(T.out, e0, w);
-      } else if (OUT_BF16) {
+        store8<OUT>(T.out, e0, w);
+      } else if (OUT != kFP32) {
         uint16_t *o = reinterpret_cast<uint16_t *>(T.out) + e0;
-        for (int i = 0; i < 8 && e0 + i < T.n; ++i) o[i] = (uint16_t)(pack_bf16x2(w[i], 0.0f) & 0xffffu);
+        for (int i = 0; i < 8 && e0 + i < T.n; ++i) o[i] = (uint16_t)out_bits<OUT>(w[i]);
       } else {
         float *o = reinterpret_cast<float *>(T.out) + e0;
         for (int i = 0; i < 8 && e0 + i < T.n; ++i) o[i] = w[i];
@@ -193,12 +203,24 @@ __global__ __launch_bounds__(kThreads) void dequantize_kernel(DequantArgs args) 
   }
 }
 
+template <int OUT, int DQ>
+void launch_cfg(dim3 grid, const DequantArgs &args, hipStream_t stream) {
+  hipLaunchKernelGGL((dequantize_kernel<OUT, DQ>), grid, dim3(kThreads), 0, stream, args);
+}
+
+template <int OUT>
+void launch_out(int dq, dim3 grid, const DequantArgs &args, hipStream_t stream) {
+  if (dq == kDqCentred) launch_cfg<OUT, kDqCentred>(grid, args, stream);
+  else if (dq == kDqSym) launch_cfg<OUT, kDqSym>(grid, args, stream);
+  else launch_cfg<OUT, kDqNone>(grid, args, stream);
+}
+
 }  // namespace
 
 int dequantize_max_group() { return kMaxDGroup; }
 
-hipError_t launch_dequantize(int count, const DequantDesc *ds, int quant_type, bool double_quant,
-                             bool out_bf16, hipStream_t stream) {
+hipError_t launch_dequantize(int count, const DequantDesc *ds, int quant_type, int dq,
+                             int out_dtype, hipStream_t stream) {
   if (count > kMaxDGroup) return hipErrorInvalidValue;
   const CodeTables &t = code_tables(quant_type);
   DequantArgs args;
@@ -225,14 +247,9 @@ hipError_t launch_dequantize(int count, const DequantDesc *ds, int quant_type, b
   int64_t blocks = (tiles + args.count + 4 * 2 - 1) / (4 * 2);
   if (blocks > 16384) blocks = 16384;
   dim3 grid((unsigned)blocks);
-  if (out_bf16 && double_quant)
-    hipLaunchKernelGGL((dequantize_kernel<true, true>), grid, dim3(kThreads), 0, stream, args);
-  else if (out_bf16)
-    hipLaunchKernelGGL((dequantize_kernel<true, false>), grid, dim3(kThreads), 0, stream, args);
-  else if (double_quant)
-    hipLaunchKernelGGL((dequantize_kernel<false, true>), grid, dim3(kThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL((dequantize_kernel<false, false>), grid, dim3(kThreads), 0, stream, args);
+  if (out_dtype == kFP16) launch_out<kFP16>(dq, grid, args, stream);
+  else if (out_dtype == kFP32) launch_out<kFP32>(dq, grid, args, stream);
+  else launch_out<kBF16>(dq, grid, args, stream);
   return hipGetLastError();
 }
 

@@ -1,5 +1,6 @@
-// gemm.hip -- prefill product Y[M, N] = X[M, K] . bf16(dequant(W))[N, K]^T on
-// gfx950 bf16 matrix cores, fp32 accumulation.
+// gemm.hip -- prefill product Y[M, N] = X[M, K] . cd(dequant(W))[N, K]^T on
+// gfx950 matrix cores, fp32 accumulation; cd is the rounding to the compute
+// dtype (bf16 or fp16), the type of X and of the MFMA operands.
 //
 // [repo page ossradar.top bitsandbytes, release notes 0.50.0: a fused 4-bit
 //  dequantize + GEMM replaces dequantize + F.linear; usage page
@@ -24,8 +25,9 @@
 // c ^ ((r / 2) mod 8): the operand reads (16 rows, one chunk each) and the
 // row writes then cover every bank once. Staged double-quant scales are held
 // block-column-major, so neighbouring rows read neighbouring bytes.
-// An optional bf16 bias per output column (nf4_linear) is loaded before the
-// K walk and added to the fp32 accumulators before the output rounding.
+// An optional bias per output column (nf4_linear; compute dtype) is loaded
+// before the K walk and added to the fp32 accumulators before the output
+// rounding. Rows of X and Y may be strided (ldx, ldy elements).
 // Tile order: consecutive workgroups go to different XCDs (8 of them), so
 // workgroup i takes M tile i % m_tiles and N tile i / m_tiles: with 8 M tiles
 // (M = 2048) each XCD keeps its own X rows hot in its L2 across N tiles.
@@ -60,16 +62,19 @@ struct GemmArgs {
   const uint16_t *x;
   const uint8_t *packed;
   void *y;
-  const uint16_t *bias;  // [N] bf16 or null
+  const uint16_t *bias;  // [N] in the compute dtype, or null
   int32_t M, N, K;
+  uint32_t ldx, ldy;     // row strides of x and y, elements
   int32_t log2_bs;
   ScaleArgs sc;
   int32_t m_tiles, n_tiles;
   float value[16];
 };
 
-// 8 codes of one packed word -> 4 bf16 pairs in k order, through the 16-entry
-// fp32 code table in LDS (byte offsets are 4 * code, cut from the word).
+// 8 codes of one packed word -> 4 pairs of the compute type in k order,
+// through the 16-entry fp32 code table in LDS (byte offsets are 4 * code, cut
+// from the word).
+template <int CT>
 __device__ __forceinline__ uint4 dequant8(uint32_t word, float ap, const char *tb) {
   const uint32_t even4 = (word >> 2) & 0x3c3c3c3cu;  // 4 * high nibble of each byte
   const uint32_t odd4 = (word << 2) & 0x3c3c3c3cu;   // 4 * low nibble of each byte
@@ -78,7 +83,7 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, float ap, const char *t
   for (int j = 0; j < 4; ++j) {
     const float c0 = *reinterpret_cast<const float *>(tb + ((even4 >> (8 * j)) & 0xffu));
     const float c1 = *reinterpret_cast<const float *>(tb + ((odd4 >> (8 * j)) & 0xffu));
-    out[j] = pack_bf16x2(c0 * ap, c1 * ap);
+    out[j] = pack2<CT>(c0 * ap, c1 * ap);
   }
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
@@ -88,12 +93,12 @@ __device__ __forceinline__ uint4 dequant8(uint32_t word, float ap, const char *t
 constexpr int kQStage = 20480;   // int8 block scales of one weight tile
 constexpr int kGStage = 512;     // fp32 group scales of one weight tile
 
-template <bool DQ, bool SQ, bool OUT_BF16>
+template <int DQ, bool SQ, int OUT, int CT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmArgs args) {
   // memory loads a thread issues per step for the weight tile (codes, plus
   // the block scales when they are not staged in LDS)
-  constexpr int kCodeLoads = kWPer * (SQ ? 1 : (DQ ? 3 : 2));
+  constexpr int kCodeLoads = kWPer * (SQ ? 1 : (DQ == kDqCentred ? 4 : (DQ ? 3 : 2)));
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * kStride];
   // one spare row past the tile: threads without a weight piece (the last
   // wave) write their zeros there, so the step body needs no branch
@@ -101,6 +106,7 @@ void gemm_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) float table[16];
   __shared__ __attribute__((aligned(16))) int8_t q_lds[SQ ? kQStage : 1];
   __shared__ __attribute__((aligned(16))) float s2_lds[SQ ? kGStage : 1];
+  __shared__ __attribute__((aligned(16))) float mu_lds[SQ && DQ == kDqCentred ? kGStage : 1];
   if (threadIdx.x < 16) table[threadIdx.x] = args.value[threadIdx.x];
   const char *tb = reinterpret_cast<const char *>(table);
 
@@ -115,9 +121,10 @@ void gemm_kernel(GemmArgs args) {
   const uint32_t row_bytes = (uint32_t)K >> 1;
 
   const int x_rows = M - m0 < BM ? M - m0 : BM;
+  const uint32_t ldx = args.ldx;
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(args.x + (int64_t)m0 * K), (short)0, (int)(2u * (uint32_t)x_rows * (uint32_t)K),
-      kBufferFlags);
+      (void *)(args.x + (int64_t)m0 * ldx), (short)0,
+      (int)(2u * ((uint32_t)(x_rows - 1) * ldx + (uint32_t)K)), kBufferFlags);
   // weight tile: piece p = tid + kThreads * u (< kWPieces) is row p / 2,
   // 32-code half p % 2
   const int w_rows = N - n0 < BN ? N - n0 : BN;
@@ -140,6 +147,9 @@ void gemm_kernel(GemmArgs args) {
   const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
       DQ ? (void *)(args.sc.absmax_scale + gbase) : (void *)args.sc.absmax, (short)0,
       (int)(DQ ? 4u * groups : 0u), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      DQ == kDqCentred ? (void *)(args.sc.absmax_offset + gbase) : (void *)args.sc.absmax,
+      (short)0, (int)(DQ == kDqCentred ? 4u * groups : 0u), kBufferFlags);
 
   uint4 wr[kWPer];
   float w_scale[kWPer];
@@ -162,10 +172,14 @@ void gemm_kernel(GemmArgs args) {
         } else if (DQ) {
           const int q =
               (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)(ok ? blk : kOOB), 0, 0);
+          const uint32_t goff = ok ? ((blk_in + blk) >> log2_bs2) << 2 : kOOB;
           const float s2 = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(
-                         srs, (int)(ok ? ((blk_in + blk) >> log2_bs2) << 2 : kOOB), 0, 0));
-          w_scale[u] = (float)q * s2;
+              float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)goff, 0, 0));
+          const float mu = DQ == kDqCentred
+                               ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                               mrs, (int)goff, 0, 0))
+                               : 0.0f;
+          w_scale[u] = scale_from<DQ>(q, s2, mu);
         } else {
           w_scale[u] = __builtin_bit_cast(
               float, __builtin_amdgcn_raw_buffer_load_b32(qrs, (int)(ok ? blk << 2 : kOOB), 0, 0));
@@ -184,7 +198,7 @@ void gemm_kernel(GemmArgs args) {
       const int r = (4 * wave + i) * 8 + (lane >> 3), q = lane & 7;
       const int c = q ^ ((r >> 1) & 7);
       const int kc = k0 + 8 * c;
-      const uint32_t off = kc < K ? 2u * ((uint32_t)r * (uint32_t)K + (uint32_t)kc) : kOOB;
+      const uint32_t off = kc < K ? 2u * ((uint32_t)r * ldx + (uint32_t)kc) : kOOB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xrs, (__attribute__((address_space(3))) void *)&xs[buf][(4 * wave + i) * 512], 16,
           (int)off, 0, 0, 0);
@@ -205,12 +219,15 @@ void gemm_kernel(GemmArgs args) {
           const bool ok = w_blk[u] != 0xffffffffu;
           const uint32_t b = ok ? w_blk[u] : 0u;
           const uint32_t row = (uint32_t)(p >> 1), kb = b - row * row_blocks;
-          ap = ok ? (float)q_lds[kb * BN + row] * s2_lds[(blk_in + b) >> log2_bs2] : 0.0f;
+          const uint32_t gi = (blk_in + b) >> log2_bs2;
+          ap = ok ? scale_from<DQ>(q_lds[kb * BN + row], s2_lds[gi],
+                                   DQ == kDqCentred ? mu_lds[gi] : 0.0f)
+                  : 0.0f;
         }
-        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 0)) = dequant8(wr[u].x, ap, tb);
-        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 1)) = dequant8(wr[u].y, ap, tb);
-        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 2)) = dequant8(wr[u].z, ap, tb);
-        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 3)) = dequant8(wr[u].w, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 0)) = dequant8<CT>(wr[u].x, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 1)) = dequant8<CT>(wr[u].y, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 2)) = dequant8<CT>(wr[u].z, ap, tb);
+        *reinterpret_cast<uint4 *>(wbase + swz(wrow, wc + 3)) = dequant8<CT>(wr[u].w, ap, tb);
       }
     }
   };
@@ -225,7 +242,7 @@ void gemm_kernel(GemmArgs args) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int n = n0 + wn * TN + 16 * j + (lane & 15);
-      bias_n[j] = bf16_bits_to_f32(
+      bias_n[j] = widen16<CT>(
           __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)n), 0, 0));
     }
   }
@@ -243,8 +260,12 @@ void gemm_kernel(GemmArgs args) {
       const uint32_t row = i / row_blocks, kb = i - row * row_blocks;
       q_lds[kb * BN + row] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)i, 0, 0);
     }
-    for (uint32_t i = tid; i < groups; i += kThreads)
+    for (uint32_t i = tid; i < groups; i += kThreads) {
       s2_lds[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(4 * i), 0, 0));
+      if (DQ == kDqCentred)
+        mu_lds[i] =
+            __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(mrs, (int)(4 * i), 0, 0));
+    }
   }
   __syncthreads();  // code table, staged scales
   x_direct(0, 0);
@@ -271,25 +292,22 @@ void gemm_kernel(GemmArgs args) {
     load_step(ks + 2 < nk ? ks + 2 : nk - 1);
     // both halves' operands first, so the reads of the second half overlap
     // the first half's matrix-core work
-    bf16x8 a[2][FM], b[2][FN];
+    uint4 a[2][FM], b[2][FN];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
-        a[h][i] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4 *>(&xs[cur][swz(wm * TM + 16 * i + lr, 4 * h + lc)]));
+        a[h][i] = *reinterpret_cast<const uint4 *>(&xs[cur][swz(wm * TM + 16 * i + lr, 4 * h + lc)]);
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        b[h][j] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const uint4 *>(&ws[cur][swz(wn * TN + 16 * j + lr, 4 * h + lc)]));
+        b[h][j] = *reinterpret_cast<const uint4 *>(&ws[cur][swz(wn * TN + 16 * j + lr, 4 * h + lc)]);
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<CT>(a[h][i], b[h][j], acc[i][j]);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(kCodeLoads));
     __syncthreads();
   }
@@ -298,10 +316,11 @@ void gemm_kernel(GemmArgs args) {
   // 4 (l / 16) + r. Stores go through a buffer resource: rows past M and
   // columns past N get an out-of-range offset and are dropped. The bias of
   // the lane's columns (loaded before the K walk) is added in fp32.
-  constexpr uint32_t kOut = OUT_BF16 ? 2u : 4u;
+  constexpr uint32_t kOut = OUT == kFP32 ? 4u : 2u;
+  const uint32_t ldy = args.ldy;
   const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((char *)args.y + (int64_t)m0 * N * kOut), (short)0,
-      (int)((uint32_t)x_rows * (uint32_t)N * kOut), kBufferFlags);
+      (void *)((char *)args.y + (int64_t)m0 * ldy * kOut), (short)0,
+      (int)(((uint32_t)(x_rows - 1) * ldy + (uint32_t)N) * kOut), kBufferFlags);
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -310,13 +329,12 @@ void gemm_kernel(GemmArgs args) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = wm * TM + 16 * i + 4 * (lane >> 4) + r;  // row within the tile
-        const uint32_t off = n < N ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * kOut : kOOB;
+        const uint32_t off = (n < N && m < x_rows) ? ((uint32_t)m * ldy + (uint32_t)n) * kOut : kOOB;
         // (a scalar copy first: a bit cast of a vector element directly
         // has been compiled as a cast of element 0)
         const float v = has_bias ? acc[i][j][r] + bias_n[j] : acc[i][j][r];
-        if (OUT_BF16)
-          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(pack_bf16x2(v, 0.0f) & 0xffffu), yrs,
-                                                (int)off, 0, 0);
+        if (OUT != kFP32)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<OUT>(v), yrs, (int)off, 0, 0);
         else
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), yrs, (int)off, 0,
                                                 0);
@@ -324,30 +342,51 @@ void gemm_kernel(GemmArgs args) {
     }
 }
 
-template <bool DQ, bool SQ>
-hipError_t launch_cfg(const GemmArgs &args, int grid, bool out_bf16, hipStream_t stream) {
-  if (out_bf16)
-    hipLaunchKernelGGL((gemm_kernel<DQ, SQ, true>), dim3(grid), dim3(kThreads), 0, stream, args);
+template <int DQ, bool SQ, int CT>
+hipError_t launch_cfg(const GemmArgs &args, int grid, int out_dtype, hipStream_t stream) {
+  if (out_dtype == kFP32)
+    hipLaunchKernelGGL((gemm_kernel<DQ, SQ, kFP32, CT>), dim3(grid), dim3(kThreads), 0, stream, args);
+  else if (out_dtype == kFP16)
+    hipLaunchKernelGGL((gemm_kernel<DQ, SQ, kFP16, CT>), dim3(grid), dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL((gemm_kernel<DQ, SQ, false>), dim3(grid), dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL((gemm_kernel<DQ, SQ, kBF16, CT>), dim3(grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();
+}
+
+template <int CT>
+hipError_t launch_ct(const GemmArgs &args, int grid, int out_dtype, int blocksize,
+                     hipStream_t stream) {
+  const ScaleArgs &sc = args.sc;
+  if (!sc.double_quant) return launch_cfg<kDqNone, false, CT>(args, grid, out_dtype, stream);
+  // a tile's scales fit in LDS: at most kQStage blocks, and the groups they
+  // touch (one more than they fill, at most) within kGStage
+  const int64_t tile_blocks = (int64_t)BN * (args.K / blocksize);
+  const int64_t groups = tile_blocks / (1 << sc.log2_bs2) + 2;
+  const bool sq = tile_blocks <= kQStage && groups <= kGStage;
+  if (sc.double_quant == kDqCentred)
+    return sq ? launch_cfg<kDqCentred, true, CT>(args, grid, out_dtype, stream)
+              : launch_cfg<kDqCentred, false, CT>(args, grid, out_dtype, stream);
+  return sq ? launch_cfg<kDqSym, true, CT>(args, grid, out_dtype, stream)
+            : launch_cfg<kDqSym, false, CT>(args, grid, out_dtype, stream);
 }
 
 }  // namespace
 
-hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
-                       int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
-                       void *y, const uint16_t *bias, hipStream_t stream) {
+hipError_t launch_gemm(const void *x, int64_t ldx, int M, const uint8_t *packed, int N, int K,
+                       int blocksize, int quant_type, const ScaleArgs &sc, int compute_dtype,
+                       int out_dtype, void *y, int64_t ldy, const void *bias, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const CodeTables &t = code_tables(quant_type);
   GemmArgs args;
-  args.x = x;
+  args.x = static_cast<const uint16_t *>(x);
   args.packed = packed;
   args.y = y;
-  args.bias = bias;
+  args.bias = static_cast<const uint16_t *>(bias);
   args.M = M;
   args.N = N;
   args.K = K;
+  args.ldx = (uint32_t)ldx;
+  args.ldy = (uint32_t)ldy;
   args.log2_bs = __builtin_ctz((unsigned)blocksize);
   args.sc = sc;
   args.m_tiles = (M + BM - 1) / BM;
@@ -355,14 +394,8 @@ hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, i
   for (int i = 0; i < 16; ++i) args.value[i] = t.value[i];
   const int64_t grid = (int64_t)args.m_tiles * args.n_tiles;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  if (!sc.double_quant) return launch_cfg<false, false>(args, (int)grid, out_bf16, stream);
-  // a tile's scales fit in LDS: at most kQStage blocks, and the groups they
-  // touch (one more than they fill, at most) within kGStage
-  const int64_t tile_blocks = (int64_t)BN * (K / blocksize);
-  const int64_t groups = tile_blocks / (1 << sc.log2_bs2) + 2;
-  if (tile_blocks <= kQStage && groups <= kGStage)
-    return launch_cfg<true, true>(args, (int)grid, out_bf16, stream);
-  return launch_cfg<true, false>(args, (int)grid, out_bf16, stream);
+  if (compute_dtype == kFP16) return launch_ct<kFP16>(args, (int)grid, out_dtype, blocksize, stream);
+  return launch_ct<kBF16>(args, (int)grid, out_dtype, blocksize, stream);
 }
 
 }  // namespace nf4

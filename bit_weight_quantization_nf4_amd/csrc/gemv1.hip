@@ -497,10 +497,10 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
     const GemvDesc &d = descs[i];
     if (d.N == 0) continue;
     Gemv1Problem &p = args.p[args.count++];
-    p.x = d.x;
+    p.x = static_cast<const uint16_t *>(d.x);
     p.packed = d.packed;
     p.y = d.y;
-    p.bias = d.bias;
+    p.bias = static_cast<const uint16_t *>(d.bias);
     p.absmax = d.sc.absmax;
     p.absmax_q = d.sc.absmax_q;
     p.absmax_scale = d.sc.absmax_scale;

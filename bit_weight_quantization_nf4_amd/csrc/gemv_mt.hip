@@ -1,0 +1,430 @@
+// gemv_mt.hip -- decode products y_i[M, N_i] = x_i[M, K] . cd(dequant(W_i))^T
+// for 1 <= M <= 64 on gfx950 matrix cores, one or several independent
+// problems (sharing M and K) per launch; cd is the rounding to the compute
+// dtype (bf16 or fp16).
+//
+// [repo page ossradar.top bitsandbytes, release notes 0.50.0: 4-bit inference
+//  at batch 2..64 uses a fused 4-bit dequantize + GEMM in place of dequantize
+//  + F.linear, with nested (double) quantization and the bias fused in, the
+//  kernel chosen at run time from the shape; usage page icman.com.cn/news/48546,
+//  "Configuration": weights are dequantized to the compute dtype before the
+//  product.]
+//
+// Design (HBM-bound below M ~ 64: every 4-bit weight is read once):
+//  - work items are 16 NT weight rows of one problem; a persistent workgroup
+//    of W waves (one per CU) takes items blockIdx.x, + gridDim.x, ... and its
+//    waves split K into W fixed contiguous ranges of 128-code chunks, so every
+//    output is summed in the same order whatever the grouping, NT or grid;
+//  - v_mfma_f32_16x16x32 with x as the A operand (rows m >= M read zeros) and
+//    the dequantized weights as B. Lane (n, kg) = (l % 16, l / 16) loads the 32
+//    codes k0 + 32 kg .. + 31 of row n of a chunk (16 bytes) and feeds four
+//    MFMAs, one per 8-code word; the x fragments are loaded with the same k
+//    permutation, so the order of k inside a chunk does not matter;
+//  - a "unit" is one chunk of the wave's range for the NT row tiles of an item:
+//    its code words, block-scale parts and x fragments. Each wave walks its
+//    units item after item through a ring of D register sets, issuing unit
+//    u + D - 1 before computing unit u; the ring runs on across item ends, so
+//    the loads of the next item are in flight while an item's partial sums
+//    are combined. Every unit issues the same loads (past the wave's last unit,
+//    or past K, the offsets are out of range and read zeros without a memory
+//    access), so the compiler's waits count exactly one unit's loads;
+//  - dequantization through the conflict-free LDS pair table (entry = fp32
+//    code values of both nibbles of a code byte, 32 interleaved copies, the
+//    address built by one v_perm_b32), times the block scale, rounded to the
+//    compute dtype in pairs;
+//  - at an item's end the W partial tiles meet in LDS and are added in wave
+//    order, then the optional bias (compute dtype) is added in fp32 and the
+//    result rounded to the output dtype and stored (row stride ldy).
+#include <limits.h>
+
+#include "nf4_internal.h"
+
+namespace nf4 {
+namespace {
+
+constexpr int kChunk = 128;              // codes of one row per unit
+constexpr int kCopies = 32;              // interleaved copies of the pair table
+constexpr int kTableBytes = 256 * 256;   // 256 entries x 256-byte rows
+constexpr int kMaxGroup = 16;
+constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer resource (gfx9)
+constexpr uint32_t kOOB = 0x80000000u;    // an offset past every buffer's range
+
+struct MtProblem {
+  const char *x;          // activations (compute dtype), row m at m * ldx_bytes
+  const uint8_t *packed;
+  char *y;                // output, row m at m * ldy_bytes
+  const char *bias;       // [N] compute dtype, or null
+  const float *absmax;    // absmax (no double quant) or absmax_scale
+  const int8_t *absmax_q;
+  const float *absmax_offset;
+  int32_t N;
+  int32_t item_begin;     // first work item of the problem
+  int32_t log2_bs, log2_bs2;
+  uint32_t ldx_bytes, ldy_bytes;
+  uint32_t x_bytes, y_bytes;  // ranges of x and y
+};
+
+struct MtArgs {
+  int32_t item_begin[kMaxGroup];  // first item of each problem; unused: INT_MAX
+  MtProblem p[kMaxGroup];
+  int32_t count, M, K, total_items;
+  int32_t out_dtype;
+  float value[16];
+};
+
+// 8 codes of one packed word -> 4 packed pairs of the compute type, in k order
+// (byte j holds element 2j in its high nibble and 2j + 1 in its low nibble).
+template <int CT>
+__device__ __forceinline__ uint4 dequant8(uint32_t word, float ap, const char *tbl,
+                                          uint32_t lane_base) {
+  uint32_t out[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // address bytes: [0] lane_base (8 * copy), [1] code byte j, [2..3] zero
+    const uint32_t addr = __builtin_amdgcn_perm(word, lane_base, 0x0c0c0000u | ((4u + j) << 8));
+    const f32x2 c = *reinterpret_cast<const f32x2 *>(tbl + addr);
+    out[j] = pack2<CT>(c.x * ap, c.y * ap);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+template <int MT, int NT, int PER>
+struct Unit {
+  uint4 w[NT];        // 32 codes of row 16 t + n
+  int32_t q[NT];      // int8 block code (double quant)
+  float s[NT];        // absmax, or the group scale s2
+  float mu[NT];       // group offset (mean-centred double quant)
+  uint4 xa[MT][4];    // x[16 mt + n][k0 + 32 kg + 8 s .. + 7]
+  uint32_t bias[PER]; // bias bits of the outputs this thread stores at the item's end
+};
+
+template <int W, int MT, int NT, int DQ, int CT>
+__global__ __launch_bounds__(64 * W) void gemv_mt_kernel(MtArgs args) {
+  constexpr int D = 2;  // units in the ring
+  __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
+  __shared__ __attribute__((aligned(16))) float red[W * NT * MT * 4 * 64];
+  __shared__ float vals[16];
+
+  if (threadIdx.x < 16) vals[threadIdx.x] = args.value[threadIdx.x];
+  __syncthreads();
+  // pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy;
+  // consecutive threads write consecutive copies
+  for (int idx = threadIdx.x; idx < 256 * kCopies; idx += 64 * W) {
+    const int e = idx >> 5;
+    const f32x2 v = {vals[e >> 4], vals[e & 15]};
+    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * (idx & 31)) = v;
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n = lane & 15, kg = lane >> 4;
+  const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
+  const int M = args.M, K = args.K;
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int c0 = (wave * nch) / W, c1 = ((wave + 1) * nch) / W;
+  const int items = args.total_items;
+  const int I = (int)blockIdx.x < items ? (items - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+  const uint32_t row_bytes = (uint32_t)K >> 1;
+
+  int ib[kMaxGroup];
+#pragma unroll
+  for (int k = 0; k < kMaxGroup; ++k) ib[k] = args.item_begin[k];
+  // problem of an item: a short compare chain over the first items (scalar;
+  // the array is never indexed by a computed value, which would move it to
+  // vector registers)
+  auto problem_of = [&](int item) {
+    int p = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxGroup; ++k) p = ib[k] <= item ? k : p;
+    return p;
+  };
+
+  // outputs of the item's end: thread t stores output o = t + 64 W j
+  constexpr int kOuts = NT * MT * 256;
+  constexpr int kPer = (kOuts + 64 * W - 1) / (64 * W);
+
+  // Loads of unit (item ordinal i of this workgroup, chunk c). Past the
+  // workgroup's items every offset is out of range. Every unit also fetches
+  // the bias of the outputs this thread stores at an item's end (used after
+  // the item's last unit): a load issued there would be the newest in flight,
+  // and waiting for it would drain the ring.
+  auto issue = [&](int i, int c) {
+    Unit<MT, NT, kPer> u;
+    const bool valid = i < I;
+    const int item = (int)blockIdx.x + (valid ? i : 0) * (int)gridDim.x;
+    const int p = problem_of(item);
+    const MtProblem &P = args.p[p];
+    const int row0 = (item - P.item_begin) * 16 * NT;
+    const int rows = P.N - row0 < 16 * NT ? P.N - row0 : 16 * NT;
+    const int k0 = c * kChunk + 32 * kg;
+    const bool kok = valid && k0 < K;
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.packed + (int64_t)row0 * row_bytes), (short)0, (int)((uint32_t)rows * row_bytes),
+        kBufferFlags);
+    // the item's first block, and its group split into a group base and the
+    // block's place in that group (64-bit safe)
+    const uint64_t blk0 = ((uint64_t)row0 * (uint64_t)K) >> P.log2_bs;
+    const uint32_t nblk = ((uint32_t)rows * (uint32_t)K) >> P.log2_bs;
+    const uint64_t g0 = DQ ? blk0 >> P.log2_bs2 : 0;
+    const uint32_t blk_in = DQ ? (uint32_t)(blk0 & ((1ull << P.log2_bs2) - 1)) : 0;
+    const uint32_t ngr = DQ ? (blk_in + nblk + (1u << P.log2_bs2) - 1) >> P.log2_bs2 : 0;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.absmax + (DQ ? g0 : blk0)), (short)0, (int)(4u * (DQ ? ngr : nblk)),
+        kBufferFlags);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(DQ ? (const void *)(P.absmax_q + blk0) : (const void *)P.absmax), (short)0,
+        (int)(DQ ? nblk : 0u), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(DQ == kDqCentred ? P.absmax_offset + g0 : P.absmax), (short)0,
+        (int)(DQ == kDqCentred ? 4u * ngr : 0u), kBufferFlags);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t r = (uint32_t)(16 * t + n);
+      u.w[t] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     wrs, (int)(kok ? r * row_bytes + ((uint32_t)k0 >> 1) : kOOB), 0, 0));
+      const uint32_t b = (r * (uint32_t)K + (uint32_t)k0) >> P.log2_bs;  // block in the item
+      if (DQ == kDqNone) {
+        u.q[t] = 1;
+        u.mu[t] = 0.0f;
+        u.s[t] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(kok ? 4u * b : kOOB), 0, 0));
+      } else {
+        const uint32_t g = (blk_in + b) >> P.log2_bs2;
+        u.q[t] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)(kok ? b : kOOB), 0, 0);
+        u.s[t] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(kok ? 4u * g : kOOB), 0, 0));
+        if (DQ == kDqCentred)
+          u.mu[t] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(mrs, (int)(kok ? 4u * g : kOOB), 0, 0));
+        else
+          u.mu[t] = 0.0f;
+      }
+    }
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)P.x, (short)0, (int)P.x_bytes, kBufferFlags);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = 16 * mt + n;
+      const uint32_t off = (kok && m < M) ? (uint32_t)m * P.ldx_bytes + 2u * (uint32_t)k0 : kOOB;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        u.xa[mt][s] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(off + 16u * s), 0, 0));
+    }
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)P.bias, (short)0, P.bias != nullptr ? (int)(2u * (uint32_t)P.N) : 0, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = (int)threadIdx.x + 64 * W * j;
+      const int row = row0 + 16 * ((o >> 8) / MT) + (o & 15);
+      u.bias[j] = __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)row), 0, 0);
+    }
+    return u;
+  };
+
+  f32x4 acc[NT][MT];
+  auto zero = [&]() {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  auto compute = [&](const Unit<MT, NT, kPer> &u) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float ap = scale_from<DQ>(u.q[t], u.s[t], u.mu[t]);
+      const uint32_t wd[4] = {u.w[t].x, u.w[t].y, u.w[t].z, u.w[t].w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint4 b = dequant8<CT>(wd[s], ap, tbl, lane_base);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32<CT>(u.xa[mt][s], b, acc[t][mt]);
+      }
+    }
+  };
+
+  // The end of item ordinal i: partial tiles through LDS, added in wave order
+  // by the threads that own the outputs, bias, rounding and store.
+  auto finish = [&](int i, const uint32_t (&bias_bits)[kPer]) {
+    const int item = (int)blockIdx.x + i * (int)gridDim.x;
+    const int p = problem_of(item);
+    const MtProblem &P = args.p[p];
+    const int row0 = (item - P.item_begin) * 16 * NT;
+    const bool has_bias = P.bias != nullptr;
+    __syncthreads();  // the previous item's sums have been read
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          red[(((wave * NT + t) * MT + mt) * 4 + r) * 64 + lane] = acc[t][mt][r];
+    __syncthreads();
+    const int ob = args.out_dtype == kFP32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)P.y, (short)0, (int)P.y_bytes, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = (int)threadIdx.x + 64 * W * j;
+      if (kOuts % (64 * W) != 0 && o >= kOuts) break;
+      const int l = o & 63, r = (o >> 6) & 3, mt = (o >> 8) % MT, t = (o >> 8) / MT;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) sum += red[(((w * NT + t) * MT + mt) * 4 + r) * 64 + l];
+      if (has_bias) sum += widen16<CT>(bias_bits[j]);
+      // D layout of the 16x16 MFMA: lane l holds rows 4 (l / 16) + r of column l % 16
+      const int m = 16 * mt + 4 * (l >> 4) + r;
+      const int row = row0 + 16 * t + (l & 15);
+      const uint32_t off = (m < M && row < P.N)
+                               ? (uint32_t)m * P.ldy_bytes + (uint32_t)row * (uint32_t)ob
+                               : kOOB;
+      if (args.out_dtype == kFP32)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), yrs, (int)off, 0, 0);
+      else if (args.out_dtype == kFP16)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<kFP16>(sum), yrs, (int)off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<kBF16>(sum), yrs, (int)off, 0, 0);
+    }
+  };
+
+  zero();
+  __syncthreads();  // table built
+  if (c1 == c0) {
+    // no chunks for this wave (K below W chunks): zero partials, same barriers
+    // (a unit of chunk 0 fetches the bias; its codes are not used)
+    for (int i = 0; i < I; ++i) {
+      const Unit<MT, NT, kPer> u = issue(i, 0);
+      finish(i, u.bias);
+    }
+    return;
+  }
+  // issue pointer (item ordinal, chunk) runs D - 1 units ahead of the compute
+  // pointer
+  int is_i = 0, is_c = c0;
+  auto advance = [&]() {
+    if (++is_c == c1) {
+      is_c = c0;
+      ++is_i;
+    }
+  };
+  Unit<MT, NT, kPer> ring[D];
+#pragma unroll
+  for (int j = 0; j < D - 1; ++j) {
+    ring[j] = issue(is_i, is_c);
+    advance();
+  }
+  const int U = I * (c1 - c0);
+  int cu_i = 0, cu_c = c0;
+  for (int u0 = 0; u0 < U; u0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      ring[(j + D - 1) % D] = issue(is_i, is_c);
+      advance();
+      if (u0 + j < U) {
+        compute(ring[j]);
+        if (++cu_c == c1) {
+          finish(cu_i, ring[j].bias);
+          zero();
+          cu_c = c0;
+          ++cu_i;
+        }
+      }
+    }
+  }
+}
+
+template <int W, int MT, int NT, int DQ>
+hipError_t launch_ct(const MtArgs &args, int grid, int ct, hipStream_t stream) {
+  if (ct == kFP16)
+    hipLaunchKernelGGL((gemv_mt_kernel<W, MT, NT, DQ, kFP16>), dim3(grid), dim3(64 * W), 0, stream,
+                       args);
+  else
+    hipLaunchKernelGGL((gemv_mt_kernel<W, MT, NT, DQ, kBF16>), dim3(grid), dim3(64 * W), 0, stream,
+                       args);
+  return hipGetLastError();
+}
+
+template <int W, int MT, int NT>
+hipError_t launch_dq(const MtArgs &args, int grid, int dq, int ct, hipStream_t stream) {
+  if (dq == kDqCentred) return launch_ct<W, MT, NT, kDqCentred>(args, grid, ct, stream);
+  if (dq == kDqSym) return launch_ct<W, MT, NT, kDqSym>(args, grid, ct, stream);
+  return launch_ct<W, MT, NT, kDqNone>(args, grid, ct, stream);
+}
+
+// items of 16 nt rows over the launch's problems
+int count_items(int count, const GemvDesc *descs, int nt) {
+  int items = 0;
+  for (int i = 0; i < count; ++i) items += (descs[i].N + 16 * nt - 1) / (16 * nt);
+  return items;
+}
+
+}  // namespace
+
+int gemv_max_group() { return kMaxGroup; }
+
+hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int quant_type, int dq,
+                          int compute_dtype, int out_dtype, hipStream_t stream) {
+  if (count == 0 || M == 0) return hipSuccess;
+  if (count > kMaxGroup || M > 64) return hipErrorInvalidValue;
+  const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  // row tiles per item: the most (fewer x fragment loads per weight byte) that
+  // still leave every CU a few items; the register budget caps it (4 waves
+  // per SIMD at MT = 1 leave 128 registers: NT = 4 would spill)
+  const int cu = device_cu_count();
+  const int nt_max = MT == 2 ? 4 : 2;
+  int nt = 1;
+  for (int c = 2; c <= nt_max; c *= 2)
+    if (count_items(count, descs, c) >= 3 * cu) nt = c;
+  const CodeTables &tb = code_tables(quant_type);
+  MtArgs args;
+  args.count = 0;
+  args.M = M;
+  args.K = K;
+  args.out_dtype = out_dtype;
+  const uint32_t xe = compute_dtype == kFP32 ? 4u : 2u;
+  const uint32_t ye = out_dtype == kFP32 ? 4u : 2u;
+  int items = 0;
+  for (int i = 0; i < kMaxGroup; ++i) args.item_begin[i] = INT_MAX;
+  for (int i = 0; i < count; ++i) {
+    const GemvDesc &d = descs[i];
+    if (d.N == 0) continue;
+    const int k = args.count++;
+    MtProblem &p = args.p[k];
+    p.x = static_cast<const char *>(d.x);
+    p.packed = d.packed;
+    p.y = static_cast<char *>(d.y);
+    p.bias = static_cast<const char *>(d.bias);
+    p.absmax = dq ? d.sc.absmax_scale : d.sc.absmax;
+    p.absmax_q = d.sc.absmax_q;
+    p.absmax_offset = d.sc.absmax_offset;
+    p.N = d.N;
+    p.log2_bs = __builtin_ctz((unsigned)d.blocksize);
+    p.log2_bs2 = d.sc.log2_bs2;
+    p.ldx_bytes = (uint32_t)(d.ldx * xe);
+    p.ldy_bytes = (uint32_t)(d.ldy * ye);
+    p.x_bytes = (uint32_t)(((int64_t)(M - 1) * d.ldx + K) * xe);
+    p.y_bytes = (uint32_t)(((int64_t)(M - 1) * d.ldy + d.N) * ye);
+    args.item_begin[k] = items;
+    p.item_begin = items;
+    items += (d.N + 16 * nt - 1) / (16 * nt);
+  }
+  if (args.count == 0) return hipSuccess;
+  args.total_items = items;
+  for (int i = 0; i < 16; ++i) args.value[i] = tb.value[i];
+  const int grid = items < cu ? items : cu;
+  if (MT == 1) {
+    if (nt == 2) return launch_dq<16, 1, 2>(args, grid, dq, compute_dtype, stream);
+    return launch_dq<16, 1, 1>(args, grid, dq, compute_dtype, stream);
+  }
+  if (MT == 2) {
+    if (nt == 4) return launch_dq<8, 2, 4>(args, grid, dq, compute_dtype, stream);
+    if (nt == 2) return launch_dq<8, 2, 2>(args, grid, dq, compute_dtype, stream);
+    return launch_dq<8, 2, 1>(args, grid, dq, compute_dtype, stream);
+  }
+  if (nt == 2) return launch_dq<8, 4, 2>(args, grid, dq, compute_dtype, stream);
+  return launch_dq<8, 4, 1>(args, grid, dq, compute_dtype, stream);
+}
+
+}  // namespace nf4

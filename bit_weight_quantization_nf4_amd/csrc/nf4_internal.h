@@ -15,6 +15,19 @@ hipError_t launch_quantize(const uint16_t *w, int64_t n, int blocksize, int quan
 hipError_t launch_double_quant(const float *absmax, int64_t nb, int blocksize2, int8_t *q,
                                float *s2, hipStream_t stream);
 
+// The mean-centred second level (offsets mu per group of blocksize2 scales).
+hipError_t launch_double_quant_centred(const float *absmax, int64_t nb, int blocksize2, int8_t *q,
+                                       float *s2, float *mu, hipStream_t stream);
+
+// Quantization of a [rows, cols] matrix of bf16 / fp16 / fp32 elements whose
+// rows start ld elements apart (any blocksize), as the flattened row-major
+// tensor; absmax only (double quantization is a second launch). The code
+// decisions use the correctly rounded quotient, so a contiguous bf16 input
+// gives bitwise the codes of launch_quantize.
+hipError_t launch_quantize_generic(const void *w, int w_dtype, int64_t rows, int64_t cols,
+                                   int64_t ld, int blocksize, int quant_type, uint8_t *packed,
+                                   float *absmax, hipStream_t stream);
+
 // One tensor of a quantization launch (absmax_q / absmax_scale used with
 // double quantization only).
 struct QuantTensorDesc {
@@ -45,32 +58,35 @@ struct DequantDesc {
 };
 
 // Dequantization of up to dequantize_max_group() tensors in one launch; they
-// share the quant type, the double-quant flag and the output dtype. Each
-// tensor's output equals what it gets launched alone.
+// share the quant type, the double-quant mode and the output dtype (kBF16,
+// kFP16 or kFP32). Each tensor's output equals what it gets launched alone.
 int dequantize_max_group();
-hipError_t launch_dequantize(int count, const DequantDesc *ds, int quant_type, bool double_quant,
-                             bool out_bf16, hipStream_t stream);
+hipError_t launch_dequantize(int count, const DequantDesc *ds, int quant_type, int dq,
+                             int out_dtype, hipStream_t stream);
 
 // One decode product of a group launched together by launch_gemv_grouped.
 struct GemvDesc {
-  const uint16_t *x;      // [M, K] bf16
+  const void *x;          // [M, K] in the compute dtype, row m at m * ldx elements
   const uint8_t *packed;  // [N*K/2]
-  void *y;                // [M, N]
+  void *y;                // [M, N] in the output dtype, row m at m * ldy elements
   ScaleArgs sc;
   int32_t N, K, blocksize;
-  const uint16_t *bias;   // [N] bf16, added in fp32 before the output rounding; or null
+  const void *bias;       // [N] in the compute dtype, added in fp32 before the output rounding; or null
+  int64_t ldx, ldy;
 };
 
 // Largest number of products in one grouped launch.
 int gemv_max_group();
 
-// All products share M, the quant type (one code table) and the double-quant
-// flag; blocksizes and shapes may differ.
-hipError_t launch_gemv_grouped(int count, const GemvDesc *descs, int M, int quant_type,
-                               bool double_quant, bool out_bf16, hipStream_t stream);
+// Decode products (1 <= M <= 64) on the matrix cores. All products share M,
+// K, the compute dtype (bf16 / fp16), the output dtype, the quant type (one
+// code table) and the double-quant mode; blocksizes and N may differ. A
+// product's result depends only on its own data, M and K.
+hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int quant_type, int dq,
+                          int compute_dtype, int out_dtype, hipStream_t stream);
 
 // Single-activation-row products (M = 1) for K <= gemv1_max_k(): waves own
-// whole rows; same grouping rules as launch_gemv_grouped.
+// whole rows; same grouping rules (contiguous x and y).
 int gemv1_max_k();
 hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type,
                                 bool double_quant, bool out_bf16, hipStream_t stream);
@@ -78,9 +94,17 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
-// bias: [N] bf16 added in fp32 before the output rounding, or null
-hipError_t launch_gemm(const uint16_t *x, int M, const uint8_t *packed, int N, int K,
-                       int blocksize, int quant_type, const ScaleArgs &sc, bool out_bf16,
-                       void *y, const uint16_t *bias, hipStream_t stream);
+// Prefill GEMM, any M, compute dtype bf16 or fp16 (x, bias), output dtype
+// kBF16 / kFP16 / kFP32; x rows ldx elements apart, y rows ldy apart.
+// bias: [N] in the compute dtype, added in fp32 before the output rounding,
+// or null.
+hipError_t launch_gemm(const void *x, int64_t ldx, int M, const uint8_t *packed, int N, int K,
+                       int blocksize, int quant_type, const ScaleArgs &sc, int compute_dtype,
+                       int out_dtype, void *y, int64_t ldy, const void *bias, hipStream_t stream);
+
+// Products in the fp32 compute dtype (weights RN(c a') kept in fp32, fp32
+// activations and bias, fp32 accumulation), any M; same descriptor rules.
+hipError_t launch_matmul_f32(const GemvDesc &d, int M, int quant_type, int out_dtype,
+                             hipStream_t stream);
 
 }  // namespace nf4

@@ -637,6 +637,162 @@ QuantArgs make_args(int count, const QuantTensorDesc *ts, int blocksize, int qua
   return args;
 }
 
+// ---- general inputs: bf16 / fp16 / fp32 elements, row-strided matrices ---
+// [repo page, release notes 0.49.2: quantize accepts non-contiguous tensors;
+//  usage page, Core Usage 3: Linear4bit quantizes fp16 or bf16 weights.]
+// The flattened row-major element e of a [rows, cols] matrix with row stride
+// ld lives at e + (e / cols) (ld - cols); with a stride, cols % 8 == 0, so the
+// 8 elements a lane takes lie in one row. Each element is widened exactly to
+// fp32, s = x / a is the correctly rounded IEEE quotient (no reciprocal
+// shortcut: that equality is shown for bf16 pairs only), and its code comes
+// from the same cell lookup, which is exact for every fp32 s in [-1, 1].
+// A wave owns tiles of max(bs, 512) elements; lane l takes elements 512 j +
+// 8 l .. + 7 of its tile.
+template <int DT>
+__device__ __forceinline__ void load8_elems(float (&x)[8], const void *w, int64_t off, int valid) {
+  if (DT == kFP32) {
+    const float *p = static_cast<const float *>(w) + off;
+    if (valid == 8) {
+      const float4 a = *reinterpret_cast<const float4 *>(p);
+      const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = j < valid ? p[j] : 0.0f;
+    }
+  } else {
+    const uint16_t *p = static_cast<const uint16_t *>(w) + off;
+    uint16_t h[8];
+    if (valid == 8) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(p);
+      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        h[2 * j] = (uint16_t)(d[j] & 0xffffu);
+        h[2 * j + 1] = (uint16_t)(d[j] >> 16);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) h[j] = j < valid ? p[j] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = DT == kFP16 ? widen16<kFP16>(h[j]) : widen16<kBF16>(h[j]);
+  }
+}
+
+// code of s through the cell lookup: the one threshold inside s's cell
+// decides between the codes below and above it
+__device__ __forceinline__ uint32_t code_of(float s, const uint2 *lut) {
+  const uint2 e = cell_of(s, lut);
+  return s > __uint_as_float(e.x) ? (e.y >> 8) & 0xfu : e.y & 0xfu;
+}
+
+template <int DT, int BS>
+__global__ __launch_bounds__(kThreads) void quantize_generic_kernel(
+    const void *w, int64_t n, int64_t cols, int64_t ld, uint8_t *packed, float *absmax,
+    int64_t ntiles, QuantArgs args) {
+  constexpr int kTile = BS > 512 ? BS : 512;
+  constexpr int P = kTile / 512;   // 8-element pieces per lane
+  constexpr int G = BS >= 512 ? 64 : BS / 8;  // lanes per block within a piece
+  __shared__ uint2 lut[kLutSize];
+  __shared__ uint32_t recip[128];
+  load_tables(lut, recip, args);
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
+  const int64_t nb = (n + BS - 1) / BS;
+  const bool strided = ld != cols;
+  for (int64_t tile = wave; tile < ntiles; tile += nwaves) {
+    float x[P][8];
+    int64_t e0[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      e0[j] = tile * kTile + 512 * j + 8 * lane;
+      const int64_t rem = n - e0[j];
+      const int valid = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
+      int64_t off = e0[j];
+      if (strided && valid > 0) {
+        const int64_t row = e0[j] / cols;
+        off = row * ld + (e0[j] - row * cols);
+      }
+      if (valid > 0) load8_elems<DT>(x[j], w, off, valid);
+      else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[j][k] = 0.0f;
+      }
+    }
+    // block maxima: within a piece for bs <= 512, over the whole tile beyond
+    float m[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      float v = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v = fmaxf(v, fabsf(x[j][k]));
+      m[j] = v;
+    }
+    if (BS > 512) {
+      float v = m[0];
+#pragma unroll
+      for (int j = 1; j < P; ++j) v = fmaxf(v, m[j]);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+#pragma unroll
+      for (int j = 0; j < P; ++j) m[j] = v;
+      if (lane == 0 && tile < nb) absmax[tile] = v;
+    } else {
+#pragma unroll
+      for (int j = 0; j < P; ++j) {
+        // |x| >= 0, so the fp32 bit patterns order like the values
+        m[j] = __uint_as_float(group_max<G>(__float_as_uint(m[j])));
+        const int64_t b = e0[j] / BS;
+        if (lane % G == 0 && b < nb) absmax[b] = m[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const float a = m[j];
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float sv = a == 0.0f ? 0.0f : x[j][k] / a;
+        const uint32_t c = code_of(sv, lut);
+        // byte k / 2: element 2i in the high nibble, 2i + 1 in the low one
+        word |= c << (8 * (k >> 1) + ((k & 1) ? 0 : 4));
+      }
+      QTensor T;
+      T.packed = packed;
+      T.n = n;
+      store_codes(T, e0[j], word);
+    }
+  }
+}
+
+template <int DT>
+hipError_t launch_generic_dt(const void *w, int64_t n, int64_t cols, int64_t ld, int blocksize,
+                             uint8_t *packed, float *absmax, int64_t ntiles, dim3 grid,
+                             const QuantArgs &args, hipStream_t stream) {
+  switch (blocksize) {
+#define NF4_QGCASE(BSV)                                                                          \
+  case BSV:                                                                                      \
+    hipLaunchKernelGGL((quantize_generic_kernel<DT, BSV>), grid, dim3(kThreads), 0, stream, w, n, \
+                       cols, ld, packed, absmax, ntiles, args);                                  \
+    break;
+    NF4_QGCASE(32)
+    NF4_QGCASE(64)
+    NF4_QGCASE(128)
+    NF4_QGCASE(256)
+    NF4_QGCASE(512)
+    NF4_QGCASE(1024)
+    NF4_QGCASE(2048)
+    NF4_QGCASE(4096)
+#undef NF4_QGCASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool quantize_dq_fused(int blocksize, int blocksize2) {
@@ -676,6 +832,34 @@ hipError_t launch_quantize(const uint16_t *w, int64_t n, int blocksize, int quan
   dim3 grid((unsigned)blocks);
   return quant_type == kQuantFP4 ? launch_qt<kQuantFP4>(blocksize, grid, args, stream)
                                  : launch_qt<kQuantNF4>(blocksize, grid, args, stream);
+}
+
+}  // namespace nf4
+
+namespace nf4 {
+
+hipError_t launch_quantize_generic(const void *w, int w_dtype, int64_t rows, int64_t cols,
+                                   int64_t ld, int blocksize, int quant_type, uint8_t *packed,
+                                   float *absmax, hipStream_t stream) {
+  const int64_t n = rows * cols;
+  if (n == 0) return hipSuccess;
+  const QuantTensorDesc one{nullptr, n, packed, absmax, nullptr, nullptr};
+  const QuantArgs args = make_args(1, &one, blocksize, quant_type);
+  const int64_t tile = blocksize > 512 ? blocksize : 512;
+  const int64_t ntiles = (n + tile - 1) / tile;
+  int64_t blocks = (ntiles + (kThreads / 64) - 1) / (kThreads / 64);
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  const dim3 grid((unsigned)blocks);
+  // one row (or a contiguous matrix) is its flattened self
+  const int64_t c = rows > 1 ? cols : n, l = rows > 1 ? ld : n;
+  if (w_dtype == kFP32)
+    return launch_generic_dt<kFP32>(w, n, c, l, blocksize, packed, absmax, ntiles, grid, args,
+                                    stream);
+  if (w_dtype == kFP16)
+    return launch_generic_dt<kFP16>(w, n, c, l, blocksize, packed, absmax, ntiles, grid, args,
+                                    stream);
+  return launch_generic_dt<kBF16>(w, n, c, l, blocksize, packed, absmax, ntiles, grid, args,
+                                  stream);
 }
 
 }  // namespace nf4

@@ -29,7 +29,9 @@
  *    returns a non-zero status and writes nothing.
  *  - bf16 tensors are passed as raw 16-bit patterns (upper half of a binary32).
  *  - Inputs must be finite; NaN/Inf inputs give unspecified codes.
- *  - Every device pointer must be 16-byte aligned (NF4_ERR_MISALIGNED).
+ *  - Every device pointer must be 16-byte aligned (NF4_ERR_MISALIGNED);
+ *    row strides of inputs (the *_ex calls) must keep every row 16-byte
+ *    aligned.
  *  - n == 0 (or M == 0 / N == 0 for the products) is a valid no-op.
  *  - The device must be gfx950 (NF4_ERR_UNSUPPORTED otherwise); with no HIP
  *    device at all the calls return NF4_ERR_DEVICE.
@@ -42,7 +44,8 @@
  *            in bits 3..0; an odd n leaves the last low nibble 0;
  *  - absmax  float[nb]: max |x| over the block's real elements;
  *  - with double quantization, groups of `blocksize2` consecutive absmax values:
- *    absmax_q int8[nb] and absmax_scale float[ceil(nb/blocksize2)];
+ *    absmax_q int8[nb] and absmax_scale float[ceil(nb/blocksize2)], plus
+ *    absmax_offset float[ceil(nb/blocksize2)] in the mean-centred mode;
  *  - NF4 codes are ranks in the ascending 16-value codebook (code 7 is 0);
  *    FP4 codes are E2M1 nibbles (bit 3 sign, bits 2..1 exponent, bit 0
  *    mantissa) of the E2M1 magnitudes divided by 6.
@@ -59,7 +62,11 @@
 extern "C" {
 #endif
 
-#define NF4_ABI_VERSION 1
+#define NF4_ABI_VERSION 2
+
+/* Largest M of the decode products (nf4_gemv, nf4_gemv_grouped); nf4_linear
+ * sends M up to this to the decode kernels and larger M to the GEMM. */
+#define NF4_GEMV_MAX_M 64
 
 typedef enum nf4_status {
   NF4_OK = 0,
@@ -71,22 +78,46 @@ typedef enum nf4_status {
 
 typedef enum nf4_quant_type { NF4_QUANT_NF4 = 0, NF4_QUANT_FP4 = 1 } nf4_quant_type;
 
-typedef enum nf4_dtype { NF4_DTYPE_BF16 = 0, NF4_DTYPE_FP32 = 1 } nf4_dtype;
+/* Element types of activations, outputs, biases and quantize inputs. The
+ * compute dtype of a product is the type the 4-bit weights are dequantized to
+ * before the multiply [usage page, "Configuration": bf16 preferred; fp16 and
+ * fp32 also used; NF4 page, notes 补充说明: NF4 + double quant + FP16 compute]. */
+typedef enum nf4_dtype { NF4_DTYPE_BF16 = 0, NF4_DTYPE_FP32 = 1, NF4_DTYPE_FP16 = 2 } nf4_dtype;
+
+/* Second-level (double) quantization of the block scales [NF4 page, table
+ * 实际性能差异 row 训练稳定性（QLoRA）: the NF4 scales are quantized again to
+ * INT8]. Per group of blocksize2 consecutive absmax values:
+ *  NF4_DQ_SYMMETRIC: m = max a, s2 = RN(m / 127) (0 if m = 0),
+ *                    q = clamp(rint(RN(a / s2)), -127, 127); a' = RN(q s2).
+ *  NF4_DQ_CENTRED:   mu = RN(S / L) with S the pairwise fp32 sum of the
+ *                    group's L values zero-padded to blocksize2 (adjacent
+ *                    pairs first, level by level), D = max |RN(a - mu)|,
+ *                    s2 = RN(D / 127) (0 if D = 0),
+ *                    q = clamp(rint(RN(RN(a - mu) / s2)), -127, 127);
+ *                    a' = RN(RN(q s2) + mu). The codes use both signs. */
+typedef enum nf4_double_quant_mode {
+  NF4_DQ_NONE = 0,
+  NF4_DQ_SYMMETRIC = 1,
+  NF4_DQ_CENTRED = 2
+} nf4_double_quant_mode;
 
 /* Descriptor of one quantized tensor. The pointers are device pointers owned by
- * the caller; `absmax` is read when double_quant == 0, `absmax_q` and
- * `absmax_scale` when double_quant == 1. Mirrors the pages' configuration
- * fields (quant_type, use_double_quant) plus the blocksizes. */
+ * the caller; `absmax` is read when double_quant == NF4_DQ_NONE, `absmax_q`
+ * and `absmax_scale` in both double-quant modes, `absmax_offset` in
+ * NF4_DQ_CENTRED only; fields a mode does not read are ignored. Mirrors the
+ * pages' configuration fields (quant_type, use_double_quant) plus the
+ * blocksizes. */
 typedef struct nf4_qweight {
   const uint8_t *packed;
   const float *absmax;
   const int8_t *absmax_q;
   const float *absmax_scale;
   int64_t n;
-  int32_t blocksize;  /* power of two in [32, 4096] */
-  int32_t quant_type; /* nf4_quant_type */
-  int32_t double_quant;
-  int32_t blocksize2; /* power of two in [64, 4096]; read when double_quant == 1 */
+  int32_t blocksize;    /* power of two in [32, 4096] */
+  int32_t quant_type;   /* nf4_quant_type */
+  int32_t double_quant; /* nf4_double_quant_mode */
+  int32_t blocksize2;   /* power of two in [64, 4096]; read with double quant */
+  const float *absmax_offset; /* [ceil(nb / blocksize2)], NF4_DQ_CENTRED */
 } nf4_qweight;
 
 /* ------------------------------------------------------------ host helpers */
@@ -122,10 +153,29 @@ nf4_status nf4_device_check(void);
  *      absmax_q [nb] and absmax_scale [ceil(nb/256)] (blocksize2 = 256).
  * Per block: a = max|x|; s = RN(x / a) (s = 0 when a = 0); code = nearest
  * codebook value to s, an exact tie going to the smaller value; FP4 encodes
- * zero as nibble 0. absmax_q/absmax_scale may be NULL when double_quant == 0. */
+ * zero as nibble 0. absmax_q/absmax_scale may be NULL when double_quant == 0.
+ * double_quant is NF4_DQ_NONE or NF4_DQ_SYMMETRIC here (nf4_quantize_ex takes
+ * every mode, input type and row stride). */
 nf4_status nf4_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_t quant_type,
                         int32_t double_quant, uint8_t *packed, float *absmax, int8_t *absmax_q,
                         float *absmax_scale, void *stream);
+
+/* The general form of nf4_quantize [NF4 page, table 数学原理对比; repo page
+ * 0.49.2 release notes: quantize/dequantize accept non-contiguous tensors].
+ * In:  w, a [rows, cols] matrix of w_dtype elements (NF4_DTYPE_BF16, FP16 or
+ *      FP32) whose row r starts ld elements after row r - 1 (ld >= cols);
+ *      it is quantized as the flattened row-major tensor of n = rows * cols
+ *      elements, each element taken at its exact fp32 value. A strided
+ *      matrix (ld > cols, rows > 1) needs cols % 8 == 0 (NF4_ERR_UNSUPPORTED
+ *      otherwise) and 16-byte aligned rows.
+ * Out: as nf4_quantize; double_quant is any nf4_double_quant_mode with
+ *      blocksize2 = 256, and absmax_offset [ceil(nb/256)] is written in
+ *      NF4_DQ_CENTRED (it may be NULL otherwise). For a contiguous bf16
+ *      input and double_quant 0 or 1 the result is bitwise nf4_quantize's. */
+nf4_status nf4_quantize_ex(const void *w, int32_t w_dtype, int64_t rows, int64_t cols, int64_t ld,
+                           int32_t blocksize, int32_t quant_type, int32_t double_quant,
+                           uint8_t *packed, float *absmax, int8_t *absmax_q, float *absmax_scale,
+                           float *absmax_offset, void *stream);
 
 /* Double quantization of block scales to 8 bits [NF4 page, table 实际性能差异
  * row 训练稳定性（QLoRA）]. Groups of blocksize2 consecutive absmax values; per
@@ -135,10 +185,20 @@ nf4_status nf4_quantize(const void *w_bf16, int64_t n, int32_t blocksize, int32_
 nf4_status nf4_double_quant(const float *absmax, int64_t nb, int32_t blocksize2, int8_t *absmax_q,
                             float *absmax_scale, void *stream);
 
+/* Double quantization in either mode (nf4_double_quant_mode; see its
+ * comment for the arithmetic). In: absmax [nb]. Out: absmax_q [nb],
+ * absmax_scale [ceil(nb/blocksize2)], and for NF4_DQ_CENTRED absmax_offset
+ * [ceil(nb/blocksize2)] (may be NULL in NF4_DQ_SYMMETRIC, where the call is
+ * nf4_double_quant). mode NF4_DQ_NONE is NF4_ERR_INVALID_ARGUMENT. */
+nf4_status nf4_double_quant_ex(const float *absmax, int64_t nb, int32_t blocksize2, int32_t mode,
+                               int8_t *absmax_q, float *absmax_scale, float *absmax_offset,
+                               void *stream);
+
 /* Dequantization [usage page, Configuration: compute dtype]. Out [w->n] as fp32
- * (out_dtype NF4_DTYPE_FP32: w = RN(c[code] * a')) or bf16 (NF4_DTYPE_BF16:
- * RNE_bf16 of that fp32 value), where a' = absmax, or RN(q * s2) with double
- * quant. */
+ * (out_dtype NF4_DTYPE_FP32: w = RN(c[code] * a')), bf16 (NF4_DTYPE_BF16:
+ * RNE_bf16 of that fp32 value) or fp16 (NF4_DTYPE_FP16: RNE_fp16 of it), where
+ * a' is the block's effective scale (absmax, or the double-quant a' of the
+ * descriptor's mode). */
 nf4_status nf4_dequantize(const nf4_qweight *w, int32_t out_dtype, void *out, void *stream);
 
 /* Largest `count` accepted by nf4_quantize_grouped and nf4_dequantize_grouped. */
@@ -173,13 +233,13 @@ nf4_status nf4_dequantize_grouped(int32_t count, const nf4_qweight *w, int32_t o
 
 /* Decode product for small batches [repo page 0.50.0: 4-bit GEMV and fused
  * 4-bit dequantize + GEMM for batch 1..64]:
- *   y[m, j] = sum_k bf16(dequant(W)[j, k]) * x[m, k],  fp32 accumulation,
- * x bf16 [M, K] row-major, W the quantized [N, K] tensor (w->n == N*K), y [M, N]
- * row-major in out_dtype (bf16 = RNE of the fp32 result). 1 <= M <= 16;
- * K <= 2^26 (NF4_ERR_UNSUPPORTED above).
- * compute_dtype must be NF4_DTYPE_BF16. The reduction order is fixed, so
- * repeated calls give identical bits. */
-nf4_status nf4_gemv(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+ *   y[m, j] = sum_k cd(dequant(W)[j, k]) * x[m, k],  fp32 accumulation,
+ * with cd the rounding to compute_dtype (bf16 or fp16 RNE; none for fp32).
+ * x [M, K] row-major in compute_dtype, W the quantized [N, K] tensor (w->n ==
+ * N*K), y [M, N] row-major in out_dtype (bf16 / fp16 = RNE of the fp32
+ * result). 1 <= M <= NF4_GEMV_MAX_M; K <= 2^26 (NF4_ERR_UNSUPPORTED above).
+ * The reduction order is fixed, so repeated calls give identical bits. */
+nf4_status nf4_gemv(const void *x, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                     int32_t compute_dtype, int32_t out_dtype, void *y, void *stream);
 
 /* Largest `count` accepted by nf4_gemv_grouped. */
@@ -192,40 +252,51 @@ nf4_status nf4_gemv(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t
  *   y[i][m, j] = sum_k bf16(dequant(w[i])[j, k]) * x[i][m, k],
  * with the layouts and rules of nf4_gemv for each product. x_bf16, w, N, K and
  * y are HOST arrays of `count` entries (the tensors they point to are on the
- * device). All products share M (1..16), the quant type and the double-quant
- * flag (NF4_ERR_UNSUPPORTED otherwise); shapes and blocksizes may differ.
+ * device). All products share M (1..NF4_GEMV_MAX_M), the compute dtype, the
+ * quant type and the double-quant mode (NF4_ERR_UNSUPPORTED otherwise); shapes
+ * and blocksizes may differ.
  * 0 <= count <= NF4_GEMV_MAX_GROUP. Each product's result is bitwise the same
  * as nf4_gemv on it alone. */
-nf4_status nf4_gemv_grouped(int32_t count, const void *const *x_bf16, int32_t M,
+nf4_status nf4_gemv_grouped(int32_t count, const void *const *x, int32_t M,
                             const nf4_qweight *w, const int32_t *N, const int32_t *K,
                             int32_t compute_dtype, int32_t out_dtype, void *const *y,
                             void *stream);
 
-/* Prefill product, any M >= 1: the same contraction as nf4_gemv, computed with
- * bf16 matrix cores on dequantized weight tiles and fp32 accumulation [repo
- * page 0.50.0: fused 4-bit dequantize + GEMM in place of dequantize +
- * F.linear]. Same layouts and rules as nf4_gemv, except that M is any
- * M >= 0, and K <= 2^22 and N <= 2^21 (NF4_ERR_UNSUPPORTED above). */
-nf4_status nf4_gemm(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+/* Prefill product, any M >= 0: the same contraction as nf4_gemv, computed with
+ * matrix cores (bf16 / fp16 compute) on dequantized weight tiles and fp32
+ * accumulation [repo page 0.50.0: fused 4-bit dequantize + GEMM in place of
+ * dequantize + F.linear]. Same layouts and rules as nf4_gemv, except that M
+ * is any M >= 0, and K <= 2^22 and N <= 2^21 (NF4_ERR_UNSUPPORTED above). */
+nf4_status nf4_gemm(const void *x, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                     int32_t compute_dtype, int32_t out_dtype, void *y, void *stream);
 
-/* Largest M that nf4_linear sends to the decode kernels (nf4_gemv's range). */
-#define NF4_GEMV_MAX_M 16
 
 /* A 4-bit linear layer with an optional fused bias, the kernel picked from the
  * shape [repo page ossradar.top bitsandbytes, release notes 0.50.0,
  * "Highlights": the new fused 4-bit kernels take the bias as well, and the
  * kernel is selected at run time from the shape]:
- *   y[m, j] = RN_fp32( sum_k bf16(dequant(W)[j, k]) * x[m, k] ) + bias[j]
+ *   y[m, j] = RN_fp32( sum_k cd(dequant(W)[j, k]) * x[m, k] ) + bias[j]
  * with the sum accumulated in fp32 exactly as nf4_gemv / nf4_gemm do, then the
- * bf16 bias added in fp32, then the output rounding (bf16 = RNE of that fp32
- * value). bias_bf16: device [N] bf16, 2-byte aligned (NF4_ERR_MISALIGNED
- * otherwise), or NULL for none. 0 <= M <= NF4_GEMV_MAX_M runs nf4_gemv's
- * kernels, larger M nf4_gemm's, with their layouts, limits and errors. Without
- * a bias the result is bitwise that of nf4_gemv / nf4_gemm. */
-nf4_status nf4_linear(const void *x_bf16, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
-                      const void *bias_bf16, int32_t compute_dtype, int32_t out_dtype, void *y,
+ * bias (compute_dtype, widened exactly) added in fp32, then the output
+ * rounding (bf16 / fp16 = RNE of that fp32 value). bias: device [N] in
+ * compute_dtype, aligned to its element size (NF4_ERR_MISALIGNED otherwise),
+ * or NULL for none. 0 <= M <= NF4_GEMV_MAX_M runs nf4_gemv's kernels, larger
+ * M nf4_gemm's, with their layouts, limits and errors. Without a bias the
+ * result is bitwise that of nf4_gemv / nf4_gemm. */
+nf4_status nf4_linear(const void *x, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
+                      const void *bias, int32_t compute_dtype, int32_t out_dtype, void *y,
                       void *stream);
+
+/* nf4_linear on strided activations and outputs [repo page, release notes
+ * 0.49.2: non-contiguous tensors are accepted]: row m of x starts ldx
+ * elements after row m - 1 (ldx >= K) and row m of y ldy elements after row
+ * m - 1 (ldy >= N); every row of x must start 16-byte aligned
+ * (NF4_ERR_MISALIGNED otherwise; y needs only its element alignment). With ldx == K and ldy == N it is
+ * nf4_linear; otherwise the result equals nf4_linear on contiguous copies,
+ * bit for bit, and elements of y outside the [M, N] window are not written. */
+nf4_status nf4_linear_ex(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w, int32_t N,
+                         int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
+                         void *y, int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }

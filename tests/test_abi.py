@@ -40,7 +40,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(nf4):
     declared = header_functions()
-    assert len(declared) == 15
+    assert len(declared) == 18
     handle = ctypes.CDLL(nf4.LIB_PATH)
     for name in declared:
         assert hasattr(handle, name), name
@@ -49,7 +49,7 @@ def test_exports_every_declared_symbol(nf4):
 
 def test_version_and_strings(nf4):
     L = nf4.lib()
-    assert L.nf4_abi_version() == 1
+    assert L.nf4_abi_version() == 2
     for s in range(5):
         assert L.nf4_status_string(s).decode().startswith("NF4_")
     assert b"unknown" in L.nf4_status_string(99)
@@ -70,8 +70,8 @@ def test_library_codebook_equals_oracle(nf4, orc, qt):
     assert np.array_equal(lib_vals.view(np.uint32), orc.codebook(qt).view(np.uint32))
 
 
-def _desc(nf4, n=4096, bs=64, qt=0, dq=0, bs2=256, packed=A, absmax=B, q=A, s2=B):
-    return nf4.QWeightDesc(packed, absmax, q, s2, n, bs, qt, dq, bs2)
+def _desc(nf4, n=4096, bs=64, qt=0, dq=0, bs2=256, packed=A, absmax=B, q=A, s2=B, off=B):
+    return nf4.QWeightDesc(packed, absmax, q, s2, n, bs, qt, dq, bs2, off)
 
 
 def test_quantize_validation(nf4):
@@ -111,10 +111,12 @@ def test_dequantize_validation(nf4):
     assert dq(ctypes.byref(d), 0, None, None) == INVALID
     assert dq(ctypes.byref(d), 0, MIS, None) == MISALIGNED
     for bad in (_desc(nf4, n=-1), _desc(nf4, bs=96), _desc(nf4, qt=3), _desc(nf4, dq=3),
-                _desc(nf4, absmax=0), _desc(nf4, dq=1, q=0), _desc(nf4, dq=1, bs2=48)):
+                _desc(nf4, absmax=0), _desc(nf4, dq=1, q=0), _desc(nf4, dq=1, bs2=48),
+                _desc(nf4, dq=2, off=0)):
         assert dq(ctypes.byref(bad), 0, A, None) == INVALID
     assert dq(ctypes.byref(_desc(nf4, packed=MIS)), 0, A, None) == MISALIGNED
     assert dq(ctypes.byref(_desc(nf4, dq=1, s2=MIS)), 0, A, None) == MISALIGNED
+    assert dq(ctypes.byref(_desc(nf4, dq=2, off=MIS)), 0, A, None) == MISALIGNED
     assert dq(ctypes.byref(_desc(nf4, n=0)), 0, None, None) == OK
 
 
@@ -127,14 +129,14 @@ def test_product_validation(nf4, entry):
     assert call(-1, 64, 128) == INVALID
     assert call(1, 64, 128, od=4) == INVALID
     assert call(1, 64, 128, cd=9) == INVALID
-    assert call(1, 64, 128, cd=1) == UNSUPPORTED  # fp32 compute dtype not built
+    assert call(1, 64, 128, cd=3) == INVALID
     assert call(1, 64, 128, x=None) == INVALID
     assert call(1, 64, 128, y=MIS) == MISALIGNED
     d96 = _desc(nf4, n=64 * 96, bs=64)
     assert call(1, 64, 96, desc=d96) == UNSUPPORTED  # K % blocksize != 0
     assert call(0, 64, 128, x=None, y=None) == OK
     if entry == "nf4_gemv":
-        assert call(17, 64, 128) == INVALID
+        assert call(65, 64, 128) == INVALID  # past the decode range
 
 
 def test_grouped_validation(nf4):
@@ -149,7 +151,7 @@ def test_grouped_validation(nf4):
     assert g(17, xs, 1, d, Ns, Ks, 0, 1, ys, None) == INVALID
     assert g(-1, xs, 1, d, Ns, Ks, 0, 1, ys, None) == INVALID
     assert g(2, None, 1, d, Ns, Ks, 0, 1, ys, None) == INVALID
-    assert g(2, xs, 17, d, Ns, Ks, 0, 1, ys, None) == INVALID
+    assert g(2, xs, 65, d, Ns, Ks, 0, 1, ys, None) == INVALID
     assert g(0, None, 1, None, None, None, 0, 1, None, None) == OK
     Kbad = (ctypes.c_int32 * 2)(128, 100)
     assert g(2, xs, 1, d, Ns, Kbad, 0, 1, ys, None) == INVALID  # second product N*K != n
@@ -157,6 +159,51 @@ def test_grouped_validation(nf4):
     assert g(2, xs, 1, mixed, Ns, Ks, 0, 1, ys, None) == UNSUPPORTED
     ys_bad = (P * 2)(B, MIS)
     assert g(2, xs, 1, d, Ns, Ks, 0, 1, ys_bad, None) == MISALIGNED
+
+
+def test_quantize_ex_validation(nf4):
+    q = nf4.lib().nf4_quantize_ex
+    #        w, dtype, rows, cols, ld, bs, qt, dq, packed, absmax, q, s2, off, stream
+    ok = dict(w=A, dt=0, rows=4, cols=64, ld=64, bs=64, qt=0, dq=0, p=A, a=B, qq=None, s2=None,
+              off=None)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return q(a["w"], a["dt"], a["rows"], a["cols"], a["ld"], a["bs"], a["qt"], a["dq"],
+                 a["p"], a["a"], a["qq"], a["s2"], a["off"], None)
+
+    assert call(dt=3) == INVALID
+    assert call(rows=-1) == INVALID
+    assert call(ld=32) == INVALID                      # ld < cols
+    assert call(dq=3) == INVALID
+    assert call(dq=2, qq=A, s2=B) == INVALID           # centred mode needs the offsets
+    assert call(dq=1) == INVALID                       # no absmax_q / absmax_scale
+    assert call(cols=60, ld=64) == UNSUPPORTED         # a strided row of 60 elements
+    assert call(ld=68) == MISALIGNED                   # rows 136 bytes apart
+    assert call(w=MIS) == MISALIGNED
+    assert call(dq=2, qq=A, s2=B, off=MIS) == MISALIGNED
+    assert call(w=None, rows=0) == OK                  # empty matrix: no-op
+
+
+def test_double_quant_ex_validation(nf4):
+    dq = nf4.lib().nf4_double_quant_ex
+    assert dq(A, 10, 256, 0, A, B, A, None) == INVALID      # mode none
+    assert dq(A, 10, 256, 3, A, B, A, None) == INVALID
+    assert dq(A, 10, 256, 2, A, B, None, None) == INVALID   # centred without offsets
+    assert dq(A, 10, 256, 2, A, B, MIS, None) == MISALIGNED
+    assert dq(None, 0, 256, 2, None, None, None, None) == OK
+
+
+def test_linear_ex_validation(nf4):
+    fn = nf4.lib().nf4_linear_ex
+    d = _desc(nf4, n=64 * 128)  # N = 64, K = 128
+    call = lambda M, ldx, ldy, cd=0, bias=None: fn(A, ldx, M, ctypes.byref(d), 64, 128, bias, cd, 1, B, ldy, None)  # noqa: E731
+    assert call(2, 100, 64) == INVALID        # ldx < K
+    assert call(2, 128, 32) == INVALID        # ldy < N
+    assert call(2, 132, 64) == MISALIGNED     # x rows 264 bytes apart
+    assert call(2, 128, 64, bias=A + 1) == MISALIGNED
+    assert call(2, 128, 64, cd=2, bias=A + 1) == MISALIGNED
+    assert call(2, 1 << 30, 64) == UNSUPPORTED  # x beyond 31-bit offsets
 
 
 def test_no_device_is_reported(nf4):

@@ -482,8 +482,10 @@ def test_stack7b_sampled_matrices(nf4, orc, bs):
     (4, 1000, 512, 64, True),     # x in registers
     (4, 130, 8192, 128, False),   # K > 6144: the K-split kernel
     (16, 257, 1024, 64, True),
-    (17, 300, 512, 64, True),     # past the decode range: the prefill GEMM
-    (64, 1000, 512, 32, False),
+    (17, 300, 512, 64, True),     # two 16-row M tiles
+    (64, 1000, 512, 32, False),   # the largest decode batch
+    (65, 300, 512, 64, True),     # past the decode range: the prefill GEMM
+    (130, 200, 256, 32, False),
 ])
 def test_linear_bias_matches_oracle(nf4, orc, M, N, K, bs, dq):
     """nf4_linear with a bf16 bias against the oracle's linear layer, each path
@@ -501,7 +503,7 @@ def test_linear_bias_matches_oracle(nf4, orc, M, N, K, bs, dq):
     y16 = nf4.linear(xd, qs, bd, torch.bfloat16)
     check_product(y32, y16, y_ref, wc16.reshape(N, K), x16, b16)
     y_nb = nf4.linear(xd, qs, None, torch.float32)
-    direct = nf4.gemv(xd, qs, torch.float32) if M <= 16 else nf4.gemm(xd, qs, torch.float32)
+    direct = nf4.gemv(xd, qs, torch.float32) if M <= 64 else nf4.gemm(xd, qs, torch.float32)
     assert torch.equal(y_nb, direct), "without a bias, nf4_linear differs from the direct call"
     assert torch.equal(y32, y_nb + bd.float()[None, :]), "the bias is not one fp32 add"
     assert torch.equal(nf4.linear(xd, qs, bd, torch.float32), y32), "not deterministic"
