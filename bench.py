@@ -85,17 +85,19 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--phases", default="quantize,quantize_grouped,dequantize,dequantize_grouped,"
-                                        "gemv,gemv_single,linear_bias,gemm,gemm_bias,sweep,mlp,"
-                                        "batched",
+                                        "gemv,gemv_deps,gemv_single,linear_bias,gemm,gemm_bias,"
+                                        "sweep,mlp,batched",
                     help="comma list of quantize, quantize_grouped, dequantize, dequantize_grouped "
                          "(per matrix / the seven weights of a layer per call), gemv (grouped per "
-                         "layer), gemv_single (one launch per matrix), linear_bias (the same "
+                         "layer), gemv_deps (grouped as a decoder's dependencies allow: "
+                         "{q,k,v}, {o}, {gate,up}, {down} per layer), "
+                         "gemv_single (one launch per matrix), linear_bias (the same "
                          "through nf4_linear with a bf16 bias), gemm, gemm_bias (the prefill "
                          "GEMM without / with a fused bias), "
                          "sweep (quantize, dequantize and gemv at the other blocksizes of "
-                         "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16), "
-                         "batched (the stack's decode products at M = 4 and 16, a layer per "
-                         "grouped launch); "
+                         "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16, 32, "
+                         "64), batched (the stack's decode products at M = 4, 16 and 64, a layer "
+                         "per grouped launch); "
                          "'copy' adds a plain 1 GiB device copy, the known-size reference "
                          "for HBM byte counters")
     ap.add_argument("--no-graph", action="store_true",
@@ -123,8 +125,8 @@ def main():
     bs = args.bs
     requested = args.phases.split(",")
     sweep_bs = [b for b in (64, 128, 256) if b != bs] if "sweep" in requested else []
-    mlp_ms = (1, 4, 8, 16) if "mlp" in requested else ()
-    batch_ms = (4, 16) if "batched" in requested else ()
+    mlp_ms = (1, 4, 8, 16, 32, 64) if "mlp" in requested else ()
+    batch_ms = (4, 16, 64) if "batched" in requested else ()
     phases = [p for p in requested if p not in ("sweep", "mlp", "batched")]
     for m in batch_ms:
         phases.append(f"gemv_m{m}")
@@ -155,6 +157,7 @@ def main():
                          wd=torch.empty_like(w),
                          y=torch.empty((1, m.rows), dtype=torch.float32, device=dev),
                          y_single=torch.empty((1, m.rows), dtype=torch.float32, device=dev),
+                         y_deps=torch.empty((1, m.rows), dtype=torch.float32, device=dev),
                          y_lin=torch.empty((1, m.rows), dtype=torch.float32, device=dev)))
     # the other blocksizes of the sweep share the bf16 weights and outputs
     for d in mats:
@@ -211,6 +214,19 @@ def main():
                 nf4.gemv_grouped([d["x"] for d in grp], [d["qs_bs"][b] for d in grp],
                                  outs=[d["y_bs"][b] for d in grp])
         return f
+
+    # a decoder's layer cannot co-launch its seven products: o waits for the
+    # attention of q, k, v and the last MLP product for the first two, so the
+    # launches are {q, k, v}, {o}, {gate, up}, {down} (matrices 0-2, 3, 4-5, 6)
+    dep_groups = [[0, 1, 2], [3], [4, 5], [6]]
+
+    def gemv_deps():
+        for grp in layers:
+            for idx in dep_groups:
+                sub = [grp[i] for i in idx if i < len(grp)]
+                if sub:
+                    nf4.gemv_grouped([d["x"] for d in sub], [d["qs"] for d in sub],
+                                     outs=[d["y_deps"] for d in sub])
 
     def gemv_single():
         # the same products, one launch per matrix (labelled apart from the
@@ -286,7 +302,7 @@ def main():
         copy_dst.copy_(copy_src)
 
     fns = dict(quantize=quantize_at(bs, True), dequantize=dequantize_at(bs), gemv=gemv_at(bs),
-               gemv_single=gemv_single, quantize_grouped=quantize_grouped,
+               gemv_single=gemv_single, gemv_deps=gemv_deps, quantize_grouped=quantize_grouped,
                dequantize_grouped=dequantize_grouped,
                gemm=ph_gemm, copy=ph_copy, linear_bias=linear_bias, gemm_bias=ph_gemm_bias)
     for b in sweep_bs:
@@ -388,6 +404,9 @@ def main():
     work["dequantize_grouped"] = dict(bytes=work["dequantize"]["bytes"], launches=len(layers))
     work["gemv"] = gemv_work(bs)
     work["gemv_single"] = dict(bytes=work["gemv"]["bytes"], launches=len(mats))
+    work["gemv_deps"] = dict(bytes=work["gemv"]["bytes"],
+                             launches=sum(1 for grp in layers for idx in dep_groups
+                                          if any(i < len(grp) for i in idx)))
     for b in sweep_bs:
         work[f"quantize_bs{b}"] = quantize_work(b, False)
         work[f"dequantize_bs{b}"] = dequantize_work(b)
@@ -456,8 +475,9 @@ def main():
                           "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
                           "[11008,4096] (up) and [4096,11008] (down) NF4 bs64 + double quant, "
                           "one product per launch over >1 GB of distinct weights, M = 1/4/8/16; "
-                          "gemv_m4 / gemv_m16: the stack's decode products at M = 4 / 16, a layer "
-                          "per grouped launch",
+                          "gemv_m4 / gemv_m16 / gemv_m64: the stack's decode products at M = 4 / "
+                          "16 / 64, a layer per grouped launch; gemv_deps: the M = 1 products "
+                          "grouped {q,k,v}, {o}, {gate,up}, {down} per layer",
         },
     }
     if "gemv" in phase_out:

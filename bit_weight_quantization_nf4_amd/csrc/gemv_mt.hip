@@ -335,6 +335,235 @@ __global__ __launch_bounds__(64 * W) void gemv_mt_kernel(MtArgs args) {
   }
 }
 
+// ---- x held in registers (M <= 16, K <= 16 * 128 * CMAX) ------------------
+// The same K split over 16 waves, but each wave keeps x of its chunk range in
+// registers, loaded when the workgroup reaches a problem with other
+// activations; a unit is then a whole item of the wave (its CMAX chunks, the
+// ones past its range reading zeros), and the ring runs over items. The
+// workgroups take contiguous item ranges, so a workgroup changes problems
+// only at the few boundaries inside its range. Every output is summed in the
+// same order as by the streaming kernel, so both give identical results.
+template <int NT, int CMAX, int PER>
+struct XUnit {
+  uint4 w[CMAX][NT];
+  int32_t q[CMAX][NT];
+  float s[CMAX][NT];
+  float mu[CMAX][NT];
+  uint32_t bias[PER];
+  int32_t p;            // problem (uniform)
+};
+
+template <int NT, int CMAX, int DQ, int CT>
+__global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
+  constexpr int W = 16, MT = 1;
+  __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
+  __shared__ __attribute__((aligned(16))) float red[W * NT * 4 * 64];
+  __shared__ float vals[16];
+
+  if (threadIdx.x < 16) vals[threadIdx.x] = args.value[threadIdx.x];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 256 * kCopies; idx += 64 * W) {
+    const int e = idx >> 5;
+    const f32x2 v = {vals[e >> 4], vals[e & 15]};
+    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * (idx & 31)) = v;
+  }
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int n = lane & 15, kg = lane >> 4;
+  const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
+  const int M = args.M, K = args.K;
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int c0 = (wave * nch) / W, c1 = ((wave + 1) * nch) / W;
+  // this workgroup's items: a contiguous range
+  const int items = args.total_items;
+  const int ibeg = (int)(((int64_t)blockIdx.x * items) / gridDim.x);
+  const int iend = (int)(((int64_t)(blockIdx.x + 1) * items) / gridDim.x);
+  const int I = iend - ibeg;
+  const uint32_t row_bytes = (uint32_t)K >> 1;
+  constexpr int kOuts = NT * 256;
+  constexpr int kPer = (kOuts + 64 * W - 1) / (64 * W);
+
+  int ib[kMaxGroup];
+#pragma unroll
+  for (int k = 0; k < kMaxGroup; ++k) ib[k] = args.item_begin[k];
+  auto problem_of = [&](int item) {
+    int p = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxGroup; ++k) p = ib[k] <= item ? k : p;
+    return p;
+  };
+
+  auto issue = [&](int i) {
+    XUnit<NT, CMAX, kPer> u;
+    const bool valid = i < I;
+    const int item = ibeg + (valid ? i : 0);
+    const int p = problem_of(item);
+    u.p = p;
+    const MtProblem &P = args.p[p];
+    const int row0 = (item - P.item_begin) * 16 * NT;
+    const int rows = P.N - row0 < 16 * NT ? P.N - row0 : 16 * NT;
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.packed + (int64_t)row0 * row_bytes), (short)0, (int)((uint32_t)rows * row_bytes),
+        kBufferFlags);
+    const uint64_t blk0 = ((uint64_t)row0 * (uint64_t)K) >> P.log2_bs;
+    const uint32_t nblk = ((uint32_t)rows * (uint32_t)K) >> P.log2_bs;
+    const uint64_t g0 = DQ ? blk0 >> P.log2_bs2 : 0;
+    const uint32_t blk_in = DQ ? (uint32_t)(blk0 & ((1ull << P.log2_bs2) - 1)) : 0;
+    const uint32_t ngr = DQ ? (blk_in + nblk + (1u << P.log2_bs2) - 1) >> P.log2_bs2 : 0;
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.absmax + (DQ ? g0 : blk0)), (short)0, (int)(4u * (DQ ? ngr : nblk)),
+        kBufferFlags);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(DQ ? (const void *)(P.absmax_q + blk0) : (const void *)P.absmax), (short)0,
+        (int)(DQ ? nblk : 0u), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(DQ == kDqCentred ? P.absmax_offset + g0 : P.absmax), (short)0,
+        (int)(DQ == kDqCentred ? 4u * ngr : 0u), kBufferFlags);
+#pragma unroll
+    for (int cc = 0; cc < CMAX; ++cc) {
+      const int k0 = (c0 + cc) * kChunk + 32 * kg;
+      const bool kok = valid && c0 + cc < c1 && k0 < K;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t r = (uint32_t)(16 * t + n);
+        u.w[cc][t] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       wrs, (int)(kok ? r * row_bytes + ((uint32_t)k0 >> 1) : kOOB), 0, 0));
+        const uint32_t b = (r * (uint32_t)K + (uint32_t)k0) >> P.log2_bs;
+        if (DQ == kDqNone) {
+          u.q[cc][t] = 1;
+          u.mu[cc][t] = 0.0f;
+          u.s[cc][t] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(kok ? 4u * b : kOOB), 0, 0));
+        } else {
+          const uint32_t g = (blk_in + b) >> P.log2_bs2;
+          u.q[cc][t] =
+              (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)(kok ? b : kOOB), 0, 0);
+          u.s[cc][t] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(kok ? 4u * g : kOOB), 0, 0));
+          u.mu[cc][t] = DQ == kDqCentred
+                            ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                            mrs, (int)(kok ? 4u * g : kOOB), 0, 0))
+                            : 0.0f;
+        }
+      }
+    }
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)P.bias, (short)0, P.bias != nullptr ? (int)(2u * (uint32_t)P.N) : 0, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = (int)threadIdx.x + 64 * W * j;
+      const int row = row0 + 16 * (o >> 8) + (o & 15);
+      u.bias[j] = __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)row), 0, 0);
+    }
+    return u;
+  };
+
+  // x of the wave's chunks for problem p (rows m >= M and pieces past K or
+  // past the wave's range read zeros)
+  uint4 xr[CMAX][4];
+  auto load_x = [&](int p) {
+    const MtProblem &P = args.p[p];
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)P.x, (short)0, (int)P.x_bytes, kBufferFlags);
+#pragma unroll
+    for (int cc = 0; cc < CMAX; ++cc) {
+      const int k0 = (c0 + cc) * kChunk + 32 * kg;
+      const bool ok = c0 + cc < c1 && k0 < K && n < M;
+      const uint32_t off = ok ? (uint32_t)n * P.ldx_bytes + 2u * (uint32_t)k0 : kOOB;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        xr[cc][s] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(off + 16u * s), 0, 0));
+    }
+  };
+
+  f32x4 acc[NT];
+  auto compute = [&](const XUnit<NT, CMAX, kPer> &u) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < CMAX; ++cc)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float ap = scale_from<DQ>(u.q[cc][t], u.s[cc][t], u.mu[cc][t]);
+        const uint32_t wd[4] = {u.w[cc][t].x, u.w[cc][t].y, u.w[cc][t].z, u.w[cc][t].w};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint4 b = dequant8<CT>(wd[s], ap, tbl, lane_base);
+          acc[t] = mfma16x16x32<CT>(xr[cc][s], b, acc[t]);
+        }
+      }
+  };
+
+  auto finish = [&](int i, const XUnit<NT, CMAX, kPer> &u) {
+    const int item = ibeg + i;
+    const MtProblem &P = args.p[u.p];
+    const int row0 = (item - P.item_begin) * 16 * NT;
+    const bool has_bias = P.bias != nullptr;
+    __syncthreads();  // the previous item's sums have been read
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[((wave * NT + t) * 4 + r) * 64 + lane] = acc[t][r];
+    __syncthreads();
+    const int ob = args.out_dtype == kFP32 ? 4 : 2;
+    const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)P.y, (short)0, (int)P.y_bytes, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int o = (int)threadIdx.x + 64 * W * j;
+      if (kOuts % (64 * W) != 0 && o >= kOuts) break;
+      const int l = o & 63, r = (o >> 6) & 3, t = o >> 8;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < W; ++w) sum += red[((w * NT + t) * 4 + r) * 64 + l];
+      if (has_bias) sum += widen16<CT>(u.bias[j]);
+      const int m = 4 * (l >> 4) + r;
+      const int row = row0 + 16 * t + (l & 15);
+      const uint32_t off = (m < M && row < P.N)
+                               ? (uint32_t)m * P.ldy_bytes + (uint32_t)row * (uint32_t)ob
+                               : kOOB;
+      if (args.out_dtype == kFP32)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), yrs, (int)off, 0, 0);
+      else if (args.out_dtype == kFP16)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<kFP16>(sum), yrs, (int)off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<kBF16>(sum), yrs, (int)off, 0, 0);
+    }
+  };
+
+  __syncthreads();  // table built
+  if (I <= 0) return;  // (whole workgroup)
+  // Ring of two item units. Before issuing the next unit, the x of the unit
+  // about to be computed is loaded if its activations differ from the ones
+  // held, so the wait for x leaves the next unit's loads in flight.
+  const char *x_held = nullptr;
+  uint32_t x_ld = 0;
+  XUnit<NT, CMAX, kPer> ring[2];
+  ring[0] = issue(0);
+  for (int i0 = 0; i0 < I; i0 += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool live = i0 + j < I;
+      if (live) {
+        const MtProblem &P = args.p[ring[j].p];
+        if (P.x != x_held || P.ldx_bytes != x_ld) {
+          load_x(ring[j].p);
+          x_held = P.x;
+          x_ld = P.ldx_bytes;
+        }
+      }
+      ring[(j + 1) % 2] = issue(i0 + j + 1);
+      if (live) {
+        compute(ring[j]);
+        finish(i0 + j, ring[j]);
+      }
+    }
+  }
+}
+
 template <int W, int MT, int NT, int DQ>
 hipError_t launch_ct(const MtArgs &args, int grid, int ct, hipStream_t stream) {
   if (ct == kFP16)
@@ -351,6 +580,24 @@ hipError_t launch_dq(const MtArgs &args, int grid, int dq, int ct, hipStream_t s
   if (dq == kDqCentred) return launch_ct<W, MT, NT, kDqCentred>(args, grid, ct, stream);
   if (dq == kDqSym) return launch_ct<W, MT, NT, kDqSym>(args, grid, ct, stream);
   return launch_ct<W, MT, NT, kDqNone>(args, grid, ct, stream);
+}
+
+template <int NT, int CMAX, int DQ>
+hipError_t launch_xct(const MtArgs &args, int grid, int ct, hipStream_t stream) {
+  if (ct == kFP16)
+    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, DQ, kFP16>), dim3(grid), dim3(1024), 0, stream,
+                       args);
+  else
+    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, DQ, kBF16>), dim3(grid), dim3(1024), 0, stream,
+                       args);
+  return hipGetLastError();
+}
+
+template <int NT, int CMAX>
+hipError_t launch_x(const MtArgs &args, int grid, int dq, int ct, hipStream_t stream) {
+  if (dq == kDqCentred) return launch_xct<NT, CMAX, kDqCentred>(args, grid, ct, stream);
+  if (dq == kDqSym) return launch_xct<NT, CMAX, kDqSym>(args, grid, ct, stream);
+  return launch_xct<NT, CMAX, kDqNone>(args, grid, ct, stream);
 }
 
 // items of 16 nt rows over the launch's problems
@@ -414,6 +661,16 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   args.total_items = items;
   for (int i = 0; i < 16; ++i) args.value[i] = tb.value[i];
   const int grid = items < cu ? items : cu;
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int cmax = (nch + 15) / 16;  // chunks of the widest wave's range
+  if (MT == 1 && cmax <= 3) {
+    // x in registers; 3 chunks per wave leave room for one row tile only
+    if (cmax == 3) return launch_x<1, 3>(args, grid, dq, compute_dtype, stream);
+    if (nt == 2) return cmax == 1 ? launch_x<2, 1>(args, grid, dq, compute_dtype, stream)
+                                  : launch_x<2, 2>(args, grid, dq, compute_dtype, stream);
+    return cmax == 1 ? launch_x<1, 1>(args, grid, dq, compute_dtype, stream)
+                     : launch_x<1, 2>(args, grid, dq, compute_dtype, stream);
+  }
   if (MT == 1) {
     if (nt == 2) return launch_dq<16, 1, 2>(args, grid, dq, compute_dtype, stream);
     return launch_dq<16, 1, 1>(args, grid, dq, compute_dtype, stream);

@@ -1,6 +1,7 @@
 // nf4_api.hip -- the extern "C" boundary of libnf4 (declared in include/nf4.h):
 // argument validation, device checks and dispatch to the kernel launchers.
 // Every check runs before the first launch, so a rejected call writes nothing.
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -356,11 +357,22 @@ nf4_status nf4_dequantize_grouped(int32_t count, const nf4_qweight *w, int32_t o
 
 namespace {
 
+// NF4_FORCE_KERNEL=mfma in the environment sends M = 1 products to the
+// matrix-core decode kernel instead of the single-row kernel (for A/B
+// measurement); read once per process.
+bool force_mfma_decode() {
+  static const bool force = [] {
+    const char *v = getenv("NF4_FORCE_KERNEL");
+    return v != nullptr && strcmp(v, "mfma") == 0;
+  }();
+  return force;
+}
+
 // The single-row kernel takes M = 1 products with a bf16 compute dtype, a bf16
 // or fp32 output and at most the symmetric second level, up to its longest K.
 bool single_row_path(int32_t M, int32_t K, int32_t compute_dtype, int32_t out_dtype, int dq) {
   return M == 1 && compute_dtype == NF4_DTYPE_BF16 && out_dtype != NF4_DTYPE_FP16 &&
-         dq != NF4_DQ_CENTRED && K <= gemv1_max_k();
+         dq != NF4_DQ_CENTRED && K <= gemv1_max_k() && !force_mfma_decode();
 }
 
 // The decode products of a grouped call (each with an optional bias; bias ==
