@@ -86,7 +86,7 @@ def parse():
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--phases", default="quantize,quantize_grouped,dequantize,dequantize_grouped,"
                                         "gemv,gemv_deps,gemv_single,linear_bias,gemm,gemm_bias,"
-                                        "sweep,mlp,batched",
+                                        "sweep,mlp,batched,configs",
                     help="comma list of quantize, quantize_grouped, dequantize, dequantize_grouped "
                          "(per matrix / the seven weights of a layer per call), gemv (grouped per "
                          "layer), gemv_deps (grouped as a decoder's dependencies allow: "
@@ -97,7 +97,8 @@ def parse():
                          "sweep (quantize, dequantize and gemv at the other blocksizes of "
                          "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16, 32, "
                          "64), batched (the stack's decode products at M = 4, 16 and 64, a layer "
-                         "per grouped launch); "
+                         "per grouped launch), configs (the tiny 256x512 workload, the 4096x4096 "
+                         "one with 0.1%% outliers x20 and double quant, and the MLP shapes in FP4); "
                          "'copy' adds a plain 1 GiB device copy, the known-size reference "
                          "for HBM byte counters")
     ap.add_argument("--no-graph", action="store_true",
@@ -127,7 +128,10 @@ def main():
     sweep_bs = [b for b in (64, 128, 256) if b != bs] if "sweep" in requested else []
     mlp_ms = (1, 4, 8, 16, 32, 64) if "mlp" in requested else ()
     batch_ms = (4, 16, 64) if "batched" in requested else ()
-    phases = [p for p in requested if p not in ("sweep", "mlp", "batched")]
+    phases = [p for p in requested if p not in ("sweep", "mlp", "batched", "configs")]
+    if "configs" in requested:
+        phases += ["cfg1_quantize", "cfg1_dequantize", "cfg1_gemv", "cfg2_quantize", "cfg2_gemv"]
+        phases += [f"mlp_fp4_{name}_m{m}" for m in (1, 4, 8, 16) for name in ("up", "down")]
     for m in batch_ms:
         phases.append(f"gemv_m{m}")
     for b in sweep_bs:
@@ -268,6 +272,70 @@ def main():
                 y = torch.empty((m, N), dtype=torch.float32, device=dev)
                 mlp[f"mlp_{name}_m{m}"] = dict(qss=qss, x=x, y=y, N=N, K=K, M=m)
 
+    # the other workloads: the tiny [256, 512] weight (NF4 bs 64, no double
+    # quant, M = 1; 200 launches back to back on the same cache-resident data:
+    # latency-bound), the [4096, 4096] weight with 0.1 % of its entries x20
+    # (NF4 bs 64 + double quant, M = 1; 64 distinct seeded copies in rotation,
+    # beyond the last-level cache) and the MLP shapes in FP4 (as mlp_*)
+    cfg = {}
+    if "configs" in requested:
+        t = gpu_normal((256, 512), 0.02, 1001)
+        cfg["tiny_w"] = t
+        cfg["tiny_qs"] = nf4.quantize(t, 64, "nf4", double_quant=False)
+        cfg["tiny_x"] = gpu_normal((1, 512), 1.0, 2001)
+        cfg["tiny_y"] = torch.empty((1, 256), dtype=torch.float32, device=dev)
+        cfg["tiny_wd"] = torch.empty_like(t)
+        sq_w, sq_qs = [], []
+        for r in range(64):
+            g = torch.Generator(device=dev).manual_seed(1002 + 100 * r)
+            w = torch.randn((4096, 4096), generator=g, device=dev, dtype=torch.float32).mul_(0.02)
+            k = round(0.001 * w.numel())
+            go = torch.Generator(device=dev).manual_seed(3002 + 100 * r)
+            idx = torch.randperm(w.numel(), generator=go, device=dev)[:k]
+            w.view(-1)[idx] *= 20.0
+            w = w.to(torch.bfloat16)
+            if r < 16:
+                sq_w.append(w)  # the quantize phase rotates 16 copies (0.5 GB of bf16)
+            sq_qs.append(nf4.quantize(w, 64, "nf4", double_quant=True))
+            del w
+        cfg["sq_w"], cfg["sq_qs"] = sq_w, sq_qs
+        cfg["sq_x"] = gpu_normal((1, 4096), 1.0, 2002)
+        cfg["sq_y"] = torch.empty((1, 4096), dtype=torch.float32, device=dev)
+        up4 = [nf4.quantize(d["w"], 64, "fp4", True) for d in mats if d["spec"].rows == 11008][:48]
+        down4 = []
+        for r in range(24):
+            w = gpu_normal((4096, 11008), 0.02, 7000 + r)
+            down4.append(nf4.quantize(w, 64, "fp4", double_quant=True))
+            del w
+        for m in (1, 4, 8, 16):
+            for name, qss, N, K in (("up", up4, 11008, 4096), ("down", down4, 4096, 11008)):
+                x = gpu_normal((m, K), 1.0, 7100 + m + K)
+                y = torch.empty((m, N), dtype=torch.float32, device=dev)
+                mlp[f"mlp_fp4_{name}_m{m}"] = dict(qss=qss, x=x, y=y, N=N, K=K, M=m)
+
+    def cfg_fn(name):
+        def tiny_quantize():
+            for _ in range(200):
+                nf4.quantize(cfg["tiny_w"], 64, "nf4", False, out=cfg["tiny_qs"])
+
+        def tiny_dequantize():
+            for _ in range(200):
+                nf4.dequantize(cfg["tiny_qs"], out=cfg["tiny_wd"])
+
+        def tiny_gemv():
+            for _ in range(200):
+                nf4.gemv(cfg["tiny_x"], cfg["tiny_qs"], out=cfg["tiny_y"])
+
+        def sq_quantize():
+            for w, q in zip(cfg["sq_w"], cfg["sq_qs"]):
+                nf4.quantize(w, 64, "nf4", True, out=q)
+
+        def sq_gemv():
+            for q in cfg["sq_qs"]:
+                nf4.gemv(cfg["sq_x"], q, out=cfg["sq_y"])
+        return dict(cfg1_quantize=tiny_quantize, cfg1_dequantize=tiny_dequantize,
+                    cfg1_gemv=tiny_gemv, cfg2_quantize=sq_quantize, cfg2_gemv=sq_gemv)[name]
+
     # the stack's decode products at batch M, a layer's seven per grouped launch
     # (one activation block per M, shared by the products; an output per product)
     batch = {}
@@ -311,6 +379,9 @@ def main():
         fns[f"gemv_bs{b}"] = gemv_at(b)
     for key in mlp:
         fns[key] = mlp_at(key)
+    for key in ("cfg1_quantize", "cfg1_dequantize", "cfg1_gemv", "cfg2_quantize", "cfg2_gemv"):
+        if key in phases:
+            fns[key] = cfg_fn(key)
     for m in batch_ms:
         fns[f"gemv_m{m}"] = gemv_batched(m)
 
@@ -415,6 +486,19 @@ def main():
         N, K, m = e["N"], e["K"], e["M"]
         per = N * K // 2 + meta_bytes(N * K, 64) + 2 * m * K + 4 * m * N
         work[key] = dict(bytes=per * len(e["qss"]), launches=len(e["qss"]))
+    if "configs" in requested:
+        n1, n2 = 256 * 512, 4096 * 4096
+        nb1 = n1 // 64
+        work["cfg1_quantize"] = dict(bytes=200 * (2 * n1 + n1 // 2 + 4 * nb1), launches=200)
+        work["cfg1_dequantize"] = dict(bytes=200 * (n1 // 2 + 4 * nb1 + 2 * n1), launches=200)
+        work["cfg1_gemv"] = dict(bytes=200 * (n1 // 2 + 4 * nb1 + 2 * 512 + 4 * 256), launches=200)
+        nb2 = n2 // 64
+        work["cfg2_quantize"] = dict(
+            bytes=len(cfg["sq_w"]) * (2 * n2 + n2 // 2 + 4 * nb2 + nb2 + 4 * (-(-nb2 // 256))),
+            launches=len(cfg["sq_w"]))
+        work["cfg2_gemv"] = dict(
+            bytes=len(cfg["sq_qs"]) * (n2 // 2 + meta_bytes(n2, 64) + 2 * 4096 + 4 * 4096),
+            launches=len(cfg["sq_qs"]))
     M = prefill.ms[0]
     work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols * len(gemm_w), launches=len(gemm_w))
     work["gemm_bias"] = dict(work["gemm"])
@@ -477,7 +561,10 @@ def main():
                           "one product per launch over >1 GB of distinct weights, M = 1/4/8/16; "
                           "gemv_m4 / gemv_m16 / gemv_m64: the stack's decode products at M = 4 / "
                           "16 / 64, a layer per grouped launch; gemv_deps: the M = 1 products "
-                          "grouped {q,k,v}, {o}, {gate,up}, {down} per layer",
+                          "grouped {q,k,v}, {o}, {gate,up}, {down} per layer; cfg1_*: the tiny "
+                          "[256,512] workload (latency-bound, 200 launches on cache-resident data); "
+                          "cfg2_*: [4096,4096] with 0.1% outliers x20, NF4 bs64 + double quant; "
+                          "mlp_fp4_*: the MLP shapes in FP4",
         },
     }
     if "gemv" in phase_out:
@@ -504,8 +591,9 @@ def main():
 
     parity_ok = None
     if args.cpu_seconds > 0:
-        result["cpu_baseline"], parity_ok = cpu_baseline(mats, bs, args.cpu_seconds,
-                                                         check="gemv" in phases)
+        result["cpu_baseline"], parity_ok, sample = cpu_baseline(mats, bs, args.cpu_seconds,
+                                                                 check="gemv" in phases)
+        result["cpu_baseline_all_cores"] = cpu_baseline_threads(sample, bs, args.cpu_seconds / 2)
         result["cpu_baselines"] = cpu_baselines(mats, pw, px, bs, args.cpu_seconds / 2)
     result["parity_ok"] = parity_ok
     print(json.dumps(result), flush=True)
@@ -526,7 +614,7 @@ def cpu_baseline(mats, bs, target_s, check=True):
     With `check`, its result is also compared, element by element, with the
     output the timed gemv phase left for those matrices (relative L2 <= 1e-4
     and |y - y_ref| <= 1e-3 ||w_row|| ||x|| with w_row the bf16 dequantized
-    row). Returns (record, parity_ok or None)."""
+    row). Returns (record, parity_ok or None, the quantized sample for reuse)."""
     import numpy as np
 
     import oracle
@@ -534,6 +622,7 @@ def cpu_baseline(mats, bs, target_s, check=True):
 
     oracle.ensure_built(force=False)
     done_bytes, done_s, count, worst_rel, worst_elem = 0, 0.0, 0, 0.0, 0.0
+    sample = []
     for d in mats:
         N, K = d["spec"].rows, d["spec"].cols
         w16 = workloads.to_u16(d["w"].cpu().reshape(-1))
@@ -543,6 +632,7 @@ def cpu_baseline(mats, bs, target_s, check=True):
         t = time.perf_counter()
         y = oracle.gemv_quantized(x16, p, N, K, bs, "nf4", absmax_q=q, absmax_scale=s2)
         done_s += time.perf_counter() - t
+        sample.append((N, K, x16, p, q, s2))
         nb = -(-(N * K) // bs)
         done_bytes += N * K // 2 + nb + 4 * (-(-nb // 256)) + 2 * K + 4 * N
         if check:
@@ -562,12 +652,64 @@ def cpu_baseline(mats, bs, target_s, check=True):
     parity = (f"; GPU gemv-phase y vs oracle y: rel-L2 max {worst_rel:.2e} (gate {REL_L2_GATE:g}), "
               f"max |err| / (1e-3 ||w|| ||x||) {worst_elem:.2e} (gate 1)" if check else
               "; gemv phase not run, no parity check")
+    model, _, smt = host_info()
     return {
         "value": round(done_bytes / done_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
         "sample": f"oracle decode GEMV (M=1, fp64 sums) over the first {count} matrices of the "
-                  f"stack ({done_bytes / 1e6:.1f} MB algorithmic), {done_s:.1f} s single-threaded"
-                  + parity,
-    }, ok
+                  f"stack ({done_bytes / 1e6:.1f} MB algorithmic), {done_s:.1f} s single-threaded "
+                  f"on {model} (SMT {smt})" + parity,
+    }, ok, sample
+
+
+def host_info():
+    """CPU model, logical CPUs this process may use, SMT state (Linux)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    smt = "unknown"
+    try:
+        with open("/sys/devices/system/cpu/smt/active") as f:
+            smt = "on" if f.read().strip() == "1" else "off"
+    except OSError:
+        pass
+    cpus = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return model, cpus, smt
+
+
+def cpu_baseline_threads(sample, bs, target_s):
+    """The same oracle decode GEMV split by rows over every CPU this process
+    may use (one host thread each; bitwise the single-threaded result), over
+    the matrices the single-threaded leg quantized, in passes until about
+    target_s seconds of wall time."""
+    import oracle
+
+    model, cpus, smt = host_info()
+    done_bytes, done_s, count = 0, 0.0, 0
+    while sample and done_s < target_s:
+        for N, K, x16, p, q, s2 in sample:
+            t = time.perf_counter()
+            oracle.gemv_quantized_threads(x16, p, N, K, cpus, bs, "nf4", absmax_q=q,
+                                          absmax_scale=s2)
+            done_s += time.perf_counter() - t
+            nb = -(-(N * K) // bs)
+            done_bytes += N * K // 2 + nb + 4 * (-(-nb // 256)) + 2 * K + 4 * N
+            count += 1
+            if done_s >= target_s:
+                break
+    return {
+        "value": round(done_bytes / max(done_s, 1e-9) / 1e9, 4), "unit": "GB/s", "cores": cpus,
+        "kind": "oracle",
+        "sample": f"oracle decode GEMV (M=1, fp64 sums) split by rows over {cpus} host threads: "
+                  f"{count} products over the single-threaded leg's matrices "
+                  f"({done_bytes / 1e6:.1f} MB algorithmic) in {done_s:.1f} s; CPU {model}, "
+                  f"SMT {smt}",
+    }
 
 
 def cpu_baselines(mats, pw, px, bs, target_s):

@@ -75,6 +75,9 @@ def _load():
     lib.orc_matmul_typed.argtypes = [P, P, i32, i64, i64, i64, P]
     lib.orc_gemv_quantized_typed.restype = i32
     lib.orc_gemv_quantized_typed.argtypes = [P, i32, i64, P, i64, i64, i32, i32, P, P, P, P, i32, P]
+    lib.orc_gemv_quantized_threads.restype = i32
+    lib.orc_gemv_quantized_threads.argtypes = [P, i32, i64, P, i64, i64, i32, i32, P, P, P, P, i32, P,
+                                               i32, i64]
     lib.orc_convert.restype = i32
     lib.orc_convert.argtypes = [P, i32, i64, P, i32]
     lib.orc_f32_to_f16.restype = ctypes.c_uint16
@@ -318,4 +321,30 @@ def gemv_quantized_typed(x: np.ndarray, packed: np.ndarray, N: int, K: int, bloc
     _check(_load().orc_gemv_quantized_typed(_ptr(xx), _dt(dtype), M, _ptr(p), N, K, blocksize,
                                             _qt(quant_type), _ptr(a), _ptr(q), _ptr(s2), _ptr(off),
                                             blocksize2, _ptr(y)), "gemv_typed")
+    return y
+
+
+def gemv_quantized_threads(x: np.ndarray, packed: np.ndarray, N: int, K: int, threads: int,
+                           blocksize: int = 64, quant_type="nf4", absmax=None, absmax_q=None,
+                           absmax_scale=None, absmax_offset=None, blocksize2: int = 256,
+                           dtype="bf16") -> np.ndarray:
+    """gemv_quantized_typed split over `threads` host threads by rows (whole
+    double-quant groups per thread); bitwise the single-threaded result."""
+    xx = _typed(x, dtype)
+    if xx.ndim == 1:
+        xx = xx.reshape(1, -1)
+    M = xx.shape[0]
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    a = None if absmax is None else np.ascontiguousarray(absmax, dtype=np.float32)
+    q = None if absmax_q is None else np.ascontiguousarray(absmax_q, dtype=np.int8)
+    s2 = None if absmax_scale is None else np.ascontiguousarray(absmax_scale, dtype=np.float32)
+    off = None if absmax_offset is None else np.ascontiguousarray(absmax_offset, dtype=np.float32)
+    # rows per share: whole groups of bs2 blocks
+    import math
+    row_blocks = K // blocksize
+    align = blocksize2 // math.gcd(blocksize2, row_blocks) if q is not None else 1
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(_load().orc_gemv_quantized_threads(
+        _ptr(xx), _dt(dtype), M, _ptr(p), N, K, blocksize, _qt(quant_type), _ptr(a), _ptr(q),
+        _ptr(s2), _ptr(off), blocksize2, _ptr(y), int(threads), align), "gemv_threads")
     return y

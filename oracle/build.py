@@ -16,7 +16,7 @@ def build_oracle(force: bool = True) -> str:
     if not force and os.path.exists(OUT) and os.path.getmtime(OUT) >= os.path.getmtime(SRC):
         return OUT
     tmp = OUT + ".tmp"
-    subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm"])
+    subprocess.check_call(["gcc", *CFLAGS, "-o", tmp, SRC, "-lm", "-lpthread"])
     os.replace(tmp, OUT)
     return OUT
 

@@ -40,7 +40,9 @@
  *  - matmul: y[m, n] = sum_k bf16(w[n, k]) * x[m, k] summed in fp64.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_OK 0
@@ -536,4 +538,72 @@ int orc_convert(const void *in, int in_dtype, int64_t n, void *out, int out_dtyp
     else return ORC_ERR;
   }
   return ORC_OK;
+}
+
+/* ----------------------------------------------------- host-thread harness */
+
+/* The decode product split over T host threads by whole output rows, each
+ * thread running the sequential code above on its share, so the result is
+ * bitwise that of the single-threaded call. Used only to time the oracle on
+ * all host cores. */
+
+struct orc_gemv_job {
+  const void *x;
+  int dtype;
+  int64_t M, N0, N1, K;
+  const uint8_t *packed;
+  int bs, quant_type, bs2;
+  const float *absmax, *s2, *offset;
+  const int8_t *q;
+  double *y; /* [M, N1 - N0] rows of this job, row stride N1 - N0 */
+  int rc;
+};
+
+static void *orc_gemv_worker(void *arg) {
+  struct orc_gemv_job *j = (struct orc_gemv_job *)arg;
+  /* the rows [N0, N1) of W are a weight of N1 - N0 rows starting at element
+   * N0 * K; its blocks start at block N0 * K / bs (K % bs == 0) */
+  int64_t e0 = j->N0 * j->K, b0 = e0 / j->bs;
+  const float *a = j->absmax ? j->absmax + b0 : NULL;
+  const int8_t *q = j->q ? j->q + b0 : NULL;
+  /* group-aligned shares only (the caller splits on multiples of bs2 blocks) */
+  const float *s2 = j->s2 ? j->s2 + b0 / j->bs2 : NULL;
+  const float *off = j->offset ? j->offset + b0 / j->bs2 : NULL;
+  j->rc = orc_gemv_quantized_typed(j->x, j->dtype, j->M, j->packed + e0 / 2, j->N1 - j->N0, j->K,
+                                   j->bs, j->quant_type, a, q, s2, off, j->bs2, j->y);
+  return NULL;
+}
+
+/* orc_gemv_quantized_typed over T threads; rows are split on multiples of
+ * `row_align` rows (whole double-quant groups when row_align * K / bs is a
+ * multiple of bs2). y is [M, N]. */
+int orc_gemv_quantized_threads(const void *x, int dtype, int64_t M, const uint8_t *packed,
+                               int64_t N, int64_t K, int bs, int quant_type, const float *absmax,
+                               const int8_t *q, const float *s2, const float *offset, int bs2,
+                               double *y, int threads, int64_t row_align) {
+  if (threads < 1 || threads > 1024 || row_align < 1 || M < 0 || N < 0) return ORC_ERR;
+  if (K % bs != 0 || (q != NULL && ((row_align * K / bs) % bs2) != 0)) return ORC_ERR;
+  struct orc_gemv_job jobs[1024];
+  pthread_t tid[1024];
+  double *parts[1024];
+  int64_t units = (N + row_align - 1) / row_align;
+  int nt = threads < units ? threads : (int)(units > 0 ? units : 1);
+  for (int t = 0; t < nt; ++t) {
+    int64_t u0 = units * t / nt, u1 = units * (t + 1) / nt;
+    int64_t n0 = u0 * row_align, n1 = u1 * row_align < N ? u1 * row_align : N;
+    parts[t] = (double *)malloc(sizeof(double) * (size_t)(M * (n1 - n0) + 1));
+    jobs[t] = (struct orc_gemv_job){x, dtype, M, n0, n1, K, packed, bs, quant_type, bs2,
+                                    absmax, s2, offset, q, parts[t], 0};
+    pthread_create(&tid[t], NULL, orc_gemv_worker, &jobs[t]);
+  }
+  int rc = ORC_OK;
+  for (int t = 0; t < nt; ++t) {
+    pthread_join(tid[t], NULL);
+    if (jobs[t].rc != ORC_OK) rc = ORC_ERR;
+    int64_t w = jobs[t].N1 - jobs[t].N0;
+    for (int64_t m = 0; m < M; ++m)
+      for (int64_t n = 0; n < w; ++n) y[m * N + jobs[t].N0 + n] = parts[t][m * w + n];
+    free(parts[t]);
+  }
+  return rc;
 }

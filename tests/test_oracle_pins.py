@@ -671,3 +671,23 @@ def test_gemv_typed_equals_dequant_then_matmul(orc, dtype, dq):
     y = orc.gemv_quantized_typed(x, p, N, K, 64, "nf4", dtype=dtype, **kw)
     ref = orc.matmul_typed(x, wc.reshape(N, K), dtype)
     assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("dq", [0, 1, 2])
+def test_threaded_gemv_is_bitwise_the_sequential_one(orc, dq):
+    """The host-thread harness (used only to time the oracle on all cores)
+    splits whole rows and runs the sequential code on each share."""
+    N, K = 300, 1024
+    w = workloads.to_u16(workloads.normal_bf16((N, K), 0.02, 61))
+    x = workloads.to_u16(workloads.normal_bf16((3, K), 1.0, 62))
+    p, a = orc.quantize(w.reshape(-1), 64, "nf4")
+    kw = dict(absmax=a)
+    if dq == 1:
+        q, s2 = orc.double_quant(a, 256)
+        kw = dict(absmax_q=q, absmax_scale=s2)
+    elif dq == 2:
+        q, s2, mu = orc.double_quant_centred(a, 256)
+        kw = dict(absmax_q=q, absmax_scale=s2, absmax_offset=mu)
+    y1 = orc.gemv_quantized_typed(x, p, N, K, 64, "nf4", **kw)
+    for t in (1, 3, 8):
+        assert np.array_equal(orc.gemv_quantized_threads(x, p, N, K, t, 64, "nf4", **kw), y1)
