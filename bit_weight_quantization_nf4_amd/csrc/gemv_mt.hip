@@ -343,30 +343,66 @@ __global__ __launch_bounds__(64 * W) void gemv_mt_kernel(MtArgs args) {
 // workgroups take contiguous item ranges, so a workgroup changes problems
 // only at the few boundaries inside its range. Every output is summed in the
 // same order as by the streaming kernel, so both give identical results.
-template <int NT, int CMAX, int PER>
+//
+// The waves of a workgroup move through the items together (a barrier per
+// item): each wave reads only its 128-code slices of a row, so the item's
+// rows are fetched as whole DRAM pages only while all 16 waves ask for them
+// at about the same time. Within an item, the code words of the item D - 1
+// ahead are issued chunk by chunk between this item's chunks, so address
+// processing overlaps arithmetic, and a wave lowers its priority as it gets
+// through the item, so the four waves sharing a SIMD finish together rather
+// than oldest-first.
+//
+// Block scales are staged: one item ahead, the whole workgroup loads the
+// item's block codes (and group scales) row by row -- a wave reads 64
+// consecutive blocks of a row, so every load is one or two cache lines, and
+// each block is read once per workgroup instead of once per wave and piece --
+// forms a' = scale_from(q, s2, mu) once per block and writes it to an LDS
+// buffer (two buffers, alternating by item); a lane then reads the scale of
+// each of its 32-code pieces from LDS. Rows of the staged item are RS floats
+// apart with RS = 4 (mod 64), so the 16 rows x (up to 4) blocks a wave reads
+// at once fall in distinct banks.
+template <int NT, int CMAX>
+struct XStage {
+  static constexpr int kRows = 16 * NT;
+  static constexpr int kTpr = 1024 / kRows;         // staging threads per row
+  static constexpr int kMaxBlocks = 64 * CMAX;      // blocks of a row (blocksize >= 32)
+  static constexpr int kMaxPitch = kMaxBlocks + ((4 - kMaxBlocks) & 63);
+  static constexpr int kSlots = (kMaxBlocks + kTpr - 1) / kTpr;
+  static constexpr int kBufFloats = kRows * kMaxPitch;
+};
+
+template <int NT, int CMAX, int SLOTS, int PER>
 struct XUnit {
   uint4 w[CMAX][NT];
-  int32_t q[CMAX][NT];
-  float s[CMAX][NT];
-  float mu[CMAX][NT];
+  int32_t q[SLOTS];     // staged blocks: int8 block code (double quant)
+  float s[SLOTS];       // absmax, or the group scale s2
+  float mu[SLOTS];      // group offset (mean-centred double quant)
   uint32_t bias[PER];
   int32_t p;            // problem (uniform)
 };
 
-template <int NT, int CMAX, int DQ, int CT>
+// s_setprio with a value known after unrolling
+__device__ __forceinline__ void set_priority(int v) {
+  if (v >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (v == 2) __builtin_amdgcn_s_setprio(2);
+  else if (v == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+template <int NT, int CMAX, int D, int DQ, int CT>
 __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
-  constexpr int W = 16, MT = 1;
+  constexpr int W = 16;
+  using SD = XStage<NT, CMAX>;
+  // partial-sum buffers: two (one barrier per item) where LDS allows
+  constexpr int kRedFloats = W * NT * 4 * 64;
+  constexpr int RB = kTableBytes + 4 * (2 * kRedFloats + 2 * SD::kBufFloats) <= 160 * 1024 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
-  __shared__ __attribute__((aligned(16))) float red[W * NT * 4 * 64];
+  __shared__ __attribute__((aligned(16))) float red[RB * kRedFloats];
+  __shared__ __attribute__((aligned(16))) float stage[2 * SD::kBufFloats];
   __shared__ float vals[16];
 
   if (threadIdx.x < 16) vals[threadIdx.x] = args.value[threadIdx.x];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 256 * kCopies; idx += 64 * W) {
-    const int e = idx >> 5;
-    const f32x2 v = {vals[e >> 4], vals[e & 15]};
-    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * (idx & 31)) = v;
-  }
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -383,6 +419,12 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   const uint32_t row_bytes = (uint32_t)K >> 1;
   constexpr int kOuts = NT * 256;
   constexpr int kPer = (kOuts + 64 * W - 1) / (64 * W);
+  // every problem of the launch has the same blocksize
+  const int log2_bs = args.p[0].log2_bs;
+  const int KB = K >> log2_bs;                  // blocks of a row
+  const int RS = KB + ((4 - KB) & 63);          // staged row pitch (floats)
+  // staging: thread -> (row sr of the item, blocks sj + kTpr v)
+  const int sr = (int)threadIdx.x / SD::kTpr, sj = (int)threadIdx.x % SD::kTpr;
 
   int ib[kMaxGroup];
 #pragma unroll
@@ -394,8 +436,30 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
     return p;
   };
 
-  auto issue = [&](int i) {
-    XUnit<NT, CMAX, kPer> u;
+  // this lane's staged scale of each piece (chunk cc; row tile t is 64 RS
+  // bytes on); pieces past the wave's range or past K take scale 0 (their
+  // codes and x read zeros)
+  uint32_t saddr[CMAX];
+  bool sok[CMAX];
+#pragma unroll
+  for (int cc = 0; cc < CMAX; ++cc) {
+    const int k0 = (c0 + cc) * kChunk + 32 * kg;
+    sok[cc] = c0 + cc < c1 && k0 < K;
+    const int j = sok[cc] ? k0 >> log2_bs : 0;
+    saddr[cc] = 4u * (uint32_t)(n * RS + j);
+  }
+
+  using U = XUnit<NT, CMAX, SD::kSlots, kPer>;
+  // where item ordinal i's loads come from
+  struct Src {
+    __amdgpu_buffer_rsrc_t wrs;
+    bool valid;
+  };
+  // Loads of item ordinal i except its code words: the staged scales (first,
+  // so that the wait before they are written to LDS leaves the code words in
+  // flight) and the bias of the outputs this thread stores at the item's end.
+  // Past the workgroup's items every offset is out of range.
+  auto issue_head = [&](int i, U &u) {
     const bool valid = i < I;
     const int item = ibeg + (valid ? i : 0);
     const int p = problem_of(item);
@@ -403,50 +467,40 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
     const MtProblem &P = args.p[p];
     const int row0 = (item - P.item_begin) * 16 * NT;
     const int rows = P.N - row0 < 16 * NT ? P.N - row0 : 16 * NT;
-    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(P.packed + (int64_t)row0 * row_bytes), (short)0, (int)((uint32_t)rows * row_bytes),
-        kBufferFlags);
-    const uint64_t blk0 = ((uint64_t)row0 * (uint64_t)K) >> P.log2_bs;
-    const uint32_t nblk = ((uint32_t)rows * (uint32_t)K) >> P.log2_bs;
+    const uint64_t blk0 = ((uint64_t)row0 * (uint64_t)K) >> log2_bs;
+    const uint32_t nblk = (uint32_t)rows * (uint32_t)KB;
     const uint64_t g0 = DQ ? blk0 >> P.log2_bs2 : 0;
     const uint32_t blk_in = DQ ? (uint32_t)(blk0 & ((1ull << P.log2_bs2) - 1)) : 0;
     const uint32_t ngr = DQ ? (blk_in + nblk + (1u << P.log2_bs2) - 1) >> P.log2_bs2 : 0;
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(P.absmax + (DQ ? g0 : blk0)), (short)0, (int)(4u * (DQ ? ngr : nblk)),
-        kBufferFlags);
+        (void *)(P.absmax + (DQ ? g0 : blk0)), (short)0,
+        valid ? (int)(4u * (DQ ? ngr : nblk)) : 0, kBufferFlags);
     const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(DQ ? (const void *)(P.absmax_q + blk0) : (const void *)P.absmax), (short)0,
-        (int)(DQ ? nblk : 0u), kBufferFlags);
+        (int)(DQ && valid ? nblk : 0u), kBufferFlags);
     const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(DQ == kDqCentred ? P.absmax_offset + g0 : P.absmax), (short)0,
-        (int)(DQ == kDqCentred ? 4u * ngr : 0u), kBufferFlags);
+        (int)(DQ == kDqCentred && valid ? 4u * ngr : 0u), kBufferFlags);
+    // (every slot's loads are issued, unused ones out of range: a load under a
+    // branch would be waited for where the branches join)
 #pragma unroll
-    for (int cc = 0; cc < CMAX; ++cc) {
-      const int k0 = (c0 + cc) * kChunk + 32 * kg;
-      const bool kok = valid && c0 + cc < c1 && k0 < K;
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const uint32_t r = (uint32_t)(16 * t + n);
-        u.w[cc][t] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       wrs, (int)(kok ? r * row_bytes + ((uint32_t)k0 >> 1) : kOOB), 0, 0));
-        const uint32_t b = (r * (uint32_t)K + (uint32_t)k0) >> P.log2_bs;
-        if (DQ == kDqNone) {
-          u.q[cc][t] = 1;
-          u.mu[cc][t] = 0.0f;
-          u.s[cc][t] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(kok ? 4u * b : kOOB), 0, 0));
-        } else {
-          const uint32_t g = (blk_in + b) >> P.log2_bs2;
-          u.q[cc][t] =
-              (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)(kok ? b : kOOB), 0, 0);
-          u.s[cc][t] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(kok ? 4u * g : kOOB), 0, 0));
-          u.mu[cc][t] = DQ == kDqCentred
-                            ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                            mrs, (int)(kok ? 4u * g : kOOB), 0, 0))
-                            : 0.0f;
-        }
+    for (int v = 0; v < SD::kSlots; ++v) {
+      const int j = sj + SD::kTpr * v;
+      const uint32_t b = (uint32_t)(sr * KB + j);  // block in the item
+      const bool ok = j < KB;
+      u.q[v] = 1;
+      u.mu[v] = 0.0f;
+      if (DQ == kDqNone) {
+        u.s[v] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(ok ? 4u * b : kOOB), 0, 0));
+      } else {
+        const uint32_t g = (blk_in + b) >> P.log2_bs2;
+        u.q[v] = (int8_t)__builtin_amdgcn_raw_buffer_load_b8(qrs, (int)(ok ? b : kOOB), 0, 0);
+        u.s[v] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(srs, (int)(ok ? 4u * g : kOOB), 0, 0));
+        if (DQ == kDqCentred)
+          u.mu[v] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(mrs, (int)(ok ? 4u * g : kOOB), 0, 0));
       }
     }
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
@@ -457,7 +511,35 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
       const int row = row0 + 16 * (o >> 8) + (o & 15);
       u.bias[j] = __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)row), 0, 0);
     }
-    return u;
+    Src src;
+    src.valid = valid;
+    src.wrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(P.packed + (int64_t)row0 * row_bytes), (short)0,
+        (int)((uint32_t)rows * row_bytes), kBufferFlags);
+    return src;
+  };
+  // the code words of chunk cc of the item
+  auto issue_chunk = [&](const Src &src, int cc, U &u) {
+    const int k0 = (c0 + cc) * kChunk + 32 * kg;
+    const bool kok = src.valid && sok[cc];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t r = (uint32_t)(16 * t + n);
+      u.w[cc][t] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     src.wrs, (int)(kok ? r * row_bytes + ((uint32_t)k0 >> 1) : kOOB), 0, 0));
+    }
+  };
+
+  // a' of the unit's staged blocks into stage buffer `buf` (rows past the
+  // problem's N read zero codes and are never stored)
+  auto write_stage = [&](const U &u, int buf) {
+    float *sb = stage + buf * SD::kBufFloats + sr * RS;
+#pragma unroll
+    for (int v = 0; v < SD::kSlots; ++v) {
+      const int j = sj + SD::kTpr * v;
+      if (j < KB) sb[j] = scale_from<DQ>(u.q[v], u.s[v], u.mu[v]);
+    }
   };
 
   // x of the wave's chunks for problem p (rows m >= M and pieces past K or
@@ -470,7 +552,7 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
     for (int cc = 0; cc < CMAX; ++cc) {
       const int k0 = (c0 + cc) * kChunk + 32 * kg;
-      const bool ok = c0 + cc < c1 && k0 < K && n < M;
+      const bool ok = sok[cc] && n < M;
       const uint32_t off = ok ? (uint32_t)n * P.ldx_bytes + 2u * (uint32_t)k0 : kOOB;
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -480,33 +562,35 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   };
 
   f32x4 acc[NT];
-  auto compute = [&](const XUnit<NT, CMAX, kPer> &u) {
+  // chunk cc of a unit (stage buffer `buf`)
+  auto compute_chunk = [&](const U &u, int cc, int buf) {
+    const char *sb = reinterpret_cast<const char *>(stage) + buf * (4 * SD::kBufFloats);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; ++t) {
+      float ap = *reinterpret_cast<const float *>(sb + saddr[cc] + 64 * RS * t);
+      ap = sok[cc] ? ap : 0.0f;
+      const uint32_t wd[4] = {u.w[cc][t].x, u.w[cc][t].y, u.w[cc][t].z, u.w[cc][t].w};
 #pragma unroll
-    for (int cc = 0; cc < CMAX; ++cc)
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float ap = scale_from<DQ>(u.q[cc][t], u.s[cc][t], u.mu[cc][t]);
-        const uint32_t wd[4] = {u.w[cc][t].x, u.w[cc][t].y, u.w[cc][t].z, u.w[cc][t].w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint4 b = dequant8<CT>(wd[s], ap, tbl, lane_base);
-          acc[t] = mfma16x16x32<CT>(xr[cc][s], b, acc[t]);
-        }
+      for (int s = 0; s < 4; ++s) {
+        const uint4 b = dequant8<CT>(wd[s], ap, tbl, lane_base);
+        acc[t] = mfma16x16x32<CT>(xr[cc][s], b, acc[t]);
       }
+    }
   };
 
-  auto finish = [&](int i, const XUnit<NT, CMAX, kPer> &u) {
+  // With two partial buffers, item ordinal i uses buffer i & 1: its last
+  // reader, item i - 2, was done by every wave before the barrier of item i - 1.
+  auto finish = [&](int i, const U &u) {
     const int item = ibeg + i;
     const MtProblem &P = args.p[u.p];
     const int row0 = (item - P.item_begin) * 16 * NT;
     const bool has_bias = P.bias != nullptr;
-    __syncthreads();  // the previous item's sums have been read
+    float *rb = red + (RB == 2 ? (i & 1) * kRedFloats : 0);
+    if (RB == 1) __syncthreads();  // the previous item's sums have been read
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[((wave * NT + t) * 4 + r) * 64 + lane] = acc[t][r];
+      for (int r = 0; r < 4; ++r) rb[((wave * NT + t) * 4 + r) * 64 + lane] = acc[t][r];
     __syncthreads();
     const int ob = args.out_dtype == kFP32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -518,7 +602,7 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
       const int l = o & 63, r = (o >> 6) & 3, t = o >> 8;
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < W; ++w) sum += red[((w * NT + t) * 4 + r) * 64 + l];
+      for (int w = 0; w < W; ++w) sum += rb[((w * NT + t) * 4 + r) * 64 + l];
       if (has_bias) sum += widen16<CT>(u.bias[j]);
       const int m = 4 * (l >> 4) + r;
       const int row = row0 + 16 * t + (l & 15);
@@ -534,32 +618,69 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
     }
   };
 
-  __syncthreads();  // table built
-  if (I <= 0) return;  // (whole workgroup)
-  // Ring of two item units. Before issuing the next unit, the x of the unit
+  if (I <= 0) return;  // (whole workgroup; never taken: the grid is at most the item count)
+  // Ring of D item units, issued D - 1 items ahead; item ordinal i uses stage
+  // buffer i & 1. The stage of item i + 1 is written after item i is
+  // computed: every wave has left item i - 1 (the buffer's last reader) at
+  // the barrier of its end, and the barrier of item i's end publishes the
+  // stage before item i + 1 is computed. Before issuing, the x of the unit
   // about to be computed is loaded if its activations differ from the ones
-  // held, so the wait for x leaves the next unit's loads in flight.
+  // held. The first units are issued before the pair table is built, so the
+  // table's construction hides their latency.
   const char *x_held = nullptr;
   uint32_t x_ld = 0;
-  XUnit<NT, CMAX, kPer> ring[2];
-  ring[0] = issue(0);
-  for (int i0 = 0; i0 < I; i0 += 2) {
+  U ring[D];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bool live = i0 + j < I;
+  for (int k = 0; k < D - 1; ++k) {
+    const Src src = issue_head(k, ring[k]);
+#pragma unroll
+    for (int cc = 0; cc < CMAX; ++cc) issue_chunk(src, cc, ring[k]);
+  }
+  __syncthreads();  // code values in LDS
+  for (int idx = threadIdx.x; idx < 256 * kCopies; idx += 64 * W) {
+    const int e = idx >> 5;
+    const f32x2 v = {vals[e >> 4], vals[e & 15]};
+    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * (idx & 31)) = v;
+  }
+  write_stage(ring[0], 0);
+  __syncthreads();  // table and the first stage built
+  for (int i0 = 0; i0 < I; i0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int i = i0 + j;
+      const bool live = i < I;
       if (live) {
         const MtProblem &P = args.p[ring[j].p];
         if (P.x != x_held || P.ldx_bytes != x_ld) {
           load_x(ring[j].p);
+          // wait for x here, where it was loaded: past the branch the
+          // compiler would otherwise count x among the newest loads and make
+          // every later wait for x also wait for the items in flight
+#pragma unroll
+          for (int cc = 0; cc < CMAX; ++cc)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              asm volatile("" ::"v"(xr[cc][s].x), "v"(xr[cc][s].y), "v"(xr[cc][s].z), "v"(xr[cc][s].w));
           x_held = P.x;
           x_ld = P.ldx_bytes;
         }
       }
-      ring[(j + 1) % 2] = issue(i0 + j + 1);
-      if (live) {
-        compute(ring[j]);
-        finish(i0 + j, ring[j]);
+      // (a unit past the workgroup's items is computed too, from zero codes,
+      // and never stored: a load under a branch would be waited for where
+      // the branches join)
+      U &nu = ring[(j + D - 1) % D];
+      const Src src = issue_head(i + D - 1, nu);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cc = 0; cc < CMAX; ++cc) {
+        set_priority(CMAX - 1 - cc);
+        compute_chunk(ring[j], cc, i & 1);
+        issue_chunk(src, cc, nu);
       }
+      __builtin_amdgcn_s_setprio(0);
+      if (i + 1 < I) write_stage(ring[(j + 1) % D], (i + 1) & 1);
+      if (live) finish(i, ring[j]);
     }
   }
 }
@@ -582,22 +703,22 @@ hipError_t launch_dq(const MtArgs &args, int grid, int dq, int ct, hipStream_t s
   return launch_ct<W, MT, NT, kDqNone>(args, grid, ct, stream);
 }
 
-template <int NT, int CMAX, int DQ>
+template <int NT, int CMAX, int D, int DQ>
 hipError_t launch_xct(const MtArgs &args, int grid, int ct, hipStream_t stream) {
   if (ct == kFP16)
-    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, DQ, kFP16>), dim3(grid), dim3(1024), 0, stream,
+    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kFP16>), dim3(grid), dim3(1024), 0, stream,
                        args);
   else
-    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, DQ, kBF16>), dim3(grid), dim3(1024), 0, stream,
+    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kBF16>), dim3(grid), dim3(1024), 0, stream,
                        args);
   return hipGetLastError();
 }
 
-template <int NT, int CMAX>
+template <int NT, int CMAX, int D>
 hipError_t launch_x(const MtArgs &args, int grid, int dq, int ct, hipStream_t stream) {
-  if (dq == kDqCentred) return launch_xct<NT, CMAX, kDqCentred>(args, grid, ct, stream);
-  if (dq == kDqSym) return launch_xct<NT, CMAX, kDqSym>(args, grid, ct, stream);
-  return launch_xct<NT, CMAX, kDqNone>(args, grid, ct, stream);
+  if (dq == kDqCentred) return launch_xct<NT, CMAX, D, kDqCentred>(args, grid, ct, stream);
+  if (dq == kDqSym) return launch_xct<NT, CMAX, D, kDqSym>(args, grid, ct, stream);
+  return launch_xct<NT, CMAX, D, kDqNone>(args, grid, ct, stream);
 }
 
 // items of 16 nt rows over the launch's problems
@@ -616,14 +737,23 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   if (count == 0 || M == 0) return hipSuccess;
   if (count > kMaxGroup || M > 64) return hipErrorInvalidValue;
   const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int cu = device_cu_count();
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int cmax = (nch + 15) / 16;  // chunks of the widest wave's range
+  bool same_bs = true;               // the staged-scale kernel takes one blocksize
+  for (int i = 1; i < count; ++i) same_bs = same_bs && descs[i].blocksize == descs[0].blocksize;
+  const bool xreg = MT == 1 && cmax <= 3 && same_bs;
   // row tiles per item: the most (fewer x fragment loads per weight byte) that
   // still leave every CU a few items; the register budget caps it (4 waves
   // per SIMD at MT = 1 leave 128 registers: NT = 4 would spill)
-  const int cu = device_cu_count();
-  const int nt_max = MT == 2 ? 4 : 2;
+  // (the register-resident kernel takes one row tile per item: its per-item
+  // cost is mostly the workgroup's meeting, which grows with the tile)
   int nt = 1;
-  for (int c = 2; c <= nt_max; c *= 2)
-    if (count_items(count, descs, c) >= 3 * cu) nt = c;
+  if (!xreg) {
+    const int nt_max = MT == 2 ? 4 : 2;
+    for (int c = 2; c <= nt_max; c *= 2)
+      if (count_items(count, descs, c) >= 3 * cu) nt = c;
+  }
   const CodeTables &tb = code_tables(quant_type);
   MtArgs args;
   args.count = 0;
@@ -661,15 +791,11 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   args.total_items = items;
   for (int i = 0; i < 16; ++i) args.value[i] = tb.value[i];
   const int grid = items < cu ? items : cu;
-  const int nch = (K + kChunk - 1) / kChunk;
-  const int cmax = (nch + 15) / 16;  // chunks of the widest wave's range
-  if (MT == 1 && cmax <= 3) {
-    // x in registers; 3 chunks per wave leave room for one row tile only
-    if (cmax == 3) return launch_x<1, 3>(args, grid, dq, compute_dtype, stream);
-    if (nt == 2) return cmax == 1 ? launch_x<2, 1>(args, grid, dq, compute_dtype, stream)
-                                  : launch_x<2, 2>(args, grid, dq, compute_dtype, stream);
-    return cmax == 1 ? launch_x<1, 1>(args, grid, dq, compute_dtype, stream)
-                     : launch_x<1, 2>(args, grid, dq, compute_dtype, stream);
+  if (xreg) {
+    // x in registers; three items in flight where registers allow
+    if (cmax == 3) return launch_x<1, 3, 2>(args, grid, dq, compute_dtype, stream);
+    if (cmax == 2) return launch_x<1, 2, 3>(args, grid, dq, compute_dtype, stream);
+    return launch_x<1, 1, 3>(args, grid, dq, compute_dtype, stream);
   }
   if (MT == 1) {
     if (nt == 2) return launch_dq<16, 1, 2>(args, grid, dq, compute_dtype, stream);
