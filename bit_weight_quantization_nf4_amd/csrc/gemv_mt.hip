@@ -561,6 +561,17 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
     }
   };
 
+  // Wait for x where it was loaded: past a branch (or into the loop) the
+  // compiler would otherwise count x among the newest loads and make every
+  // later wait for x also wait for the items in flight.
+  auto touch_x = [&]() {
+#pragma unroll
+    for (int cc = 0; cc < CMAX; ++cc)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        asm volatile("" ::"v"(xr[cc][s].x), "v"(xr[cc][s].y), "v"(xr[cc][s].z), "v"(xr[cc][s].w));
+  };
+
   f32x4 acc[NT];
   // chunk cc of a unit (stage buffer `buf`)
   auto compute_chunk = [&](const U &u, int cc, int buf) {
@@ -627,8 +638,8 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   // about to be computed is loaded if its activations differ from the ones
   // held. The first units are issued before the pair table is built, so the
   // table's construction hides their latency.
-  const char *x_held = nullptr;
-  uint32_t x_ld = 0;
+  // The first items' loads go out first (they come from HBM), then the
+  // activations (from L2 once any workgroup has touched them).
   U ring[D];
 #pragma unroll
   for (int k = 0; k < D - 1; ++k) {
@@ -636,12 +647,17 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
     for (int cc = 0; cc < CMAX; ++cc) issue_chunk(src, cc, ring[k]);
   }
+  const int p_first = ring[0].p;
+  load_x(p_first);
+  const char *x_held = args.p[p_first].x;
+  uint32_t x_ld = args.p[p_first].ldx_bytes;
   __syncthreads();  // code values in LDS
   for (int idx = threadIdx.x; idx < 256 * kCopies; idx += 64 * W) {
     const int e = idx >> 5;
     const f32x2 v = {vals[e >> 4], vals[e & 15]};
     *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * (idx & 31)) = v;
   }
+  touch_x();
   write_stage(ring[0], 0);
   __syncthreads();  // table and the first stage built
   for (int i0 = 0; i0 < I; i0 += D) {
@@ -653,14 +669,7 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
         const MtProblem &P = args.p[ring[j].p];
         if (P.x != x_held || P.ldx_bytes != x_ld) {
           load_x(ring[j].p);
-          // wait for x here, where it was loaded: past the branch the
-          // compiler would otherwise count x among the newest loads and make
-          // every later wait for x also wait for the items in flight
-#pragma unroll
-          for (int cc = 0; cc < CMAX; ++cc)
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              asm volatile("" ::"v"(xr[cc][s].x), "v"(xr[cc][s].y), "v"(xr[cc][s].z), "v"(xr[cc][s].w));
+          touch_x();
           x_held = P.x;
           x_ld = P.ldx_bytes;
         }
