@@ -73,6 +73,11 @@ def measured_traffic(source):
         return nbytes if hashlib.sha256(f.read()).hexdigest() == digest else None
 
 
+def progress(msg: str) -> None:
+    """A progress line on stderr (the JSON result alone goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -150,6 +155,7 @@ def main():
         return t.to(torch.bfloat16)
 
     # ---- resident inputs and preallocated outputs
+    progress(f"quantizing the {len(stack.matrices)}-matrix stack")
     mats = []
     for m in stack.matrices:
         w = gpu_normal((m.rows, m.cols), m.sigma, m.seed)
@@ -386,6 +392,7 @@ def main():
         fns[f"gemv_m{m}"] = gemv_batched(m)
 
     # ---- capture each phase in a graph (after an eager warm-up call)
+    progress(f"inputs ready; warm-up call and capture of {len(phases)} phases")
     graphs = {}
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -414,6 +421,7 @@ def main():
         for p in phases:
             run(p)
     torch.cuda.synchronize()
+    progress(f"captured; timing {args.steps} steps")
 
     # ---- timed region
     ev = {p: [] for p in phases}
