@@ -59,8 +59,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # for the kernel source it was taken on (its SHA-256); after any change to that
 # source the benchmark reports null until the counters are taken again.
 MEASURED_TRAFFIC = {
-    "gemv1.hip": ("fcbe1f93273d19cc6b2937644a7bde13195649b866f967babdfa6e636c2ac9a1", 105774357),
-    "gemm.hip": ("c02594d990e55772b2aebc98d40e151be696fd788721fd87ebf7b5efdc0e96d0", 334981229),
+    "gemv1.hip": ("cad4bb1ead45c48ee7d5a1645fb8df0c2180734cb1718e7276e1afd27b808289", 105737772),
+    "gemm.hip": ("8d027daf9bfc44e2f2c69d891e66ebdf3ffa75937ae131bb2dd468c70f3d9ff6", 335442426),
 }
 
 
