@@ -455,6 +455,66 @@ def test_gemm_prefill_config(nf4, orc):
     assert torch.all(diff <= 1e-4 * (y32[:16].abs() + yv.abs()) + 1e-3)
 
 
+def test_gemm_prefill_full_output(nf4, orc):
+    """Every output of the full prefill GEMM (2048 x 4096 x 14336, NF4 bs64 +
+    double quant, fp32 out) against the fp64 oracle, computed by the oracle's
+    decode product split over host threads (bitwise its single-threaded
+    result): each element within 1e-3 ||w_row|| ||x_row||, rel-L2 <= 1e-4."""
+    import os
+
+    cfg = workloads.PREFILL
+    m = cfg.matrices[0]
+    w = m.make()
+    N, K = w.shape
+    M = cfg.ms[0]
+    qs, ref = check_quant(nf4, orc, w, 64, "nf4", True)
+    x = cfg.activations(K, M)
+    x16 = to_u16(x)
+    y = nf4.gemm(dev(x), qs, torch.float32).cpu().numpy().astype(np.float64)
+    threads = max(1, min(16, os.cpu_count() or 1))
+    y_ref = orc.gemv_quantized_threads(x16, ref["packed"], N, K, threads, 64, "nf4",
+                                       absmax_q=ref["absmax_q"], absmax_scale=ref["absmax_scale"])
+    _, wc16 = orc.dequantize(ref["packed"], N * K, 64, "nf4", **oracle_scales(ref, True))
+    wn = np.linalg.norm(u16_to_f64(wc16.reshape(N, K)), axis=1)
+    xn = np.linalg.norm(u16_to_f64(x16), axis=1)
+    err = np.abs(y - y_ref)
+    assert np.all(err <= PER_ELEM * xn[:, None] * wn[None, :]), \
+        f"max err / bound {np.max(err / (PER_ELEM * xn[:, None] * wn[None, :])):.3e}"
+    assert np.linalg.norm(y - y_ref) / np.linalg.norm(y_ref) <= REL_L2
+
+
+def test_decode_k_5120_many_rows_grouped(nf4, orc):
+    """K in 4097..6144 (three 128-code chunks per wave in the register-resident
+    decode kernel) with enough rows that two-tile items would be counted: a
+    grouped call of two [13824, 5120] products at M = 4 covers every row
+    (sampled rows against the oracle, all rows against the single calls)."""
+    K, N = 5120, 13824
+    qss, refs, ws = [], [], []
+    for j in range(2):
+        w = workloads.normal_bf16((N, K), 0.02, 6100 + j)
+        qs, ref = check_quant(nf4, orc, w, 64, "nf4", True)
+        qss.append(qs)
+        refs.append(ref)
+    x = workloads.normal_bf16((4, K), 1.0, 6200)
+    x16 = to_u16(x)
+    xd = dev(x)
+    outs = [torch.full((4, N), float("nan"), device="cuda") for _ in range(2)]
+    ys = nf4.gemv_grouped([xd, xd], qss, torch.float32, outs=outs)
+    rng = np.random.default_rng(11)
+    rows = np.concatenate([[0, N - 1, N // 2], rng.integers(0, N, 61)])
+    for j in range(2):
+        y1 = nf4.gemv(xd, qss[j], torch.float32)
+        assert torch.equal(ys[j], y1), "grouped differs from single"
+        _, wc16 = orc.dequantize(refs[j]["packed"], N * K, 64, "nf4", **oracle_scales(refs[j], True))
+        wsel = wc16.reshape(N, K)[rows]
+        y_ref = orc.matmul_bf16(x16, np.ascontiguousarray(wsel))
+        yy = ys[j].cpu().numpy().astype(np.float64)[:, rows]
+        bound = PER_ELEM * np.linalg.norm(u16_to_f64(x16), axis=1)[:, None] * \
+            np.linalg.norm(u16_to_f64(wsel), axis=1)[None, :]
+        assert np.all(np.abs(yy - y_ref) <= bound)
+        assert bool(torch.isfinite(ys[j]).all()), "rows left unwritten"
+
+
 @pytest.mark.parametrize("bs", [64, 128, 256])
 def test_stack7b_sampled_matrices(nf4, orc, bs):
     """7B-shaped stack at each blocksize: first and last layer's q-shaped and
