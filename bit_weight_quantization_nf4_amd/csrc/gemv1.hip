@@ -470,18 +470,42 @@ hipError_t launch_dq(Gemv1Args &args, int64_t rows, int j, bool out_bf16, hipStr
     case 1: return launch_j<1, DQ, BS32>(args, rows, out_bf16, stream);
     case 2: return launch_j<2, DQ, BS32>(args, rows, out_bf16, stream);
     case 3: return launch_j<3, DQ, BS32>(args, rows, out_bf16, stream);
-    default: return launch_j<4, DQ, BS32>(args, rows, out_bf16, stream);
+    default:
+      // four slices at blocksize 32 would need more than 256 registers: those
+      // products take the MFMA decode kernel instead (never reached)
+      if constexpr (BS32) return hipErrorInvalidValue;
+      else return launch_j<4, DQ, BS32>(args, rows, out_bf16, stream);
   }
 }
 
 }  // namespace
 
-int gemv1_max_k() { return 4 * kSlice; }
+int gemv1_max_k(int blocksize) { return (blocksize == 32 ? 3 : 4) * kSlice; }
 
 hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type,
                                 bool double_quant, bool out_bf16, hipStream_t stream) {
   if (count == 0) return hipSuccess;
   if (count > kMaxGroup) return hipErrorInvalidValue;
+  // A launch takes the blocksize-32 variant when any of its products has
+  // blocksize 32, and that variant stops at three slices: a group that also
+  // holds longer products of other blocksizes goes out as two launches (a
+  // product's result does not depend on the launch it is in).
+  bool any32 = false, long_other = false;
+  for (int i = 0; i < count; ++i) {
+    any32 = any32 || descs[i].blocksize == 32;
+    long_other = long_other || (descs[i].blocksize != 32 && descs[i].K > 3 * kSlice);
+  }
+  if (any32 && long_other) {
+    GemvDesc a[kMaxGroup], b[kMaxGroup];
+    int na = 0, nb = 0;
+    for (int i = 0; i < count; ++i) {
+      if (descs[i].blocksize == 32) a[na++] = descs[i];
+      else b[nb++] = descs[i];
+    }
+    const hipError_t e = launch_gemv1_grouped(na, a, quant_type, double_quant, out_bf16, stream);
+    if (e != hipSuccess) return e;
+    return launch_gemv1_grouped(nb, b, quant_type, double_quant, out_bf16, stream);
+  }
   const CodeTables &t = code_tables(quant_type);
   Gemv1Args args;
   args.count = 0;

@@ -369,10 +369,12 @@ bool force_mfma_decode() {
 }
 
 // The single-row kernel takes M = 1 products with a bf16 compute dtype, a bf16
-// or fp32 output and at most the symmetric second level, up to its longest K.
-bool single_row_path(int32_t M, int32_t K, int32_t compute_dtype, int32_t out_dtype, int dq) {
+// or fp32 output and at most the symmetric second level, up to its longest K
+// (which depends on the blocksize).
+bool single_row_path(int32_t M, int32_t K, int32_t blocksize, int32_t compute_dtype,
+                     int32_t out_dtype, int dq) {
   return M == 1 && compute_dtype == NF4_DTYPE_BF16 && out_dtype != NF4_DTYPE_FP16 &&
-         dq != NF4_DQ_CENTRED && K <= gemv1_max_k() && !force_mfma_decode();
+         dq != NF4_DQ_CENTRED && K <= gemv1_max_k(blocksize) && !force_mfma_decode();
 }
 
 // The decode products of a grouped call (each with an optional bias; bias ==
@@ -415,7 +417,7 @@ nf4_status gemv_grouped_impl(int32_t count, const void *const *x, const int64_t 
   int n_one = 0;
   bool done[NF4_GEMV_MAX_GROUP] = {};
   for (int i = 0; i < count; ++i)
-    if (single_row_path(M, K[i], compute_dtype, out_dtype, dq)) {
+    if (single_row_path(M, K[i], w[i].blocksize, compute_dtype, out_dtype, dq)) {
       one[n_one++] = descs[i];
       done[i] = true;
     }

@@ -85,9 +85,9 @@ int gemv_max_group();
 hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int quant_type, int dq,
                           int compute_dtype, int out_dtype, hipStream_t stream);
 
-// Single-activation-row products (M = 1) for K <= gemv1_max_k(): waves own
+// Single-activation-row products (M = 1) for K <= gemv1_max_k(blocksize): waves own
 // whole rows; same grouping rules (contiguous x and y).
-int gemv1_max_k();
+int gemv1_max_k(int blocksize);
 hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type,
                                 bool double_quant, bool out_bf16, hipStream_t stream);
 

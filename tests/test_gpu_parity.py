@@ -344,6 +344,33 @@ def test_gemv_single_row_long_k(nf4, orc, bs, dq):
         _gemv_case(nf4, orc, w, x, bs, "nf4", dq)
 
 
+def test_gemv_grouped_m1_mixes_bs32_and_long_rows(nf4, orc):
+    """A grouped M = 1 call with a blocksize-32 product (single-row kernel), a
+    blocksize-64 product four slices long (single-row kernel, split into its
+    own launch) and a blocksize-32 product four slices long (MFMA decode
+    kernel): each equals its single call bit for bit and the oracle."""
+    shapes = [(40, 8192, 32), (56, 16384, 64), (24, 16384, 32)]
+    qss, xs, refs = [], [], []
+    for i, (N, K, bs) in enumerate(shapes):
+        w = workloads.normal_bf16((N, K), 0.02, 9500 + i)
+        qs, ref = check_quant(nf4, orc, w, bs, "nf4", True)
+        qss.append(qs)
+        refs.append((ref, N, K, bs))
+        xs.append(workloads.normal_bf16((1, K), 1.0, 9600 + i))
+    ys = nf4.gemv_grouped([dev(x) for x in xs], qss, torch.float32)
+    for i, (ref, N, K, bs) in enumerate(refs):
+        y1 = nf4.gemv(dev(xs[i]), qss[i], torch.float32)
+        assert torch.equal(ys[i], y1), f"product {i}: grouped differs from single"
+        _, wc16 = orc.dequantize(ref["packed"], N * K, bs, "nf4", **oracle_scales(ref, True))
+        x16 = to_u16(xs[i])
+        y_ref = orc.matmul_bf16(x16, wc16.reshape(N, K))
+        yy = y1.cpu().numpy().astype(np.float64)
+        bound = PER_ELEM * np.linalg.norm(u16_to_f64(x16)) * np.linalg.norm(
+            u16_to_f64(wc16.reshape(N, K)), axis=1)[None, :]
+        assert np.all(np.abs(yy - y_ref) <= bound)
+        assert np.linalg.norm(yy - y_ref) / np.linalg.norm(y_ref) <= REL_L2
+
+
 @pytest.mark.parametrize("M", [1, 3])
 def test_gemv_reads_no_activation_past_k(nf4, orc, M):
     """Rows whose length ends half-way through a lane's 64 codes (K % 64 == 32),
