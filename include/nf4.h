@@ -249,9 +249,9 @@ nf4_status nf4_gemv(const void *x, int32_t M, const nf4_qweight *w, int32_t N, i
  * one transformer layer at one decode position [repo page 0.50.0: kernels for
  * 4-bit inference chosen by shape; one launch keeps all CUs busy where a single
  * small GEMV cannot]. For i < count:
- *   y[i][m, j] = sum_k bf16(dequant(w[i])[j, k]) * x[i][m, k],
- * with the layouts and rules of nf4_gemv for each product. x_bf16, w, N, K and
- * y are HOST arrays of `count` entries (the tensors they point to are on the
+ *   y[i][m, j] = sum_k cd(dequant(w[i])[j, k]) * x[i][m, k],
+ * with the layouts and rules of nf4_gemv for each product. x, w, N, K and y
+ * are HOST arrays of `count` entries (the tensors they point to are on the
  * device). All products share M (1..NF4_GEMV_MAX_M), the compute dtype, the
  * quant type and the double-quant mode (NF4_ERR_UNSUPPORTED otherwise); shapes
  * and blocksizes may differ.
