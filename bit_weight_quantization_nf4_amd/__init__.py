@@ -38,7 +38,7 @@ DTYPE_FP16 = 2
 DQ_NONE = 0
 DQ_SYMMETRIC = 1
 DQ_CENTRED = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 GEMV_MAX_M = 64
 
 _QT = {"nf4": QUANT_NF4, "fp4": QUANT_FP4}
@@ -111,6 +111,17 @@ _SIGNATURES = [
     ("nf4_linear_ex", ctypes.c_int32,
      [_P, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32,
       ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P]),
+    ("nf4_linear_workspace_bytes", ctypes.c_int64,
+     [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32]),
+    ("nf4_linear_ws", ctypes.c_int32,
+     [_P, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32,
+      ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, ctypes.c_int64,
+      _P]),
+    ("nf4_gemv_grouped_ws", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.POINTER(QWeightDesc),
+      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+      ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p), _P, ctypes.c_int64, _P]),
 ]
 
 _lib = None
@@ -378,19 +389,41 @@ def _product(fn, name, x, qs, out_dtype, out):
     return out
 
 
-def gemv(x: torch.Tensor, qs: QuantState, out_dtype=torch.float32, out=None) -> torch.Tensor:
-    """nf4_gemv: y[M, N] = x[M, K] . cd(W)^T for M <= 64; the compute dtype
-    cd is x's dtype (bf16, fp16 or fp32)."""
-    return _product(lib().nf4_gemv, "nf4_gemv", x, qs, out_dtype, out)
+def workspace_bytes(M: int, qs: QuantState, compute_dtype, out_dtype) -> int:
+    """nf4_linear_workspace_bytes for x[M, K] . W^T with W = qs ([N, K])."""
+    N, K = (int(s) for s in qs.shape)
+    return int(lib().nf4_linear_workspace_bytes(M, N, K, qs.blocksize, _DT[compute_dtype],
+                                                _DT[out_dtype], _dq(qs.double_quant)))
+
+
+def _workspace(nbytes: int, device):
+    """(pointer, bytes) of a fresh device workspace (torch's allocator, so it
+    is safe under stream capture), or (None, 0)."""
+    if nbytes <= 0:
+        return None, 0, None
+    t = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return t.data_ptr(), nbytes, t
+
+
+def gemv(x: torch.Tensor, qs: QuantState, out_dtype=torch.float32, out=None,
+         split: bool = True) -> torch.Tensor:
+    """y[M, N] = x[M, K] . cd(W)^T for M <= 64; the compute dtype cd is x's
+    dtype (bf16, fp16 or fp32). With split=True (nf4_gemv_grouped_ws) a
+    product whose activations do not fit one compute unit's registers is split
+    along K in a workspace this call allocates; split=False is nf4_gemv."""
+    if not split:
+        return _product(lib().nf4_gemv, "nf4_gemv", x, qs, out_dtype, out)
+    return gemv_grouped([x], [qs], out_dtype, None if out is None else [out], split=True)[0]
 
 
 GEMV_MAX_GROUP = 16
 
 
-def gemv_grouped(xs, qss, out_dtype=torch.float32, outs=None):
-    """nf4_gemv_grouped: several independent decode products in one call.
-    xs[i] is [M, K_i] (same M and dtype for all), qss[i] the quantized
-    [N_i, K_i] weight. Returns the list of y_i [M, N_i]."""
+def gemv_grouped(xs, qss, out_dtype=torch.float32, outs=None, split: bool = True):
+    """nf4_gemv_grouped_ws (split=True, with a workspace this call allocates)
+    or nf4_gemv_grouped (split=False): several independent decode products in
+    one call. xs[i] is [M, K_i] (same M and dtype for all), qss[i] the
+    quantized [N_i, K_i] weight. Returns the list of y_i [M, N_i]."""
     count = len(xs)
     if count != len(qss) or count > GEMV_MAX_GROUP:
         raise ValueError("gemv_grouped takes matching lists of at most 16 problems")
@@ -415,8 +448,16 @@ def gemv_grouped(xs, qss, out_dtype=torch.float32, outs=None):
     Darr = (QWeightDesc * count)(*descs)
     Narr = (ctypes.c_int32 * count)(*Ns)
     Karr = (ctypes.c_int32 * count)(*Ks)
-    _check(lib().nf4_gemv_grouped(count, Xarr, M, Darr, Narr, Karr, _DT[xs2[0].dtype],
-                                  _DT[ys[0].dtype], Yarr, _stream(xs2[0])), "nf4_gemv_grouped")
+    if not split:
+        _check(lib().nf4_gemv_grouped(count, Xarr, M, Darr, Narr, Karr, _DT[xs2[0].dtype],
+                                      _DT[ys[0].dtype], Yarr, _stream(xs2[0])),
+               "nf4_gemv_grouped")
+        return ys
+    need = sum(workspace_bytes(M, qs, xs2[0].dtype, ys[0].dtype) for qs in qss)
+    wp, wb, _keep = _workspace(need, xs2[0].device)
+    _check(lib().nf4_gemv_grouped_ws(count, Xarr, M, Darr, Narr, Karr, _DT[xs2[0].dtype],
+                                     _DT[ys[0].dtype], Yarr, wp, wb, _stream(xs2[0])),
+           "nf4_gemv_grouped_ws")
     return ys
 
 
@@ -426,12 +467,13 @@ def gemm(x: torch.Tensor, qs: QuantState, out_dtype=torch.bfloat16, out=None) ->
 
 
 def linear(x: torch.Tensor, qs: QuantState, bias: torch.Tensor | None = None,
-           out_dtype=None, out=None) -> torch.Tensor:
-    """nf4_linear_ex: y[M, N] = x[M, K] . cd(W)^T (+ bias[N] in the compute
-    dtype, added in fp32 before the output rounding); the compute dtype is x's
-    dtype; M <= 64 runs the decode kernels, larger M the prefill GEMM. A 2-D x
-    (or ``out``) with a row stride is passed in place. out_dtype defaults to
-    the compute dtype."""
+           out_dtype=None, out=None, split: bool = True) -> torch.Tensor:
+    """nf4_linear_ws (split=True, with a workspace this call allocates when
+    nf4_linear_workspace_bytes asks for one) or nf4_linear_ex (split=False):
+    y[M, N] = x[M, K] . cd(W)^T (+ bias[N] in the compute dtype, added in fp32
+    before the output rounding); the compute dtype is x's dtype; M <= 64 runs
+    the decode kernels, larger M the prefill GEMM. A 2-D x (or ``out``) with a
+    row stride is passed in place. out_dtype defaults to the compute dtype."""
     if x.dtype not in _DT or not x.is_cuda:
         raise TypeError("nf4_linear expects bf16 / fp16 / fp32 activations on the GPU")
     if len(qs.shape) != 2:
@@ -450,14 +492,20 @@ def linear(x: torch.Tensor, qs: QuantState, bias: torch.Tensor | None = None,
         raise ValueError("nf4_linear: out must be an [M, N] view with unit column stride")
     ldy = out.stride(0) if M > 1 else N
     d = qs.desc()
-    _check(lib().nf4_linear_ex(_ptr(x2), ldx, M, ctypes.byref(d), N, K,
+    if not split:
+        _check(lib().nf4_linear_ex(_ptr(x2), ldx, M, ctypes.byref(d), N, K,
+                                   None if bias is None else _ptr(bias), _DT[x.dtype],
+                                   _DT[out.dtype], _ptr(out), ldy, _stream(x2)), "nf4_linear_ex")
+        return out
+    wp, wb, _keep = _workspace(workspace_bytes(M, qs, x.dtype, out.dtype), x.device)
+    _check(lib().nf4_linear_ws(_ptr(x2), ldx, M, ctypes.byref(d), N, K,
                                None if bias is None else _ptr(bias), _DT[x.dtype], _DT[out.dtype],
-                               _ptr(out), ldy, _stream(x2)), "nf4_linear_ex")
+                               _ptr(out), ldy, wp, wb, _stream(x2)), "nf4_linear_ws")
     return out
 
 
 __all__ = [
     "QuantState", "QWeightDesc", "Nf4Error", "lib", "exported_names", "codebook", "packed_bytes",
     "num_blocks", "quantize", "quantize_grouped", "double_quant", "dequantize",
-    "dequantize_grouped", "gemv", "gemv_grouped", "gemm", "linear",
+    "dequantize_grouped", "gemv", "gemv_grouped", "gemm", "linear", "workspace_bytes",
 ]

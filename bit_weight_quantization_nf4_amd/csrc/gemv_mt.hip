@@ -46,6 +46,7 @@ constexpr int kChunk = 128;              // codes of one row per unit
 constexpr int kCopies = 32;              // interleaved copies of the pair table
 constexpr int kTableBytes = 256 * 256;   // 256 entries x 256-byte rows
 constexpr int kMaxGroup = 16;
+constexpr int kMaxSplit = 8;             // K ranges of a split product, at most
 constexpr int kBufferFlags = 0x00020000;  // word 3 of a raw buffer resource (gfx9)
 constexpr uint32_t kOOB = 0x80000000u;    // an offset past every buffer's range
 
@@ -62,6 +63,9 @@ struct MtProblem {
   int32_t log2_bs, log2_bs2;
   uint32_t ldx_bytes, ldy_bytes;
   uint32_t x_bytes, y_bytes;  // ranges of x and y
+  // K range of the problem (register-resident kernel): chunks kc0 .. kc1 - 1,
+  // and the blocks of a row it reads, jb .. jb + jn - 1
+  int32_t kc0, kc1, jb, jn;
 };
 
 struct MtArgs {
@@ -69,6 +73,8 @@ struct MtArgs {
   MtProblem p[kMaxGroup];
   int32_t count, M, K, total_items;
   int32_t out_dtype;
+  int32_t nchs;  // chunks of a K range (the waves' split), register-resident kernel
+  int32_t kbs;   // staged blocks of a row's K range (the most over the problems)
   float value[16];
 };
 
@@ -335,14 +341,23 @@ __global__ __launch_bounds__(64 * W) void gemv_mt_kernel(MtArgs args) {
   }
 }
 
-// ---- x held in registers (M <= 16, K <= 16 * 128 * CMAX) ------------------
+// ---- x held in registers (M <= 64; a K range of at most 16 * 128 * CMAX) ---
 // The same K split over 16 waves, but each wave keeps x of its chunk range in
-// registers, loaded when the workgroup reaches a problem with other
-// activations; a unit is then a whole item of the wave (its CMAX chunks, the
-// ones past its range reading zeros), and the ring runs over items. The
-// workgroups take contiguous item ranges, so a workgroup changes problems
-// only at the few boundaries inside its range. Every output is summed in the
-// same order as by the streaming kernel, so both give identical results.
+// registers (MT row tiles of 16 activation rows), loaded when the workgroup
+// reaches a problem with other activations or another K range; a unit is then
+// a whole item of the wave (its CMAX chunks, the ones past its range reading
+// zeros), and the ring runs over items. The workgroups take contiguous item
+// ranges, so a workgroup changes problems only at the few boundaries inside
+// its range. Without a K split every output is summed in the same order as by
+// the streaming kernel, so both give identical results.
+//
+// K split. x of a long row does not fit the registers of one CU (16 rows of
+// K = 11008 are 352 KB; 64 rows of K = 4096, 512 KB). A problem then covers
+// one K range [kc0, kc1) of a product (chunks kc0 .. kc1 - 1, the launch's
+// nchs chunks at most) and writes its fp32 partial sums to a workspace; a
+// second kernel adds the ranges of each output in range order, then the
+// bias, and rounds. Every range of a product has the same nchs-chunk split
+// over the waves, so the result depends only on M and K.
 //
 // The waves of a workgroup move through the items together (a barrier per
 // item): each wave reads only its 128-code slices of a row, so the item's
@@ -354,19 +369,19 @@ __global__ __launch_bounds__(64 * W) void gemv_mt_kernel(MtArgs args) {
 // than oldest-first.
 //
 // Block scales are staged: one item ahead, the whole workgroup loads the
-// item's block codes (and group scales) row by row -- a wave reads 64
-// consecutive blocks of a row, so every load is one or two cache lines, and
-// each block is read once per workgroup instead of once per wave and piece --
-// forms a' = scale_from(q, s2, mu) once per block and writes it to an LDS
-// buffer (two buffers, alternating by item); a lane then reads the scale of
-// each of its 32-code pieces from LDS. Rows of the staged item are RS floats
-// apart with RS = 4 (mod 64), so the 16 rows x (up to 4) blocks a wave reads
-// at once fall in distinct banks.
+// item's block codes (and group scales) of its K range row by row -- a wave
+// reads 64 consecutive blocks of a row, so every load is one or two cache
+// lines, and each block is read once per workgroup instead of once per wave
+// and piece -- forms a' = scale_from(q, s2, mu) once per block and writes it
+// to an LDS buffer (two buffers, alternating by item); a lane then reads the
+// scale of each of its 32-code pieces from LDS. Rows of the staged item are
+// RS floats apart with RS = 4 (mod 64), so the 16 rows x (up to 4) blocks a
+// wave reads at once fall in distinct banks.
 template <int NT, int CMAX>
 struct XStage {
   static constexpr int kRows = 16 * NT;
   static constexpr int kTpr = 1024 / kRows;         // staging threads per row
-  static constexpr int kMaxBlocks = 64 * CMAX;      // blocks of a row (blocksize >= 32)
+  static constexpr int kMaxBlocks = 64 * CMAX;      // blocks of a row's K range (blocksize >= 32)
   static constexpr int kMaxPitch = kMaxBlocks + ((4 - kMaxBlocks) & 63);
   static constexpr int kSlots = (kMaxBlocks + kTpr - 1) / kTpr;
   static constexpr int kBufFloats = kRows * kMaxPitch;
@@ -390,12 +405,12 @@ __device__ __forceinline__ void set_priority(int v) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-template <int NT, int CMAX, int D, int DQ, int CT>
+template <int NT, int CMAX, int D, int DQ, int CT, int MT>
 __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   constexpr int W = 16;
   using SD = XStage<NT, CMAX>;
   // partial-sum buffers: two (one barrier per item) where LDS allows
-  constexpr int kRedFloats = W * NT * 4 * 64;
+  constexpr int kRedFloats = W * NT * MT * 4 * 64;
   constexpr int RB = kTableBytes + 4 * (2 * kRedFloats + 2 * SD::kBufFloats) <= 160 * 1024 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
   __shared__ __attribute__((aligned(16))) float red[RB * kRedFloats];
@@ -409,20 +424,23 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   const int n = lane & 15, kg = lane >> 4;
   const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
   const int M = args.M, K = args.K;
-  const int nch = (K + kChunk - 1) / kChunk;
-  const int c0 = (wave * nch) / W, c1 = ((wave + 1) * nch) / W;
+  // this wave's chunks of a problem's K range: kc0 + w0 .. kc0 + w1 - 1
+  // (and below the range's end kc1)
+  const int nchs = args.nchs;
+  const int w0 = (wave * nchs) / W, w1 = ((wave + 1) * nchs) / W;
   // this workgroup's items: a contiguous range
   const int items = args.total_items;
   const int ibeg = (int)(((int64_t)blockIdx.x * items) / gridDim.x);
   const int iend = (int)(((int64_t)(blockIdx.x + 1) * items) / gridDim.x);
   const int I = iend - ibeg;
   const uint32_t row_bytes = (uint32_t)K >> 1;
-  constexpr int kOuts = NT * 256;
+  constexpr int kOuts = NT * MT * 256;
   constexpr int kPer = (kOuts + 64 * W - 1) / (64 * W);
   // every problem of the launch has the same blocksize
   const int log2_bs = args.p[0].log2_bs;
   const int KB = K >> log2_bs;                  // blocks of a row
-  const int RS = KB + ((4 - KB) & 63);          // staged row pitch (floats)
+  const int KBS = args.kbs;                     // staged blocks of a row's K range
+  const int RS = KBS + ((4 - KBS) & 63);        // staged row pitch (floats)
   // staging: thread -> (row sr of the item, blocks sj + kTpr v)
   const int sr = (int)threadIdx.x / SD::kTpr, sj = (int)threadIdx.x % SD::kTpr;
 
@@ -436,23 +454,30 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
     return p;
   };
 
-  // this lane's staged scale of each piece (chunk cc; row tile t is 64 RS
-  // bytes on); pieces past the wave's range or past K take scale 0 (their
-  // codes and x read zeros)
+  // this lane's staged scale of each piece (chunk cc of the wave's range;
+  // row tile t is 64 RS bytes on); pieces past the wave's range, the
+  // problem's range or K take scale 0 (their codes and x read zeros). Set for
+  // the problem whose x is held.
   uint32_t saddr[CMAX];
   bool sok[CMAX];
+  int c0 = 0;
+  auto set_range = [&](const MtProblem &P) {
+    c0 = P.kc0 + w0;
+    const int c1 = P.kc0 + w1 < P.kc1 ? P.kc0 + w1 : P.kc1;
 #pragma unroll
-  for (int cc = 0; cc < CMAX; ++cc) {
-    const int k0 = (c0 + cc) * kChunk + 32 * kg;
-    sok[cc] = c0 + cc < c1 && k0 < K;
-    const int j = sok[cc] ? k0 >> log2_bs : 0;
-    saddr[cc] = 4u * (uint32_t)(n * RS + j);
-  }
+    for (int cc = 0; cc < CMAX; ++cc) {
+      const int k0 = (c0 + cc) * kChunk + 32 * kg;
+      sok[cc] = c0 + cc < c1 && k0 < K;
+      const int j = sok[cc] ? (k0 >> log2_bs) - P.jb : 0;
+      saddr[cc] = 4u * (uint32_t)(n * RS + j);
+    }
+  };
 
   using U = XUnit<NT, CMAX, SD::kSlots, kPer>;
   // where item ordinal i's loads come from
   struct Src {
     __amdgpu_buffer_rsrc_t wrs;
+    int c0, c1;  // the wave's chunks of the item (scalar)
     bool valid;
   };
   // Loads of item ordinal i except its code words: the staged scales (first,
@@ -486,8 +511,8 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
     for (int v = 0; v < SD::kSlots; ++v) {
       const int j = sj + SD::kTpr * v;
-      const uint32_t b = (uint32_t)(sr * KB + j);  // block in the item
-      const bool ok = j < KB;
+      const uint32_t b = (uint32_t)(sr * KB + P.jb + j);  // block in the item
+      const bool ok = j < P.jn;
       u.q[v] = 1;
       u.mu[v] = 0.0f;
       if (DQ == kDqNone) {
@@ -508,11 +533,13 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int o = (int)threadIdx.x + 64 * W * j;
-      const int row = row0 + 16 * (o >> 8) + (o & 15);
+      const int row = row0 + 16 * ((o >> 8) / MT) + (o & 15);
       u.bias[j] = __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)row), 0, 0);
     }
     Src src;
     src.valid = valid;
+    src.c0 = P.kc0 + w0;
+    src.c1 = P.kc0 + w1 < P.kc1 ? P.kc0 + w1 : P.kc1;
     src.wrs = __builtin_amdgcn_make_buffer_rsrc(
         (void *)(P.packed + (int64_t)row0 * row_bytes), (short)0,
         (int)((uint32_t)rows * row_bytes), kBufferFlags);
@@ -520,8 +547,8 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   };
   // the code words of chunk cc of the item
   auto issue_chunk = [&](const Src &src, int cc, U &u) {
-    const int k0 = (c0 + cc) * kChunk + 32 * kg;
-    const bool kok = src.valid && sok[cc];
+    const int k0 = (src.c0 + cc) * kChunk + 32 * kg;
+    const bool kok = src.valid && src.c0 + cc < src.c1 && k0 < K;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t r = (uint32_t)(16 * t + n);
@@ -532,19 +559,20 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   };
 
   // a' of the unit's staged blocks into stage buffer `buf` (rows past the
-  // problem's N read zero codes and are never stored)
+  // problem's N, and blocks past its K range, read zero codes and are never
+  // used)
   auto write_stage = [&](const U &u, int buf) {
     float *sb = stage + buf * SD::kBufFloats + sr * RS;
 #pragma unroll
     for (int v = 0; v < SD::kSlots; ++v) {
       const int j = sj + SD::kTpr * v;
-      if (j < KB) sb[j] = scale_from<DQ>(u.q[v], u.s[v], u.mu[v]);
+      if (j < KBS) sb[j] = scale_from<DQ>(u.q[v], u.s[v], u.mu[v]);
     }
   };
 
-  // x of the wave's chunks for problem p (rows m >= M and pieces past K or
-  // past the wave's range read zeros)
-  uint4 xr[CMAX][4];
+  // x of the wave's chunks for problem p, MT row tiles (rows m >= M and
+  // pieces past K or past the wave's range read zeros); set_range(p) first
+  uint4 xr[CMAX][MT][4];
   auto load_x = [&](int p) {
     const MtProblem &P = args.p[p];
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -552,12 +580,16 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
     for (int cc = 0; cc < CMAX; ++cc) {
       const int k0 = (c0 + cc) * kChunk + 32 * kg;
-      const bool ok = sok[cc] && n < M;
-      const uint32_t off = ok ? (uint32_t)n * P.ldx_bytes + 2u * (uint32_t)k0 : kOOB;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        xr[cc][s] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(off + 16u * s), 0, 0));
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = 16 * mt + n;
+        const bool ok = sok[cc] && m < M;
+        const uint32_t off = ok ? (uint32_t)m * P.ldx_bytes + 2u * (uint32_t)k0 : kOOB;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          xr[cc][mt][s] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(xrs, (int)(off + 16u * s), 0, 0));
+      }
     }
   };
 
@@ -568,11 +600,14 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
     for (int cc = 0; cc < CMAX; ++cc)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        asm volatile("" ::"v"(xr[cc][s].x), "v"(xr[cc][s].y), "v"(xr[cc][s].z), "v"(xr[cc][s].w));
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          asm volatile("" ::"v"(xr[cc][mt][s].x), "v"(xr[cc][mt][s].y), "v"(xr[cc][mt][s].z),
+                       "v"(xr[cc][mt][s].w));
   };
 
-  f32x4 acc[NT];
+  f32x4 acc[NT][MT];
   // chunk cc of a unit (stage buffer `buf`)
   auto compute_chunk = [&](const U &u, int cc, int buf) {
     const char *sb = reinterpret_cast<const char *>(stage) + buf * (4 * SD::kBufFloats);
@@ -584,7 +619,8 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         const uint4 b = dequant8<CT>(wd[s], ap, tbl, lane_base);
-        acc[t] = mfma16x16x32<CT>(xr[cc][s], b, acc[t]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32<CT>(xr[cc][mt][s], b, acc[t][mt]);
       }
     }
   };
@@ -601,7 +637,10 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) rb[((wave * NT + t) * 4 + r) * 64 + lane] = acc[t][r];
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          rb[(((wave * NT + t) * MT + mt) * 4 + r) * 64 + lane] = acc[t][mt][r];
     __syncthreads();
     const int ob = args.out_dtype == kFP32 ? 4 : 2;
     const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -610,12 +649,13 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
     for (int j = 0; j < kPer; ++j) {
       const int o = (int)threadIdx.x + 64 * W * j;
       if (kOuts % (64 * W) != 0 && o >= kOuts) break;
-      const int l = o & 63, r = (o >> 6) & 3, t = o >> 8;
+      const int l = o & 63, r = (o >> 6) & 3, mt = (o >> 8) % MT, t = (o >> 8) / MT;
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < W; ++w) sum += rb[((w * NT + t) * 4 + r) * 64 + l];
+      for (int w = 0; w < W; ++w) sum += rb[(((w * NT + t) * MT + mt) * 4 + r) * 64 + l];
       if (has_bias) sum += widen16<CT>(u.bias[j]);
-      const int m = 4 * (l >> 4) + r;
+      // D layout of the 16x16 MFMA: lane l holds rows 4 (l / 16) + r of column l % 16
+      const int m = 16 * mt + 4 * (l >> 4) + r;
       const int row = row0 + 16 * t + (l & 15);
       const uint32_t off = (m < M && row < P.N)
                                ? (uint32_t)m * P.ldy_bytes + (uint32_t)row * (uint32_t)ob
@@ -635,9 +675,9 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
   // computed: every wave has left item i - 1 (the buffer's last reader) at
   // the barrier of its end, and the barrier of item i's end publishes the
   // stage before item i + 1 is computed. Before issuing, the x of the unit
-  // about to be computed is loaded if its activations differ from the ones
-  // held. The first units are issued before the pair table is built, so the
-  // table's construction hides their latency.
+  // about to be computed is loaded if its activations or K range differ from
+  // the ones held. The first units are issued before the pair table is
+  // built, so the table's construction hides their latency.
   // The first items' loads go out first (they come from HBM), then the
   // activations (from L2 once any workgroup has touched them).
   U ring[D];
@@ -648,9 +688,11 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
     for (int cc = 0; cc < CMAX; ++cc) issue_chunk(src, cc, ring[k]);
   }
   const int p_first = ring[0].p;
+  set_range(args.p[p_first]);
   load_x(p_first);
   const char *x_held = args.p[p_first].x;
   uint32_t x_ld = args.p[p_first].ldx_bytes;
+  int kc_held = args.p[p_first].kc0;
   __syncthreads();  // code values in LDS
   for (int idx = threadIdx.x; idx < 256 * kCopies; idx += 64 * W) {
     const int e = idx >> 5;
@@ -667,11 +709,13 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
       const bool live = i < I;
       if (live) {
         const MtProblem &P = args.p[ring[j].p];
-        if (P.x != x_held || P.ldx_bytes != x_ld) {
+        if (P.x != x_held || P.ldx_bytes != x_ld || P.kc0 != kc_held) {
+          set_range(P);
           load_x(ring[j].p);
           touch_x();
           x_held = P.x;
           x_ld = P.ldx_bytes;
+          kc_held = P.kc0;
         }
       }
       // (a unit past the workgroup's items is computed too, from zero codes,
@@ -680,7 +724,9 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
       U &nu = ring[(j + D - 1) % D];
       const Src src = issue_head(i + D - 1, nu);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cc = 0; cc < CMAX; ++cc) {
         set_priority(CMAX - 1 - cc);
@@ -691,6 +737,76 @@ __global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
       if (i + 1 < I) write_stage(ring[(j + 1) % D], (i + 1) & 1);
       if (live) finish(i, ring[j]);
     }
+  }
+}
+
+// The split-K sums: y_i[m, n] = out(sum over r < S of part_i[r][m][n], in
+// range order, + bias_i[n]) for the products of a split launch. part_i is
+// [S][M][N] fp32, contiguous. A thread takes four consecutive n of one row.
+struct SplitReduceProblem {
+  const float *part;
+  char *y;               // row m at m * ldy_bytes
+  const char *bias;      // [N] compute dtype, or null
+  int32_t N;
+  uint32_t ldy_bytes;
+  int32_t block_begin;   // first workgroup of the problem
+};
+
+struct SplitReduceArgs {
+  int32_t block_begin[kMaxGroup];  // unused: INT_MAX
+  SplitReduceProblem p[kMaxGroup];
+  int32_t M, S, out_dtype;
+};
+
+constexpr int kReduceThreads = 256;
+
+template <int CT>
+__global__ __launch_bounds__(kReduceThreads) void gemv_split_reduce_kernel(SplitReduceArgs args) {
+  int p = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxGroup; ++k) p = args.block_begin[k] <= (int)blockIdx.x ? k : p;
+  const SplitReduceProblem &P = args.p[p];
+  const int N = P.N, M = args.M, S = args.S;
+  const int n4 = (N + 3) >> 2;  // quads of a row
+  const int64_t q = (int64_t)((int)blockIdx.x - P.block_begin) * kReduceThreads + threadIdx.x;
+  if (q >= (int64_t)M * n4) return;
+  const int m = (int)(q / n4), n = 4 * (int)(q % n4);
+  const uint32_t plane = (uint32_t)M * (uint32_t)N;  // floats of one range
+  const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.part, (short)0, (int)(4u * plane * (uint32_t)S), kBufferFlags);
+  float sum[4];
+  const uint32_t e0 = (uint32_t)m * (uint32_t)N + (uint32_t)n;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t off = n + j < N ? 4u * (e0 + j) : kOOB;
+    sum[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, 0));
+  }
+  for (int r = 1; r < S; ++r)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t off = n + j < N ? 4u * (e0 + j + (uint32_t)r * plane) : kOOB;
+      sum[j] += __builtin_bit_cast(float,
+                                   __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, 0));
+    }
+  const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.bias, (short)0, P.bias != nullptr ? (int)(2u * (uint32_t)N) : 0, kBufferFlags);
+  const int ob = args.out_dtype == kFP32 ? 4 : 2;
+  const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)P.y, (short)0, (int)((uint32_t)(M - 1) * P.ldy_bytes + (uint32_t)N * ob),
+      kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float v = sum[j];
+    if (P.bias != nullptr)
+      v += widen16<CT>(__builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)(n + j)), 0, 0));
+    const uint32_t off =
+        n + j < N ? (uint32_t)m * P.ldy_bytes + (uint32_t)(n + j) * (uint32_t)ob : kOOB;
+    if (args.out_dtype == kFP32)
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), yrs, (int)off, 0, 0);
+    else if (args.out_dtype == kFP16)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<kFP16>(v), yrs, (int)off, 0, 0);
+    else
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<kBF16>(v), yrs, (int)off, 0, 0);
   }
 }
 
@@ -712,22 +828,36 @@ hipError_t launch_dq(const MtArgs &args, int grid, int dq, int ct, hipStream_t s
   return launch_ct<W, MT, NT, kDqNone>(args, grid, ct, stream);
 }
 
-template <int NT, int CMAX, int D, int DQ>
+template <int NT, int CMAX, int D, int DQ, int MT>
 hipError_t launch_xct(const MtArgs &args, int grid, int ct, hipStream_t stream) {
   if (ct == kFP16)
-    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kFP16>), dim3(grid), dim3(1024), 0, stream,
-                       args);
+    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kFP16, MT>), dim3(grid), dim3(1024), 0,
+                       stream, args);
   else
-    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kBF16>), dim3(grid), dim3(1024), 0, stream,
-                       args);
+    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kBF16, MT>), dim3(grid), dim3(1024), 0,
+                       stream, args);
   return hipGetLastError();
 }
 
-template <int NT, int CMAX, int D>
+template <int NT, int CMAX, int D, int MT>
 hipError_t launch_x(const MtArgs &args, int grid, int dq, int ct, hipStream_t stream) {
-  if (dq == kDqCentred) return launch_xct<NT, CMAX, D, kDqCentred>(args, grid, ct, stream);
-  if (dq == kDqSym) return launch_xct<NT, CMAX, D, kDqSym>(args, grid, ct, stream);
-  return launch_xct<NT, CMAX, D, kDqNone>(args, grid, ct, stream);
+  if (dq == kDqCentred) return launch_xct<NT, CMAX, D, kDqCentred, MT>(args, grid, ct, stream);
+  if (dq == kDqSym) return launch_xct<NT, CMAX, D, kDqSym, MT>(args, grid, ct, stream);
+  return launch_xct<NT, CMAX, D, kDqNone, MT>(args, grid, ct, stream);
+}
+
+// the register-resident kernel for MT row tiles and a wave range of cmax
+// chunks (at most mtx_cmax(MT)); three items in flight where registers allow
+hipError_t launch_xreg(const MtArgs &args, int grid, int mt, int cmax, int dq, int ct,
+                       hipStream_t stream) {
+  if (mt == 4) return launch_x<1, 1, 2, 4>(args, grid, dq, ct, stream);
+  if (mt == 2) {
+    if (cmax == 2) return launch_x<1, 2, 2, 2>(args, grid, dq, ct, stream);
+    return launch_x<1, 1, 3, 2>(args, grid, dq, ct, stream);
+  }
+  if (cmax == 3) return launch_x<1, 3, 2, 1>(args, grid, dq, ct, stream);
+  if (cmax == 2) return launch_x<1, 2, 3, 1>(args, grid, dq, ct, stream);
+  return launch_x<1, 1, 3, 1>(args, grid, dq, ct, stream);
 }
 
 // items of 16 nt rows over the launch's problems
@@ -737,26 +867,170 @@ int count_items(int count, const GemvDesc *descs, int nt) {
   return items;
 }
 
+// The problem fields every kernel reads (the K range is the whole row).
+void fill_problem(MtProblem &p, const GemvDesc &d, int M, int K, int dq, uint32_t xe,
+                  uint32_t ye) {
+  p.x = static_cast<const char *>(d.x);
+  p.packed = d.packed;
+  p.y = static_cast<char *>(d.y);
+  p.bias = static_cast<const char *>(d.bias);
+  p.absmax = dq ? d.sc.absmax_scale : d.sc.absmax;
+  p.absmax_q = d.sc.absmax_q;
+  p.absmax_offset = d.sc.absmax_offset;
+  p.N = d.N;
+  p.log2_bs = __builtin_ctz((unsigned)d.blocksize);
+  p.log2_bs2 = d.sc.log2_bs2;
+  p.ldx_bytes = (uint32_t)(d.ldx * xe);
+  p.ldy_bytes = (uint32_t)(d.ldy * ye);
+  p.x_bytes = (uint32_t)(((int64_t)(M - 1) * d.ldx + K) * xe);
+  p.y_bytes = (uint32_t)(((int64_t)(M - 1) * d.ldy + d.N) * ye);
+  p.kc0 = 0;
+  p.kc1 = (K + kChunk - 1) / kChunk;
+  p.jb = 0;
+  p.jn = K >> p.log2_bs;
+}
+
+void init_args(MtArgs &args, int M, int K, int out_dtype, const CodeTables &tb) {
+  args.count = 0;
+  args.M = M;
+  args.K = K;
+  args.out_dtype = out_dtype;
+  args.total_items = 0;
+  args.nchs = (K + kChunk - 1) / kChunk;
+  args.kbs = 0;
+  for (int i = 0; i < kMaxGroup; ++i) args.item_begin[i] = INT_MAX;
+  for (int i = 0; i < 16; ++i) args.value[i] = tb.value[i];
+}
+
+// One split launch: products descs[0 .. count) (count * S <= kMaxGroup), each
+// as S K ranges writing fp32 partials to its part buffer, then the sums.
+hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, int M, int K, int S,
+                        int quant_type, int dq, int compute_dtype, int out_dtype,
+                        hipStream_t stream) {
+  const int mt = gemv_row_tiles(M);
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int nchs = (nch + S - 1) / S;
+  const int cmax = (nchs + 15) / 16;
+  const CodeTables &tb = code_tables(quant_type);
+  const uint32_t xe = compute_dtype == kFP32 ? 4u : 2u;
+  MtArgs args;
+  init_args(args, M, K, kFP32, tb);
+  args.nchs = nchs;
+  SplitReduceArgs rargs;
+  rargs.M = M;
+  rargs.S = S;
+  rargs.out_dtype = out_dtype;
+  int items = 0, blocks = 0, nred = 0;
+  for (int i = 0; i < kMaxGroup; ++i) rargs.block_begin[i] = INT_MAX;
+  for (int i = 0; i < count; ++i) {
+    const GemvDesc &d = descs[i];
+    if (d.N == 0) continue;
+    for (int r = 0; r < S; ++r) {
+      const int k = args.count++;
+      MtProblem &p = args.p[k];
+      fill_problem(p, d, M, K, dq, xe, 4u);
+      p.y = reinterpret_cast<char *>(part[i] + (size_t)r * M * d.N);
+      p.bias = nullptr;
+      p.ldy_bytes = 4u * (uint32_t)d.N;
+      p.y_bytes = 4u * (uint32_t)M * (uint32_t)d.N;
+      p.kc0 = r * nchs;
+      p.kc1 = (r + 1) * nchs < nch ? (r + 1) * nchs : nch;
+      const int KB = K >> p.log2_bs;
+      p.jb = (p.kc0 * kChunk) >> p.log2_bs;
+      const int je = ((p.kc1 * kChunk - 1) >> p.log2_bs) + 1;
+      p.jn = (je < KB ? je : KB) - p.jb;
+      if (p.jn > args.kbs) args.kbs = p.jn;
+      args.item_begin[k] = items;
+      p.item_begin = items;
+      items += (d.N + 15) / 16;
+    }
+    SplitReduceProblem &q = rargs.p[nred];
+    q.part = part[i];
+    q.y = static_cast<char *>(d.y);
+    q.bias = static_cast<const char *>(d.bias);
+    q.N = d.N;
+    q.ldy_bytes = (uint32_t)(d.ldy * (out_dtype == kFP32 ? 4 : 2));
+    q.block_begin = blocks;
+    rargs.block_begin[nred++] = blocks;
+    const int64_t quads = (int64_t)M * ((d.N + 3) / 4);
+    blocks += (int)((quads + kReduceThreads - 1) / kReduceThreads);
+  }
+  if (args.count == 0) return hipSuccess;
+  args.total_items = items;
+  const int cu = device_cu_count();
+  const int grid = items < cu ? items : cu;
+  hipError_t e = launch_xreg(args, grid, mt, cmax, dq, compute_dtype, stream);
+  if (e != hipSuccess) return e;
+  if (compute_dtype == kFP16)
+    hipLaunchKernelGGL((gemv_split_reduce_kernel<kFP16>), dim3(blocks), dim3(kReduceThreads), 0,
+                       stream, rargs);
+  else
+    hipLaunchKernelGGL((gemv_split_reduce_kernel<kBF16>), dim3(blocks), dim3(kReduceThreads), 0,
+                       stream, rargs);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int gemv_max_group() { return kMaxGroup; }
 
+int gemv_row_tiles(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
+
+int gemv_split_ranges(int M, int K) {
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int mt = gemv_row_tiles(M);
+  const int cap = 16 * (mt == 1 ? 3 : (mt == 2 ? 2 : 1));  // chunks of x one CU holds
+  const int s = (nch + cap - 1) / cap;
+  return s <= kMaxSplit ? s : 0;
+}
+
+size_t gemv_split_bytes(int M, int N, int K) {
+  const int s = gemv_split_ranges(M, K);
+  if (s <= 1 || M <= 0 || N <= 0) return 0;
+  return ((size_t)s * (size_t)M * (size_t)N * 4u + 255u) & ~(size_t)255u;
+}
+
 hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int quant_type, int dq,
-                          int compute_dtype, int out_dtype, hipStream_t stream) {
+                          int compute_dtype, int out_dtype, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
   if (count == 0 || M == 0) return hipSuccess;
   if (count > kMaxGroup || M > 64) return hipErrorInvalidValue;
-  const int MT = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int MT = gemv_row_tiles(M);
   const int cu = device_cu_count();
   const int nch = (K + kChunk - 1) / kChunk;
-  const int cmax = (nch + 15) / 16;  // chunks of the widest wave's range
-  bool same_bs = true;               // the staged-scale kernel takes one blocksize
+  bool same_bs = true;  // the staged-scale kernel takes one blocksize
   for (int i = 1; i < count; ++i) same_bs = same_bs && descs[i].blocksize == descs[0].blocksize;
-  const bool xreg = MT == 1 && cmax <= 3 && same_bs;
-  // row tiles per item: the most (fewer x fragment loads per weight byte) that
-  // still leave every CU a few items; the register budget caps it (4 waves
-  // per SIMD at MT = 1 leave 128 registers: NT = 4 would spill)
-  // (the register-resident kernel takes one row tile per item: its per-item
-  // cost is mostly the workgroup's meeting, which grows with the tile)
+  // K ranges on the register-resident kernel (0: too many), and the
+  // workspace their partial sums take
+  const int S = gemv_split_ranges(M, K);
+  size_t need = 0;
+  for (int i = 0; i < count; ++i) need += gemv_split_bytes(M, descs[i].N, K);
+  bool fits = true;  // 32-bit offsets into each part buffer
+  for (int i = 0; i < count; ++i)
+    fits = fits && (int64_t)S * M * descs[i].N < ((int64_t)1 << 29);
+  if (same_bs && S > 1 && fits && workspace != nullptr && workspace_bytes >= need) {
+    // products in launches of at most kMaxGroup / S, each with its part buffer
+    float *part[kMaxGroup];
+    char *ws = static_cast<char *>(workspace);
+    const int per = kMaxGroup / S;
+    for (int i0 = 0; i0 < count; i0 += per) {
+      const int c = count - i0 < per ? count - i0 : per;
+      for (int i = 0; i < c; ++i) {
+        part[i] = reinterpret_cast<float *>(ws);
+        ws += gemv_split_bytes(M, descs[i0 + i].N, K);
+      }
+      const hipError_t e = launch_split(c, descs + i0, part, M, K, S, quant_type, dq,
+                                        compute_dtype, out_dtype, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
+  const bool xreg = same_bs && S == 1;
+  // streamed kernel: row tiles per item, the most (fewer x fragment loads per
+  // weight byte) that still leave every CU a few items; the register budget
+  // caps it (4 waves per SIMD at MT = 1 leave 128 registers: NT = 4 would
+  // spill). The register-resident kernel takes one row tile per item: its
+  // per-item cost is mostly the workgroup's meeting, which grows with the tile.
   int nt = 1;
   if (!xreg) {
     const int nt_max = MT == 2 ? 4 : 2;
@@ -765,47 +1039,25 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   }
   const CodeTables &tb = code_tables(quant_type);
   MtArgs args;
-  args.count = 0;
-  args.M = M;
-  args.K = K;
-  args.out_dtype = out_dtype;
+  init_args(args, M, K, out_dtype, tb);
   const uint32_t xe = compute_dtype == kFP32 ? 4u : 2u;
   const uint32_t ye = out_dtype == kFP32 ? 4u : 2u;
   int items = 0;
-  for (int i = 0; i < kMaxGroup; ++i) args.item_begin[i] = INT_MAX;
   for (int i = 0; i < count; ++i) {
     const GemvDesc &d = descs[i];
     if (d.N == 0) continue;
     const int k = args.count++;
     MtProblem &p = args.p[k];
-    p.x = static_cast<const char *>(d.x);
-    p.packed = d.packed;
-    p.y = static_cast<char *>(d.y);
-    p.bias = static_cast<const char *>(d.bias);
-    p.absmax = dq ? d.sc.absmax_scale : d.sc.absmax;
-    p.absmax_q = d.sc.absmax_q;
-    p.absmax_offset = d.sc.absmax_offset;
-    p.N = d.N;
-    p.log2_bs = __builtin_ctz((unsigned)d.blocksize);
-    p.log2_bs2 = d.sc.log2_bs2;
-    p.ldx_bytes = (uint32_t)(d.ldx * xe);
-    p.ldy_bytes = (uint32_t)(d.ldy * ye);
-    p.x_bytes = (uint32_t)(((int64_t)(M - 1) * d.ldx + K) * xe);
-    p.y_bytes = (uint32_t)(((int64_t)(M - 1) * d.ldy + d.N) * ye);
+    fill_problem(p, d, M, K, dq, xe, ye);
     args.item_begin[k] = items;
     p.item_begin = items;
     items += (d.N + 16 * nt - 1) / (16 * nt);
   }
   if (args.count == 0) return hipSuccess;
+  args.kbs = args.p[0].jn;
   args.total_items = items;
-  for (int i = 0; i < 16; ++i) args.value[i] = tb.value[i];
   const int grid = items < cu ? items : cu;
-  if (xreg) {
-    // x in registers; three items in flight where registers allow
-    if (cmax == 3) return launch_x<1, 3, 2>(args, grid, dq, compute_dtype, stream);
-    if (cmax == 2) return launch_x<1, 2, 3>(args, grid, dq, compute_dtype, stream);
-    return launch_x<1, 1, 3>(args, grid, dq, compute_dtype, stream);
-  }
+  if (xreg) return launch_xreg(args, grid, MT, (nch + 15) / 16, dq, compute_dtype, stream);
   if (MT == 1) {
     if (nt == 2) return launch_dq<16, 1, 2>(args, grid, dq, compute_dtype, stream);
     return launch_dq<16, 1, 1>(args, grid, dq, compute_dtype, stream);

@@ -383,8 +383,12 @@ bool single_row_path(int32_t M, int32_t K, int32_t blocksize, int32_t compute_dt
 nf4_status gemv_grouped_impl(int32_t count, const void *const *x, const int64_t *ldx, int32_t M,
                              const nf4_qweight *w, const int32_t *N, const int32_t *K,
                              const void *const *bias, int32_t compute_dtype, int32_t out_dtype,
-                             void *const *y, const int64_t *ldy, void *stream) {
+                             void *const *y, const int64_t *ldy, void *workspace,
+                             int64_t workspace_bytes, void *stream) {
   if (count < 0 || count > NF4_GEMV_MAX_GROUP) return NF4_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && workspace == nullptr))
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(workspace)) return NF4_ERR_MISALIGNED;
   if (count == 0) return NF4_OK;
   if (x == nullptr || w == nullptr || N == nullptr || K == nullptr || y == nullptr)
     return NF4_ERR_INVALID_ARGUMENT;
@@ -426,19 +430,32 @@ nf4_status gemv_grouped_impl(int32_t count, const void *const *x, const int64_t 
                                        out_dtype == NF4_DTYPE_BF16, s));
     if (st != NF4_OK) return st;
   }
-  // the rest on the matrix-core kernel, one launch per distinct K
+  // the rest on the matrix-core kernels, one launch per distinct (K,
+  // blocksize); launches on one stream run in order, so each may use the
+  // whole workspace
   for (int i = 0; i < count && st == NF4_OK; ++i) {
     if (done[i]) continue;
     GemvDesc same[NF4_GEMV_MAX_GROUP];
     int ns = 0;
     for (int j = i; j < count; ++j)
-      if (!done[j] && K[j] == K[i]) {
+      if (!done[j] && K[j] == K[i] && w[j].blocksize == w[i].blocksize) {
         same[ns++] = descs[j];
         done[j] = true;
       }
-    st = from_hip(launch_gemv_mt(ns, same, M, K[i], qt, dq, compute_dtype, out_dtype, s));
+    st = from_hip(launch_gemv_mt(ns, same, M, K[i], qt, dq, compute_dtype, out_dtype, workspace,
+                                 (size_t)workspace_bytes, s));
   }
   return st;
+}
+
+// Workspace bytes a decode product takes (the K split of the matrix-core
+// kernel), 0 when its dispatch splits nothing.
+int64_t product_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t blocksize,
+                                int32_t compute_dtype, int32_t out_dtype, int dq) {
+  if (M <= 0 || M > NF4_GEMV_MAX_M || N <= 0 || K <= 0) return 0;
+  if (compute_dtype == NF4_DTYPE_FP32) return 0;
+  if (single_row_path(M, K, blocksize, compute_dtype, out_dtype, dq)) return 0;
+  return (int64_t)gemv_split_bytes(M, N, K);
 }
 
 nf4_status gemm_impl(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w, int32_t N,
@@ -464,11 +481,15 @@ nf4_status gemm_impl(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w
 
 nf4_status linear_impl(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w, int32_t N,
                        int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
-                       void *y, int64_t ldy, void *stream) {
+                       void *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                       void *stream) {
   // decode shapes take the decode kernels, larger batches the prefill GEMM
   if (M >= 0 && M <= NF4_GEMV_MAX_M)
     return gemv_grouped_impl(1, &x, &ldx, M, w, &N, &K, &bias, compute_dtype, out_dtype, &y, &ldy,
-                             stream);
+                             workspace, workspace_bytes, stream);
+  if (workspace_bytes < 0 || (workspace_bytes > 0 && workspace == nullptr))
+    return NF4_ERR_INVALID_ARGUMENT;
+  if (!aligned16(workspace)) return NF4_ERR_MISALIGNED;
   return gemm_impl(x, ldx, M, w, N, K, bias, compute_dtype, out_dtype, y, ldy, stream);
 }
 
@@ -479,7 +500,7 @@ extern "C" {
 nf4_status nf4_gemv(const void *x, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                     int32_t compute_dtype, int32_t out_dtype, void *y, void *stream) {
   return gemv_grouped_impl(1, &x, nullptr, M, w, &N, &K, nullptr, compute_dtype, out_dtype, &y,
-                           nullptr, stream);
+                           nullptr, nullptr, 0, stream);
 }
 
 nf4_status nf4_gemv_grouped(int32_t count, const void *const *x, int32_t M,
@@ -487,7 +508,21 @@ nf4_status nf4_gemv_grouped(int32_t count, const void *const *x, int32_t M,
                             int32_t compute_dtype, int32_t out_dtype, void *const *y,
                             void *stream) {
   return gemv_grouped_impl(count, x, nullptr, M, w, N, K, nullptr, compute_dtype, out_dtype, y,
-                           nullptr, stream);
+                           nullptr, nullptr, 0, stream);
+}
+
+nf4_status nf4_gemv_grouped_ws(int32_t count, const void *const *x, int32_t M,
+                               const nf4_qweight *w, const int32_t *N, const int32_t *K,
+                               int32_t compute_dtype, int32_t out_dtype, void *const *y,
+                               void *workspace, int64_t workspace_bytes, void *stream) {
+  return gemv_grouped_impl(count, x, nullptr, M, w, N, K, nullptr, compute_dtype, out_dtype, y,
+                           nullptr, workspace, workspace_bytes, stream);
+}
+
+int64_t nf4_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t blocksize,
+                                   int32_t compute_dtype, int32_t out_dtype,
+                                   int32_t double_quant) {
+  return product_workspace_bytes(M, N, K, blocksize, compute_dtype, out_dtype, double_quant);
 }
 
 nf4_status nf4_gemm(const void *x, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
@@ -498,13 +533,22 @@ nf4_status nf4_gemm(const void *x, int32_t M, const nf4_qweight *w, int32_t N, i
 nf4_status nf4_linear(const void *x, int32_t M, const nf4_qweight *w, int32_t N, int32_t K,
                       const void *bias, int32_t compute_dtype, int32_t out_dtype, void *y,
                       void *stream) {
-  return linear_impl(x, K, M, w, N, K, bias, compute_dtype, out_dtype, y, N, stream);
+  return linear_impl(x, K, M, w, N, K, bias, compute_dtype, out_dtype, y, N, nullptr, 0, stream);
 }
 
 nf4_status nf4_linear_ex(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w, int32_t N,
                          int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
                          void *y, int64_t ldy, void *stream) {
-  return linear_impl(x, ldx, M, w, N, K, bias, compute_dtype, out_dtype, y, ldy, stream);
+  return linear_impl(x, ldx, M, w, N, K, bias, compute_dtype, out_dtype, y, ldy, nullptr, 0,
+                     stream);
+}
+
+nf4_status nf4_linear_ws(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w, int32_t N,
+                         int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
+                         void *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                         void *stream) {
+  return linear_impl(x, ldx, M, w, N, K, bias, compute_dtype, out_dtype, y, ldy, workspace,
+                     workspace_bytes, stream);
 }
 
 }  // extern "C"

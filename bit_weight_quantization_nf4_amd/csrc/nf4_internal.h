@@ -80,10 +80,24 @@ int gemv_max_group();
 
 // Decode products (1 <= M <= 64) on the matrix cores. All products share M,
 // K, the compute dtype (bf16 / fp16), the output dtype, the quant type (one
-// code table) and the double-quant mode; blocksizes and N may differ. A
-// product's result depends only on its own data, M and K.
+// code table) and the double-quant mode; blocksizes and N may differ (one
+// blocksize per call takes the register-resident kernel). A product's result
+// depends only on its own data, M, K and whether the call splits K: a
+// product whose activations do not fit the registers of a CU
+// (gemv_split_ranges(M, K) > 1) is split into K ranges when `workspace`
+// holds the sum of gemv_split_bytes over the call's products (fp32 partial
+// sums, 256-byte aligned per product); otherwise it streams x.
 hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int quant_type, int dq,
-                          int compute_dtype, int out_dtype, hipStream_t stream);
+                          int compute_dtype, int out_dtype, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+// 16-row MFMA tiles that hold M activation rows (1, 2 or 4).
+int gemv_row_tiles(int M);
+// K ranges a product of this M and K is split into (1: none; 0: more than
+// the kernel takes, so it streams x).
+int gemv_split_ranges(int M, int K);
+// Workspace bytes of one such product's partial sums (0 without a split).
+size_t gemv_split_bytes(int M, int N, int K);
 
 // Single-activation-row products (M = 1) for K <= gemv1_max_k(blocksize): waves own
 // whole rows; same grouping rules (contiguous x and y).

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define NF4_ABI_VERSION 2
+#define NF4_ABI_VERSION 3
 
 /* Largest M of the decode products (nf4_gemv, nf4_gemv_grouped); nf4_linear
  * sends M up to this to the decode kernels and larger M to the GEMM. */
@@ -297,6 +297,47 @@ nf4_status nf4_linear(const void *x, int32_t M, const nf4_qweight *w, int32_t N,
 nf4_status nf4_linear_ex(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w, int32_t N,
                          int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
                          void *y, int64_t ldy, void *stream);
+
+/* Bytes of device workspace nf4_linear_ws uses for one product of this shape
+ * and these types (double_quant is the nf4_double_quant_mode; blocksize as in
+ * nf4_qweight), 0 when its kernels need none. It is non-zero only for decode
+ * shapes (M <= NF4_GEMV_MAX_M, bf16 / fp16 compute) whose activations, x[M,
+ * K], do not fit the registers of one compute unit -- for example M <= 16 with
+ * K > 6144, or M > 32 with K > 2048 -- which are then split along K: each K
+ * range is summed into fp32 partials in the workspace and a second kernel adds
+ * the ranges in order [repo page ossradar.top bitsandbytes, release notes
+ * 0.50.0, "Highlights": fused 4-bit kernels for batch 2..64, chosen at run
+ * time from the shape]. At most S * M * N * 4 bytes (S <= 8 K ranges),
+ * rounded up to 256. Never negative. */
+int64_t nf4_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t blocksize,
+                                   int32_t compute_dtype, int32_t out_dtype,
+                                   int32_t double_quant);
+
+/* nf4_linear_ex with a caller-owned device workspace (16-byte aligned;
+ * workspace_bytes >= 0, and workspace non-NULL when workspace_bytes > 0,
+ * else NF4_ERR_INVALID_ARGUMENT / NF4_ERR_MISALIGNED). With workspace_bytes >=
+ * nf4_linear_workspace_bytes(M, N, K, w->blocksize, compute_dtype, out_dtype,
+ * w->double_quant) a decode product that the query sizes is split along K as
+ * described there; with less (or none) the call is nf4_linear_ex, bit for
+ * bit. The split changes the summation order, not the accuracy contract: the
+ * result is within the same fp32 bounds, and repeated calls with a workspace
+ * give identical bits. The workspace holds no state between calls; it must
+ * not be used by other work on the device while the call runs (calls on one
+ * stream may share one workspace). */
+nf4_status nf4_linear_ws(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w, int32_t N,
+                         int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
+                         void *y, int64_t ldy, void *workspace, int64_t workspace_bytes,
+                         void *stream);
+
+/* nf4_gemv_grouped with a caller-owned device workspace, as for nf4_linear_ws:
+ * with workspace_bytes at least the sum over the products of
+ * nf4_linear_workspace_bytes, every product that query sizes is split along K;
+ * each product's result is bitwise that of nf4_linear_ws on it alone with a
+ * sufficient workspace (no bias, contiguous x and y). */
+nf4_status nf4_gemv_grouped_ws(int32_t count, const void *const *x, int32_t M,
+                               const nf4_qweight *w, const int32_t *N, const int32_t *K,
+                               int32_t compute_dtype, int32_t out_dtype, void *const *y,
+                               void *workspace, int64_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

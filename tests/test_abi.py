@@ -40,7 +40,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol(nf4):
     declared = header_functions()
-    assert len(declared) == 18
+    assert len(declared) == 21
     handle = ctypes.CDLL(nf4.LIB_PATH)
     for name in declared:
         assert hasattr(handle, name), name
@@ -49,7 +49,7 @@ def test_exports_every_declared_symbol(nf4):
 
 def test_version_and_strings(nf4):
     L = nf4.lib()
-    assert L.nf4_abi_version() == 2
+    assert L.nf4_abi_version() == 3
     for s in range(5):
         assert L.nf4_status_string(s).decode().startswith("NF4_")
     assert b"unknown" in L.nf4_status_string(99)
@@ -225,3 +225,48 @@ def test_oracle_build_callable_after_submodule_import():
 
     assert oracle.ensure_built(force=False).endswith("libnf4_oracle.so")
     assert oracle.ensure_built(force=False).endswith("libnf4_oracle.so")
+
+
+def test_workspace_bytes_query(nf4):
+    """nf4_linear_workspace_bytes: zero where the dispatch splits nothing (the
+    single-row kernel, x that fits one CU's registers, fp32 compute, the GEMM,
+    more K ranges than the kernel takes); S * M * N * 4 rounded up to 256
+    otherwise (S K ranges of at most 48 / 32 / 16 chunks of 128 codes at
+    M <= 16 / 32 / 64)."""
+    q = nf4.lib().nf4_linear_workspace_bytes
+    BF, F32, F16 = 0, 1, 2
+    assert q(1, 4096, 11008, 64, BF, F32, 1) == 0          # single-row kernel
+    assert q(16, 4096, 6144, 64, BF, F32, 1) == 0          # 48 chunks fit
+    assert q(16, 4096, 6272, 64, BF, F32, 1) == 2 * 16 * 4096 * 4
+    assert q(16, 4096, 11008, 64, BF, BF, 1) == 2 * 16 * 4096 * 4
+    assert q(1, 4096, 11008, 64, F16, F16, 1) == 2 * 1 * 4096 * 4   # fp16: decode kernel
+    assert q(1, 100, 11008, 64, BF, BF, 2) == (2 * 100 * 4 + 255) // 256 * 256  # centred
+    assert q(32, 11008, 4096, 64, BF, F32, 1) == 0
+    assert q(32, 11008, 4224, 64, BF, F32, 1) == 2 * 32 * 11008 * 4
+    assert q(64, 11008, 4096, 64, BF, F32, 1) == 2 * 64 * 11008 * 4
+    assert q(64, 4096, 11008, 64, BF, F32, 1) == 6 * 64 * 4096 * 4
+    assert q(40, 33, 2176, 64, BF, F32, 0) == (2 * 40 * 33 * 4 + 255) // 256 * 256
+    assert q(64, 4096, 2048, 64, BF, F32, 1) == 0
+    assert q(64, 4096, 1 << 20, 64, BF, F32, 1) == 0      # beyond 8 K ranges: x streams
+    assert q(65, 4096, 11008, 64, BF, F32, 1) == 0         # the GEMM
+    assert q(16, 4096, 11008, 64, F32, F32, 1) == 0        # fp32 compute
+    assert q(0, 4096, 11008, 64, BF, F32, 1) == 0
+
+
+def test_workspace_argument_validation(nf4):
+    L = nf4.lib()
+    d = _desc(nf4, n=64 * 128)  # N = 64, K = 128
+    lin = lambda M, ws, nb: L.nf4_linear_ws(A, 128, M, ctypes.byref(d), 64, 128, None, 0, 1, B, 64, ws, nb, None)  # noqa: E731
+    assert lin(2, None, -1) == INVALID
+    assert lin(2, None, 256) == INVALID       # bytes without a workspace
+    assert lin(2, MIS, 256) == MISALIGNED
+    assert lin(100, None, 256) == INVALID     # the GEMM path checks it too
+    assert lin(0, None, 0) == OK              # M = 0: no-op
+    X = (ctypes.c_void_p * 1)(A)
+    Y = (ctypes.c_void_p * 1)(B)
+    Ns = (ctypes.c_int32 * 1)(64)
+    Ks = (ctypes.c_int32 * 1)(128)
+    g = lambda ws, nb: L.nf4_gemv_grouped_ws(1, X, 0, ctypes.byref(d), Ns, Ks, 0, 1, Y, ws, nb, None)  # noqa: E731
+    assert g(None, -5) == INVALID
+    assert g(MIS, 16) == MISALIGNED
+    assert g(None, 0) == OK
