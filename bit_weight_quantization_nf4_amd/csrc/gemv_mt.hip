@@ -377,10 +377,10 @@ __global__ __launch_bounds__(64 * W) void gemv_mt_kernel(MtArgs args) {
 // scale of each of its 32-code pieces from LDS. Rows of the staged item are
 // RS floats apart with RS = 4 (mod 64), so the 16 rows x (up to 4) blocks a
 // wave reads at once fall in distinct banks.
-template <int NT, int CMAX>
+template <int W, int NT, int CMAX>
 struct XStage {
   static constexpr int kRows = 16 * NT;
-  static constexpr int kTpr = 1024 / kRows;         // staging threads per row
+  static constexpr int kTpr = 64 * W / kRows;       // staging threads per row
   static constexpr int kMaxBlocks = 64 * CMAX;      // blocks of a row's K range (blocksize >= 32)
   static constexpr int kMaxPitch = kMaxBlocks + ((4 - kMaxBlocks) & 63);
   static constexpr int kSlots = (kMaxBlocks + kTpr - 1) / kTpr;
@@ -405,10 +405,9 @@ __device__ __forceinline__ void set_priority(int v) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-template <int NT, int CMAX, int D, int DQ, int CT, int MT>
-__global__ __launch_bounds__(1024) void gemv_mtx_kernel(MtArgs args) {
-  constexpr int W = 16;
-  using SD = XStage<NT, CMAX>;
+template <int W, int NT, int CMAX, int D, int DQ, int CT, int MT>
+__global__ __launch_bounds__(64 * W) void gemv_mtx_kernel(MtArgs args) {
+  using SD = XStage<W, NT, CMAX>;
   // partial-sum buffers: two (one barrier per item) where LDS allows
   constexpr int kRedFloats = W * NT * MT * 4 * 64;
   constexpr int RB = kTableBytes + 4 * (2 * kRedFloats + 2 * SD::kBufFloats) <= 160 * 1024 ? 2 : 1;
@@ -774,20 +773,37 @@ __global__ __launch_bounds__(kReduceThreads) void gemv_split_reduce_kernel(Split
   const uint32_t plane = (uint32_t)M * (uint32_t)N;  // floats of one range
   const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.part, (short)0, (int)(4u * plane * (uint32_t)S), kBufferFlags);
-  float sum[4];
+  // every range's four values are loaded before any is added (one memory
+  // round trip); ranges past S read zeros and are not added
   const uint32_t e0 = (uint32_t)m * (uint32_t)N + (uint32_t)n;
+  float v[kMaxSplit][4];
+  if ((N & 3) == 0) {  // whole quads, 16-byte aligned
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t off = n + j < N ? 4u * (e0 + j) : kOOB;
-    sum[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, 0));
-  }
-  for (int r = 1; r < S; ++r)
+    for (int r = 0; r < kMaxSplit; ++r) {
+      const uint32_t off = r < S ? 4u * (e0 + (uint32_t)r * plane) : kOOB;
+      const f32x4 t = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(prs, (int)off, 0, 0));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t off = n + j < N ? 4u * (e0 + j + (uint32_t)r * plane) : kOOB;
-      sum[j] += __builtin_bit_cast(float,
-                                   __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, 0));
+      for (int j = 0; j < 4; ++j) v[r][j] = t[j];
     }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kMaxSplit; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t off = r < S && n + j < N ? 4u * (e0 + j + (uint32_t)r * plane) : kOOB;
+        v[r][j] = __builtin_bit_cast(float,
+                                     __builtin_amdgcn_raw_buffer_load_b32(prs, (int)off, 0, 0));
+      }
+  }
+  float sum[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sum[j] = v[0][j];
+#pragma unroll
+  for (int r = 1; r < kMaxSplit; ++r)
+    if (r < S)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum[j] += v[r][j];
   const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
       (void *)P.bias, (short)0, P.bias != nullptr ? (int)(2u * (uint32_t)N) : 0, kBufferFlags);
   const int ob = args.out_dtype == kFP32 ? 4 : 2;
@@ -828,36 +844,46 @@ hipError_t launch_dq(const MtArgs &args, int grid, int dq, int ct, hipStream_t s
   return launch_ct<W, MT, NT, kDqNone>(args, grid, ct, stream);
 }
 
-template <int NT, int CMAX, int D, int DQ, int MT>
+template <int W, int NT, int CMAX, int D, int DQ, int MT>
 hipError_t launch_xct(const MtArgs &args, int grid, int ct, hipStream_t stream) {
   if (ct == kFP16)
-    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kFP16, MT>), dim3(grid), dim3(1024), 0,
-                       stream, args);
+    hipLaunchKernelGGL((gemv_mtx_kernel<W, NT, CMAX, D, DQ, kFP16, MT>), dim3(grid), dim3(64 * W),
+                       0, stream, args);
   else
-    hipLaunchKernelGGL((gemv_mtx_kernel<NT, CMAX, D, DQ, kBF16, MT>), dim3(grid), dim3(1024), 0,
-                       stream, args);
+    hipLaunchKernelGGL((gemv_mtx_kernel<W, NT, CMAX, D, DQ, kBF16, MT>), dim3(grid), dim3(64 * W),
+                       0, stream, args);
   return hipGetLastError();
 }
 
-template <int NT, int CMAX, int D, int MT>
+template <int W, int NT, int CMAX, int D, int MT>
 hipError_t launch_x(const MtArgs &args, int grid, int dq, int ct, hipStream_t stream) {
-  if (dq == kDqCentred) return launch_xct<NT, CMAX, D, kDqCentred, MT>(args, grid, ct, stream);
-  if (dq == kDqSym) return launch_xct<NT, CMAX, D, kDqSym, MT>(args, grid, ct, stream);
-  return launch_xct<NT, CMAX, D, kDqNone, MT>(args, grid, ct, stream);
+  if (dq == kDqCentred) return launch_xct<W, NT, CMAX, D, kDqCentred, MT>(args, grid, ct, stream);
+  if (dq == kDqSym) return launch_xct<W, NT, CMAX, D, kDqSym, MT>(args, grid, ct, stream);
+  return launch_xct<W, NT, CMAX, D, kDqNone, MT>(args, grid, ct, stream);
 }
 
-// the register-resident kernel for MT row tiles and a wave range of cmax
-// chunks (at most mtx_cmax(MT)); three items in flight where registers allow
-hipError_t launch_xreg(const MtArgs &args, int grid, int mt, int cmax, int dq, int ct,
+// Waves of the register-resident kernel's workgroup by row tiles: 64 activation
+// rows take 8 waves with 2 per SIMD (x of two chunks, 128 registers, and four
+// items in flight per wave), fewer rows 16 waves with 4 per SIMD.
+constexpr int xreg_waves(int mt) { return mt == 4 ? 8 : 16; }
+
+// the register-resident kernel for MT row tiles over K ranges of nchs chunks
+// (at most xreg_waves(MT) * the x chunks a wave holds); items in flight as
+// registers allow
+hipError_t launch_xreg(const MtArgs &args, int grid, int mt, int nchs, int dq, int ct,
                        hipStream_t stream) {
-  if (mt == 4) return launch_x<1, 1, 2, 4>(args, grid, dq, ct, stream);
-  if (mt == 2) {
-    if (cmax == 2) return launch_x<1, 2, 2, 2>(args, grid, dq, ct, stream);
-    return launch_x<1, 1, 3, 2>(args, grid, dq, ct, stream);
+  const int cmax = (nchs + xreg_waves(mt) - 1) / xreg_waves(mt);
+  if (mt == 4) {
+    if (cmax == 2) return launch_x<8, 1, 2, 3, 4>(args, grid, dq, ct, stream);
+    return launch_x<8, 1, 1, 4, 4>(args, grid, dq, ct, stream);
   }
-  if (cmax == 3) return launch_x<1, 3, 2, 1>(args, grid, dq, ct, stream);
-  if (cmax == 2) return launch_x<1, 2, 3, 1>(args, grid, dq, ct, stream);
-  return launch_x<1, 1, 3, 1>(args, grid, dq, ct, stream);
+  if (mt == 2) {
+    if (cmax == 2) return launch_x<16, 1, 2, 2, 2>(args, grid, dq, ct, stream);
+    return launch_x<16, 1, 1, 3, 2>(args, grid, dq, ct, stream);
+  }
+  if (cmax == 3) return launch_x<16, 1, 3, 2, 1>(args, grid, dq, ct, stream);
+  if (cmax == 2) return launch_x<16, 1, 2, 3, 1>(args, grid, dq, ct, stream);
+  return launch_x<16, 1, 1, 3, 1>(args, grid, dq, ct, stream);
 }
 
 // items of 16 nt rows over the launch's problems
@@ -910,7 +936,6 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
   const int mt = gemv_row_tiles(M);
   const int nch = (K + kChunk - 1) / kChunk;
   const int nchs = (nch + S - 1) / S;
-  const int cmax = (nchs + 15) / 16;
   const CodeTables &tb = code_tables(quant_type);
   const uint32_t xe = compute_dtype == kFP32 ? 4u : 2u;
   MtArgs args;
@@ -959,7 +984,7 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
   args.total_items = items;
   const int cu = device_cu_count();
   const int grid = items < cu ? items : cu;
-  hipError_t e = launch_xreg(args, grid, mt, cmax, dq, compute_dtype, stream);
+  hipError_t e = launch_xreg(args, grid, mt, nchs, dq, compute_dtype, stream);
   if (e != hipSuccess) return e;
   if (compute_dtype == kFP16)
     hipLaunchKernelGGL((gemv_split_reduce_kernel<kFP16>), dim3(blocks), dim3(kReduceThreads), 0,
@@ -1057,7 +1082,7 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   args.kbs = args.p[0].jn;
   args.total_items = items;
   const int grid = items < cu ? items : cu;
-  if (xreg) return launch_xreg(args, grid, MT, (nch + 15) / 16, dq, compute_dtype, stream);
+  if (xreg) return launch_xreg(args, grid, MT, nch, dq, compute_dtype, stream);
   if (MT == 1) {
     if (nt == 2) return launch_dq<16, 1, 2>(args, grid, dq, compute_dtype, stream);
     return launch_dq<16, 1, 1>(args, grid, dq, compute_dtype, stream);
