@@ -118,6 +118,9 @@ _SIGNATURES = [
      [_P, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32,
       ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P, ctypes.c_int64,
       _P]),
+    ("nf4_linear_noalloc", ctypes.c_int32,
+     [_P, ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(QWeightDesc), ctypes.c_int32,
+      ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int64, _P]),
     ("nf4_gemv_grouped_ws", ctypes.c_int32,
      [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32, ctypes.POINTER(QWeightDesc),
       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,

@@ -144,6 +144,9 @@ const char *nf4_status_string(int32_t status) {
       return "NF4_ERR_MISALIGNED: a device pointer or row stride is not 16-byte aligned";
     case NF4_ERR_DEVICE:
       return "NF4_ERR_DEVICE: no HIP device, or a HIP call or kernel launch failed";
+    case NF4_ERR_SCRATCH:
+      return "NF4_ERR_SCRATCH: the product needs more workspace than the static scratch of "
+             "nf4_linear_noalloc holds (NF4_NOALLOC_SCRATCH_BYTES)";
     default:
       return "unknown nf4 status";
   }
@@ -494,6 +497,23 @@ nf4_status linear_impl(const void *x, int64_t ldx, int32_t M, const nf4_qweight 
 }
 
 }  // namespace
+
+namespace nf4 {
+
+nf4_status linear_with_workspace(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w,
+                                 int32_t N, int32_t K, const void *bias, int32_t compute_dtype,
+                                 int32_t out_dtype, void *y, int64_t ldy, void *workspace,
+                                 int64_t workspace_bytes, void *stream) {
+  return linear_impl(x, ldx, M, w, N, K, bias, compute_dtype, out_dtype, y, ldy, workspace,
+                     workspace_bytes, stream);
+}
+
+int64_t linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t blocksize,
+                               int32_t compute_dtype, int32_t out_dtype, int32_t double_quant) {
+  return product_workspace_bytes(M, N, K, blocksize, compute_dtype, out_dtype, double_quant);
+}
+
+}  // namespace nf4
 
 extern "C" {
 

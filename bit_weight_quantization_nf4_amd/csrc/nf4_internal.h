@@ -2,6 +2,7 @@
 // and the kernel launchers. Launchers assume validated arguments.
 #pragma once
 
+#include "nf4.h"
 #include "nf4_common.h"
 
 namespace nf4 {
@@ -120,5 +121,14 @@ hipError_t launch_gemm(const void *x, int64_t ldx, int M, const uint8_t *packed,
 // activations and bias, fp32 accumulation), any M; same descriptor rules.
 hipError_t launch_matmul_f32(const GemvDesc &d, int M, int quant_type, int out_dtype,
                              hipStream_t stream);
+
+// nf4_linear_ws and nf4_linear_workspace_bytes (the ABI layer), for the
+// allocation-free entry point.
+nf4_status linear_with_workspace(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w,
+                                 int32_t N, int32_t K, const void *bias, int32_t compute_dtype,
+                                 int32_t out_dtype, void *y, int64_t ldy, void *workspace,
+                                 int64_t workspace_bytes, void *stream);
+int64_t linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t blocksize,
+                               int32_t compute_dtype, int32_t out_dtype, int32_t double_quant);
 
 }  // namespace nf4

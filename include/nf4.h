@@ -73,7 +73,8 @@ typedef enum nf4_status {
   NF4_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, negative size, bad enum, shape mismatch */
   NF4_ERR_UNSUPPORTED = 2,      /* valid request this library does not implement, or not gfx950 */
   NF4_ERR_MISALIGNED = 3,       /* a device pointer is not 16-byte aligned */
-  NF4_ERR_DEVICE = 4            /* no HIP device, or a HIP call / launch failed */
+  NF4_ERR_DEVICE = 4,           /* no HIP device, or a HIP call / launch failed */
+  NF4_ERR_SCRATCH = 5           /* more workspace than nf4_linear_noalloc's static scratch */
 } nf4_status;
 
 typedef enum nf4_quant_type { NF4_QUANT_NF4 = 0, NF4_QUANT_FP4 = 1 } nf4_quant_type;
@@ -338,6 +339,25 @@ nf4_status nf4_gemv_grouped_ws(int32_t count, const void *const *x, int32_t M,
                                const nf4_qweight *w, const int32_t *N, const int32_t *K,
                                int32_t compute_dtype, int32_t out_dtype, void *const *y,
                                void *workspace, int64_t workspace_bytes, void *stream);
+
+/* Size of the static scratch nf4_linear_noalloc uses (one per device). */
+#define NF4_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory -- code under stream capture,
+ * tight serving loops, harnesses that forbid allocation: nf4_linear_ws with
+ * the workspace taken from a static device array of NF4_NOALLOC_SCRATCH_BYTES
+ * (32 MiB) that the library holds on each device it runs on until the process
+ * ends; nothing is allocated or freed by the call. Same arguments, layouts,
+ * results (bitwise those of nf4_linear_ws with a sufficient workspace) and
+ * errors as nf4_linear_ex, plus NF4_ERR_SCRATCH, returned before anything is
+ * launched, when nf4_linear_workspace_bytes for the product exceeds
+ * NF4_NOALLOC_SCRATCH_BYTES. The scratch holds only partial sums that each
+ * call writes before reading, so it needs no clearing; but every call on one
+ * device shares it, so calls that may overlap on one device (other streams,
+ * other host threads) race and must be serialised by the caller. */
+nf4_status nf4_linear_noalloc(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w,
+                              int32_t N, int32_t K, const void *bias, int32_t compute_dtype,
+                              int32_t out_dtype, void *y, int64_t ldy, void *stream);
 
 #ifdef __cplusplus
 }
