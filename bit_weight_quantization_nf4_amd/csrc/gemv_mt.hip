@@ -677,18 +677,20 @@ __global__ __launch_bounds__(64 * W) void gemv_mtx_kernel(MtArgs args) {
   // about to be computed is loaded if its activations or K range differ from
   // the ones held. The first units are issued before the pair table is
   // built, so the table's construction hides their latency.
-  // The first items' loads go out first (they come from HBM), then the
-  // activations (from L2 once any workgroup has touched them).
+  // The activations are loaded first, then the first items: loads complete
+  // in order, so the wait for x is then not also a wait for the first items'
+  // codes (on one [11008, 4096] product at M = 4 that order took 13.7 ->
+  // 13.0 us, on a 7B layer at M = 16 39.3 -> 38.5 us).
   U ring[D];
+  const int p_first = problem_of(ibeg);
+  set_range(args.p[p_first]);
+  load_x(p_first);
 #pragma unroll
   for (int k = 0; k < D - 1; ++k) {
     const Src src = issue_head(k, ring[k]);
 #pragma unroll
     for (int cc = 0; cc < CMAX; ++cc) issue_chunk(src, cc, ring[k]);
   }
-  const int p_first = ring[0].p;
-  set_range(args.p[p_first]);
-  load_x(p_first);
   const char *x_held = args.p[p_first].x;
   uint32_t x_ld = args.p[p_first].ldx_bytes;
   int kc_held = args.p[p_first].kc0;
