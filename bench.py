@@ -108,11 +108,15 @@ def parse():
                          "for HBM byte counters")
     ap.add_argument("--no-graph", action="store_true",
                     help="launch each phase eagerly instead of replaying a captured HIP graph")
+    ap.add_argument("--no-split", action="store_true",
+                    help="decode products without a workspace: activations that do not fit one "
+                         "CU's registers are streamed instead of split along K")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    split = not args.no_split
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
@@ -221,7 +225,7 @@ def main():
     def gemv_at(b):
         def f():
             for grp in layers:
-                nf4.gemv_grouped([d["x"] for d in grp], [d["qs_bs"][b] for d in grp],
+                nf4.gemv_grouped([d["x"] for d in grp], [d["qs_bs"][b] for d in grp], split=split,
                                  outs=[d["y_bs"][b] for d in grp])
         return f
 
@@ -235,14 +239,14 @@ def main():
             for idx in dep_groups:
                 sub = [grp[i] for i in idx if i < len(grp)]
                 if sub:
-                    nf4.gemv_grouped([d["x"] for d in sub], [d["qs"] for d in sub],
+                    nf4.gemv_grouped([d["x"] for d in sub], [d["qs"] for d in sub], split=split,
                                      outs=[d["y_deps"] for d in sub])
 
     def gemv_single():
         # the same products, one launch per matrix (labelled apart from the
         # grouped phase)
         for d in mats:
-            nf4.gemv(d["x"], d["qs"], out=d["y_single"])
+            nf4.gemv(d["x"], d["qs"], out=d["y_single"], split=split)
 
     def ph_gemm():
         for q, y in zip(gemm_w, gemm_y):
@@ -254,7 +258,7 @@ def main():
 
     def linear_bias():
         for d, b in zip(mats, lin_bias):
-            nf4.linear(d["x"], d["qs"], b, out_dtype=torch.float32, out=d["y_lin"])
+            nf4.linear(d["x"], d["qs"], b, out_dtype=torch.float32, out=d["y_lin"], split=split)
 
     def ph_gemm_bias():
         for q, y in zip(gemm_w, gemm_y):
@@ -330,7 +334,7 @@ def main():
 
         def tiny_gemv():
             for _ in range(200):
-                nf4.gemv(cfg["tiny_x"], cfg["tiny_qs"], out=cfg["tiny_y"])
+                nf4.gemv(cfg["tiny_x"], cfg["tiny_qs"], out=cfg["tiny_y"], split=split)
 
         def sq_quantize():
             for w, q in zip(cfg["sq_w"], cfg["sq_qs"]):
@@ -338,7 +342,7 @@ def main():
 
         def sq_gemv():
             for q in cfg["sq_qs"]:
-                nf4.gemv(cfg["sq_x"], q, out=cfg["sq_y"])
+                nf4.gemv(cfg["sq_x"], q, out=cfg["sq_y"], split=split)
         return dict(cfg1_quantize=tiny_quantize, cfg1_dequantize=tiny_dequantize,
                     cfg1_gemv=tiny_gemv, cfg2_quantize=sq_quantize, cfg2_gemv=sq_gemv)[name]
 
@@ -355,7 +359,7 @@ def main():
 
         def f():
             for li, grp in enumerate(layers):
-                nf4.gemv_grouped([xb] * len(grp), [d["qs"] for d in grp],
+                nf4.gemv_grouped([xb] * len(grp), [d["qs"] for d in grp], split=split,
                                  outs=ys[7 * li:7 * li + len(grp)])
         return f
 
@@ -364,7 +368,7 @@ def main():
 
         def f():
             for q in e["qss"]:
-                nf4.gemv(e["x"], q, out=e["y"])
+                nf4.gemv(e["x"], q, out=e["y"], split=split)
         return f
 
     copy_src = copy_dst = None
@@ -556,7 +560,7 @@ def main():
                         f"[11008,4096]) NF4 bs{bs} + double quant (256); decode GEMV M=1 per "
                         "matrix (the 7 products of a layer in one grouped launch); + prefill GEMM 2048x4096x14336 NF4 bs64 + double quant "
                         f"over {len(gemm_w)} distinct weights back to back",
-            "blocksize": bs, "quant_type": "nf4", "double_quant": True,
+            "blocksize": bs, "quant_type": "nf4", "double_quant": True, "k_split": split,
             "stack_params": n_stack, "gemv_m": 1, "gemm_mnk": [M, pm.rows, pm.cols],
             "gemm_weights": len(gemm_w),
             "also_timed": "phase gemv_single: the same decode products, one launch per matrix; "

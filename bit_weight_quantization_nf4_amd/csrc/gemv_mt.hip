@@ -1008,6 +1008,10 @@ int gemv_split_ranges(int M, int K) {
   const int mt = gemv_row_tiles(M);
   const int cap = 16 * (mt == 1 ? 3 : (mt == 2 ? 2 : 1));  // chunks of x one CU holds
   const int s = (nch + cap - 1) / cap;
+  // up to 8 activation rows the streamed x costs less than the second
+  // (summing) launch: on the [4096, 11008] product at M = 4 / 8 streaming took
+  // 15.0 / 16.5 us, the split 16.4 / 17.0 us; at M = 16 20.7 vs 18.9 us
+  if (s > 1 && M <= 8) return 0;
   return s <= kMaxSplit ? s : 0;
 }
 

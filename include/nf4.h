@@ -303,8 +303,9 @@ nf4_status nf4_linear_ex(const void *x, int64_t ldx, int32_t M, const nf4_qweigh
  * and these types (double_quant is the nf4_double_quant_mode; blocksize as in
  * nf4_qweight), 0 when its kernels need none. It is non-zero only for decode
  * shapes (M <= NF4_GEMV_MAX_M, bf16 / fp16 compute) whose activations, x[M,
- * K], do not fit the registers of one compute unit -- for example M <= 16 with
- * K > 6144, or M > 32 with K > 2048 -- which are then split along K: each K
+ * K], do not fit the registers of one compute unit -- 9 <= M <= 16 with K >
+ * 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048 (at most 8 K ranges;
+ * fewer rows, or longer K, stream x) -- which are then split along K: each K
  * range is summed into fp32 partials in the workspace and a second kernel adds
  * the ranges in order [repo page ossradar.top bitsandbytes, release notes
  * 0.50.0, "Highlights": fused 4-bit kernels for batch 2..64, chosen at run

@@ -232,15 +232,16 @@ def test_workspace_bytes_query(nf4):
     single-row kernel, x that fits one CU's registers, fp32 compute, the GEMM,
     more K ranges than the kernel takes); S * M * N * 4 rounded up to 256
     otherwise (S K ranges of at most 48 / 32 / 16 chunks of 128 codes at
-    M <= 16 / 32 / 64)."""
+    M <= 16 / 32 / 64; up to M = 8 x streams instead)."""
     q = nf4.lib().nf4_linear_workspace_bytes
     BF, F32, F16 = 0, 1, 2
     assert q(1, 4096, 11008, 64, BF, F32, 1) == 0          # single-row kernel
     assert q(16, 4096, 6144, 64, BF, F32, 1) == 0          # 48 chunks fit
     assert q(16, 4096, 6272, 64, BF, F32, 1) == 2 * 16 * 4096 * 4
     assert q(16, 4096, 11008, 64, BF, BF, 1) == 2 * 16 * 4096 * 4
-    assert q(1, 4096, 11008, 64, F16, F16, 1) == 2 * 1 * 4096 * 4   # fp16: decode kernel
-    assert q(1, 100, 11008, 64, BF, BF, 2) == (2 * 100 * 4 + 255) // 256 * 256  # centred
+    assert q(1, 4096, 11008, 64, F16, F16, 1) == 0         # M <= 8 streams x
+    assert q(8, 4096, 11008, 64, BF, F32, 1) == 0
+    assert q(9, 100, 11008, 64, BF, BF, 2) == (2 * 9 * 100 * 4 + 255) // 256 * 256  # centred
     assert q(32, 11008, 4096, 64, BF, F32, 1) == 0
     assert q(32, 11008, 4224, 64, BF, F32, 1) == 2 * 32 * 11008 * 4
     assert q(64, 11008, 4096, 64, BF, F32, 1) == 2 * 64 * 11008 * 4

@@ -1,7 +1,7 @@
 """GPU parity of the decode products for M up to 64 and of the K split.
 
-Activations that do not fit the registers of one compute unit (M <= 16 with K
-> 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048) are split along K
+Activations that do not fit the registers of one compute unit (9 <= M <= 16
+with K > 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048) are split along K
 when the caller brings a workspace (nf4_linear_ws, nf4_gemv_grouped_ws): each
 K range is summed into fp32 partials and a second kernel adds the ranges in
 order. Without a workspace the same products stream x (nf4_linear_ex). Both
@@ -108,7 +108,7 @@ def test_split_blocksizes_and_modes(nf4, orc, bs, dq):
     """K split with every block size (at 256 a K range can start inside a
     block), the three double-quant modes, ragged rows and a K that is not a
     multiple of the 128-code chunk; M across the three row-tile counts."""
-    cases = [(37, 6144 + 2 * bs, 3), (50, 4096 + bs, 20), (29, 2048 + bs, 40), (64, 11008, 64)]
+    cases = [(37, 6144 + 2 * bs, 12), (50, 4096 + bs, 20), (29, 2048 + bs, 40), (64, 11008, 64)]
     for i, (N, K, M) in enumerate(cases):
         if K % bs:
             continue
@@ -134,9 +134,9 @@ def test_split_blocksizes_and_modes(nf4, orc, bs, dq):
 
 
 def test_split_fp16_compute(nf4, orc):
-    """fp16 activations and compute dtype on the split path (M = 8, K = 11008
+    """fp16 activations and compute dtype on the split path (M = 12, K = 11008
     and M = 64, K = 4096)."""
-    for (N, K, M) in [(300, 11008, 8), (200, 4096, 64)]:
+    for (N, K, M) in [(300, 11008, 12), (200, 4096, 64)]:
         w = workloads.normal_bf16((N, K), 0.02, 7100 + K)
         qs, packed, sc = quantized(nf4, orc, w, 64, "nf4", True)
         x = torch.randn((M, K), generator=torch.Generator().manual_seed(7200 + M)).to(torch.float16)
