@@ -377,11 +377,14 @@ __global__ __launch_bounds__(64 * W) void gemv_mt_kernel(MtArgs args) {
 // scale of each of its 32-code pieces from LDS. Rows of the staged item are
 // RS floats apart with RS = 4 (mod 64), so the 16 rows x (up to 4) blocks a
 // wave reads at once fall in distinct banks.
-template <int W, int NT, int CMAX>
+// BPC: blocks per 128-code chunk the staging is sized for (4: blocksize 32; 2:
+// blocksize 64 and up -- a range of blocksize >= 256 may start inside a block,
+// which its extra block fits in).
+template <int W, int NT, int CMAX, int BPC>
 struct XStage {
   static constexpr int kRows = 16 * NT;
   static constexpr int kTpr = 64 * W / kRows;       // staging threads per row
-  static constexpr int kMaxBlocks = 64 * CMAX;      // blocks of a row's K range (blocksize >= 32)
+  static constexpr int kMaxBlocks = W * CMAX * BPC; // blocks of a row's K range
   static constexpr int kMaxPitch = kMaxBlocks + ((4 - kMaxBlocks) & 63);
   static constexpr int kSlots = (kMaxBlocks + kTpr - 1) / kTpr;
   static constexpr int kBufFloats = kRows * kMaxPitch;
@@ -405,9 +408,9 @@ __device__ __forceinline__ void set_priority(int v) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-template <int W, int NT, int CMAX, int D, int DQ, int CT, int MT>
+template <int W, int NT, int CMAX, int D, int DQ, int CT, int MT, int BPC>
 __global__ __launch_bounds__(64 * W) void gemv_mtx_kernel(MtArgs args) {
-  using SD = XStage<W, NT, CMAX>;
+  using SD = XStage<W, NT, CMAX, BPC>;
   // partial-sum buffers: two (one barrier per item) where LDS allows
   constexpr int kRedFloats = W * NT * MT * 4 * 64;
   constexpr int RB = kTableBytes + 4 * (2 * kRedFloats + 2 * SD::kBufFloats) <= 160 * 1024 ? 2 : 1;
@@ -846,46 +849,66 @@ hipError_t launch_dq(const MtArgs &args, int grid, int dq, int ct, hipStream_t s
   return launch_ct<W, MT, NT, kDqNone>(args, grid, ct, stream);
 }
 
-template <int W, int NT, int CMAX, int D, int DQ, int MT>
+template <int W, int NT, int CMAX, int D, int DQ, int MT, int BPC>
 hipError_t launch_xct(const MtArgs &args, int grid, int ct, hipStream_t stream) {
   if (ct == kFP16)
-    hipLaunchKernelGGL((gemv_mtx_kernel<W, NT, CMAX, D, DQ, kFP16, MT>), dim3(grid), dim3(64 * W),
-                       0, stream, args);
+    hipLaunchKernelGGL((gemv_mtx_kernel<W, NT, CMAX, D, DQ, kFP16, MT, BPC>), dim3(grid),
+                       dim3(64 * W), 0, stream, args);
   else
-    hipLaunchKernelGGL((gemv_mtx_kernel<W, NT, CMAX, D, DQ, kBF16, MT>), dim3(grid), dim3(64 * W),
-                       0, stream, args);
+    hipLaunchKernelGGL((gemv_mtx_kernel<W, NT, CMAX, D, DQ, kBF16, MT, BPC>), dim3(grid),
+                       dim3(64 * W), 0, stream, args);
   return hipGetLastError();
 }
 
-template <int W, int NT, int CMAX, int D, int MT>
+template <int W, int NT, int CMAX, int D, int MT, int BPC>
 hipError_t launch_x(const MtArgs &args, int grid, int dq, int ct, hipStream_t stream) {
-  if (dq == kDqCentred) return launch_xct<W, NT, CMAX, D, kDqCentred, MT>(args, grid, ct, stream);
-  if (dq == kDqSym) return launch_xct<W, NT, CMAX, D, kDqSym, MT>(args, grid, ct, stream);
-  return launch_xct<W, NT, CMAX, D, kDqNone, MT>(args, grid, ct, stream);
+  if (dq == kDqCentred)
+    return launch_xct<W, NT, CMAX, D, kDqCentred, MT, BPC>(args, grid, ct, stream);
+  if (dq == kDqSym) return launch_xct<W, NT, CMAX, D, kDqSym, MT, BPC>(args, grid, ct, stream);
+  return launch_xct<W, NT, CMAX, D, kDqNone, MT, BPC>(args, grid, ct, stream);
 }
 
 // Waves of the register-resident kernel's workgroup by row tiles: 64 activation
-// rows take 8 waves with 2 per SIMD (x of two chunks, 128 registers, and four
-// items in flight per wave), fewer rows 16 waves with 4 per SIMD.
+// rows take 8 waves with 2 per SIMD (x of two chunks, 128 registers), fewer
+// rows 16 waves with 4 per SIMD.
 constexpr int xreg_waves(int mt) { return mt == 4 ? 8 : 16; }
 
-// the register-resident kernel for MT row tiles over K ranges of nchs chunks
-// (at most xreg_waves(MT) * the x chunks a wave holds); items in flight as
-// registers allow
+// The register-resident kernel for MT row tiles over K ranges of nchs chunks
+// (at most xreg_waves(MT) * the x chunks a wave holds), with items in flight
+// as registers allow. Staging sized for blocksize 32 takes twice the scale
+// registers of blocksize 64 and up, so those take the smaller staging and,
+// where that frees the registers, one more item in flight.
+template <int BPC>
+hipError_t launch_xreg_bpc(const MtArgs &args, int grid, int mt, int cmax, bool long_run, int dq,
+                           int ct, hipStream_t stream) {
+  if (mt == 4) {
+    // a fourth item in flight pays on long item runs (7B layer at M = 64:
+    // 89.5 -> 85.6 us) and costs on short ones, whose start-up it lengthens
+    // ([11008, 4096] at M = 64: 31.2 -> 33.1 us)
+    if (cmax == 2) {
+      if (BPC == 2 && long_run) return launch_x<8, 1, 2, 4, 4, BPC>(args, grid, dq, ct, stream);
+      return launch_x<8, 1, 2, 3, 4, BPC>(args, grid, dq, ct, stream);
+    }
+    return launch_x<8, 1, 1, 4, 4, BPC>(args, grid, dq, ct, stream);
+  }
+  if (mt == 2) {
+    if (cmax == 2) return launch_x<16, 1, 2, 2, 2, BPC>(args, grid, dq, ct, stream);
+    return launch_x<16, 1, 1, 3, 2, BPC>(args, grid, dq, ct, stream);
+  }
+  // (three items in flight with three chunks measured slower: [4096, 11008]
+  // at M = 16, 20.1 -> 22.7 us)
+  if (cmax == 3) return launch_x<16, 1, 3, 2, 1, BPC>(args, grid, dq, ct, stream);
+  if (cmax == 2) return launch_x<16, 1, 2, 3, 1, BPC>(args, grid, dq, ct, stream);
+  return launch_x<16, 1, 1, 3, 1, BPC>(args, grid, dq, ct, stream);
+}
+
 hipError_t launch_xreg(const MtArgs &args, int grid, int mt, int nchs, int dq, int ct,
                        hipStream_t stream) {
   const int cmax = (nchs + xreg_waves(mt) - 1) / xreg_waves(mt);
-  if (mt == 4) {
-    if (cmax == 2) return launch_x<8, 1, 2, 3, 4>(args, grid, dq, ct, stream);
-    return launch_x<8, 1, 1, 4, 4>(args, grid, dq, ct, stream);
-  }
-  if (mt == 2) {
-    if (cmax == 2) return launch_x<16, 1, 2, 2, 2>(args, grid, dq, ct, stream);
-    return launch_x<16, 1, 1, 3, 2>(args, grid, dq, ct, stream);
-  }
-  if (cmax == 3) return launch_x<16, 1, 3, 2, 1>(args, grid, dq, ct, stream);
-  if (cmax == 2) return launch_x<16, 1, 2, 3, 1>(args, grid, dq, ct, stream);
-  return launch_x<16, 1, 1, 3, 1>(args, grid, dq, ct, stream);
+  const bool long_run = args.total_items >= 12 * grid;  // items per workgroup
+  if (args.p[0].log2_bs == 5)
+    return launch_xreg_bpc<4>(args, grid, mt, cmax, long_run, dq, ct, stream);
+  return launch_xreg_bpc<2>(args, grid, mt, cmax, long_run, dq, ct, stream);
 }
 
 // items of 16 nt rows over the launch's problems
