@@ -611,7 +611,13 @@ __global__ __launch_bounds__(64 * W) void gemv_mtx_kernel(MtArgs args) {
 
   f32x4 acc[NT][MT];
   // chunk cc of a unit (stage buffer `buf`)
+  // The table reads of LA 8-code words go out before their arithmetic, and
+  // their LA operands are formed before their MFMAs, so the table latency is
+  // paid once per LA words and the matrix core gets LA * MT multiply-adds back
+  // to back. LA = 4 (the whole piece) in the 8-wave layout; 2 where 128
+  // registers per wave would not hold four (1 with two row tiles of x).
   auto compute_chunk = [&](const U &u, int cc, int buf) {
+    constexpr int LA = W == 8 ? 4 : (MT == 1 ? 2 : 1);
     const char *sb = reinterpret_cast<const char *>(stage) + buf * (4 * SD::kBufFloats);
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -619,10 +625,28 @@ __global__ __launch_bounds__(64 * W) void gemv_mtx_kernel(MtArgs args) {
       ap = sok[cc] ? ap : 0.0f;
       const uint32_t wd[4] = {u.w[cc][t].x, u.w[cc][t].y, u.w[cc][t].z, u.w[cc][t].w};
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint4 b = dequant8<CT>(wd[s], ap, tbl, lane_base);
+      for (int s0 = 0; s0 < 4; s0 += LA) {
+        f32x2 cv[LA][4];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32<CT>(xr[cc][mt][s], b, acc[t][mt]);
+        for (int s = 0; s < LA; ++s)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t addr =
+                __builtin_amdgcn_perm(wd[s0 + s], lane_base, 0x0c0c0000u | ((4u + j) << 8));
+            cv[s][j] = *reinterpret_cast<const f32x2 *>(tbl + addr);
+          }
+        uint4 b[LA];
+#pragma unroll
+        for (int s = 0; s < LA; ++s)
+          b[s] = make_uint4(pack2<CT>(cv[s][0].x * ap, cv[s][0].y * ap),
+                            pack2<CT>(cv[s][1].x * ap, cv[s][1].y * ap),
+                            pack2<CT>(cv[s][2].x * ap, cv[s][2].y * ap),
+                            pack2<CT>(cv[s][3].x * ap, cv[s][3].y * ap));
+#pragma unroll
+        for (int s = 0; s < LA; ++s)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[t][mt] = mfma16x16x32<CT>(xr[cc][mt][s0 + s], b[s], acc[t][mt]);
       }
     }
   };
