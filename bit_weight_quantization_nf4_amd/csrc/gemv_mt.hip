@@ -910,7 +910,8 @@ hipError_t launch_xreg_bpc(const MtArgs &args, int grid, int mt, int cmax, bool 
     // 89.5 -> 85.6 us) and costs on short ones, whose start-up it lengthens
     // ([11008, 4096] at M = 64: 31.2 -> 33.1 us)
     if (cmax == 2) {
-      if (BPC == 2 && long_run) return launch_x<8, 1, 2, 4, 4, BPC>(args, grid, dq, ct, stream);
+      if constexpr (BPC == 2)
+        if (long_run) return launch_x<8, 1, 2, 4, 4, BPC>(args, grid, dq, ct, stream);
       return launch_x<8, 1, 2, 3, 4, BPC>(args, grid, dq, ct, stream);
     }
     return launch_x<8, 1, 1, 4, 4, BPC>(args, grid, dq, ct, stream);
@@ -922,6 +923,8 @@ hipError_t launch_xreg_bpc(const MtArgs &args, int grid, int mt, int cmax, bool 
   // (three items in flight with three chunks measured slower: [4096, 11008]
   // at M = 16, 20.1 -> 22.7 us)
   if (cmax == 3) return launch_x<16, 1, 3, 2, 1, BPC>(args, grid, dq, ct, stream);
+  // (a fourth item in flight on the 7B layer at M = 4 / 16 measured 1-6 %
+  // slower)
   if (cmax == 2) return launch_x<16, 1, 2, 3, 1, BPC>(args, grid, dq, ct, stream);
   return launch_x<16, 1, 1, 3, 1, BPC>(args, grid, dq, ct, stream);
 }
