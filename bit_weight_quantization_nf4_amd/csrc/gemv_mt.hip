@@ -75,6 +75,7 @@ struct MtArgs {
   int32_t out_dtype;
   int32_t nchs;  // chunks of a K range (the waves' split), register-resident kernel
   int32_t kbs;   // staged blocks of a row's K range (the most over the problems)
+  int32_t nt;    // row tiles per item
   float value[16];
 };
 
@@ -910,8 +911,10 @@ hipError_t launch_xreg_bpc(const MtArgs &args, int grid, int mt, int cmax, bool 
     // 89.5 -> 85.6 us) and costs on short ones, whose start-up it lengthens
     // ([11008, 4096] at M = 64: 31.2 -> 33.1 us)
     if (cmax == 2) {
-      if constexpr (BPC == 2)
+      if constexpr (BPC == 2) {
+        if (args.nt == 2) return launch_x<8, 2, 2, 2, 4, BPC>(args, grid, dq, ct, stream);
         if (long_run) return launch_x<8, 1, 2, 4, 4, BPC>(args, grid, dq, ct, stream);
+      }
       return launch_x<8, 1, 2, 3, 4, BPC>(args, grid, dq, ct, stream);
     }
     return launch_x<8, 1, 1, 4, 4, BPC>(args, grid, dq, ct, stream);
@@ -976,8 +979,19 @@ void init_args(MtArgs &args, int M, int K, int out_dtype, const CodeTables &tb) 
   args.total_items = 0;
   args.nchs = (K + kChunk - 1) / kChunk;
   args.kbs = 0;
+  args.nt = 1;
   for (int i = 0; i < kMaxGroup; ++i) args.item_begin[i] = INT_MAX;
   for (int i = 0; i < 16; ++i) args.value[i] = tb.value[i];
+}
+
+// Row tiles per item of the register-resident kernel: 64-row launches (8
+// waves) at blocksize 64 and up take 32-row items when every workgroup still
+// gets at least 6 of them -- half the item ends (barrier and partial-tile
+// sums) per weight byte; otherwise, and below 64 rows, 16-row items.
+// (the 32-row kernel holds two x chunks per wave: K ranges of 9 to 16 chunks)
+int xreg_row_tiles(int count, const GemvDesc *descs, int M, int ranges, int nchs) {
+  if (gemv_row_tiles(M) != 4 || descs[0].blocksize < 64 || (nchs + 7) / 8 != 2) return 1;
+  return ranges * count_items(count, descs, 2) >= 6 * device_cu_count() ? 2 : 1;
 }
 
 // One split launch: products descs[0 .. count) (count * S <= kMaxGroup), each
@@ -993,6 +1007,8 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
   MtArgs args;
   init_args(args, M, K, kFP32, tb);
   args.nchs = nchs;
+  const int nt = xreg_row_tiles(count, descs, M, S, nchs);
+  args.nt = nt;
   SplitReduceArgs rargs;
   rargs.M = M;
   rargs.S = S;
@@ -1019,7 +1035,7 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
       if (p.jn > args.kbs) args.kbs = p.jn;
       args.item_begin[k] = items;
       p.item_begin = items;
-      items += (d.N + 15) / 16;
+      items += (d.N + 16 * nt - 1) / (16 * nt);
     }
     SplitReduceProblem &q = rargs.p[nred];
     q.part = part[i];
@@ -1112,7 +1128,7 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   // caps it (4 waves per SIMD at MT = 1 leave 128 registers: NT = 4 would
   // spill). The register-resident kernel takes one row tile per item: its
   // per-item cost is mostly the workgroup's meeting, which grows with the tile.
-  int nt = 1;
+  int nt = xreg ? xreg_row_tiles(count, descs, M, 1, nch) : 1;
   if (!xreg) {
     const int nt_max = MT == 2 ? 4 : 2;
     for (int c = 2; c <= nt_max; c *= 2)
@@ -1136,6 +1152,7 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   }
   if (args.count == 0) return hipSuccess;
   args.kbs = args.p[0].jn;
+  args.nt = nt;
   args.total_items = items;
   const int grid = items < cu ? items : cu;
   if (xreg) return launch_xreg(args, grid, MT, nch, dq, compute_dtype, stream);
