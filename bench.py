@@ -90,7 +90,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample (0 disables it)")
     ap.add_argument("--phases", default="quantize,quantize_grouped,dequantize,dequantize_grouped,"
-                                        "gemv,gemv_deps,gemv_single,linear_bias,gemm,gemm_bias,"
+                                        "gemv,gemv_deps,gemv_single,linear_bias,gemm,gemm_fused,gemm_bias,"
                                         "sweep,mlp,batched,configs",
                     help="comma list of quantize, quantize_grouped, dequantize, dequantize_grouped "
                          "(per matrix / the seven weights of a layer per call), gemv (grouped per "
@@ -98,7 +98,9 @@ def parse():
                          "{q,k,v}, {o}, {gate,up}, {down} per layer), "
                          "gemv_single (one launch per matrix), linear_bias (the same "
                          "through nf4_linear with a bf16 bias), gemm, gemm_bias (the prefill "
-                         "GEMM without / with a fused bias), "
+                         "product through nf4_linear with a workspace, without / with a fused "
+                         "bias), gemm_fused (the same through nf4_gemm, dequantization fused "
+                         "into the GEMM), "
                          "sweep (quantize, dequantize and gemv at the other blocksizes of "
                          "64/128/256), mlp (MLP-shaped decode products at M = 1, 4, 8, 16, 32, "
                          "64), batched (the stack's decode products at M = 4, 16 and 64, a layer "
@@ -249,6 +251,13 @@ def main():
             nf4.gemv(d["x"], d["qs"], out=d["y_single"], split=split)
 
     def ph_gemm():
+        # nf4_linear with a workspace: at this M the weight is dequantized once
+        # into it and the GEMM runs on the dequantized weight
+        for q, y in zip(gemm_w, gemm_y):
+            nf4.linear(px, q, out=y, split=split)
+
+    def ph_gemm_fused():
+        # nf4_gemm: the dequantization fused into the GEMM's weight tiles
         for q, y in zip(gemm_w, gemm_y):
             nf4.gemm(px, q, out=y)
 
@@ -262,7 +271,7 @@ def main():
 
     def ph_gemm_bias():
         for q, y in zip(gemm_w, gemm_y):
-            nf4.linear(px, q, gemm_bias, out=y)
+            nf4.linear(px, q, gemm_bias, out=y, split=split)
 
     # MLP-shaped products, one matrix per launch, rotating over distinct
     # weights: the stack's [11008, 4096] matrices (bs 64), and 48 seeded
@@ -382,7 +391,8 @@ def main():
     fns = dict(quantize=quantize_at(bs, True), dequantize=dequantize_at(bs), gemv=gemv_at(bs),
                gemv_single=gemv_single, gemv_deps=gemv_deps, quantize_grouped=quantize_grouped,
                dequantize_grouped=dequantize_grouped,
-               gemm=ph_gemm, copy=ph_copy, linear_bias=linear_bias, gemm_bias=ph_gemm_bias)
+               gemm=ph_gemm, gemm_fused=ph_gemm_fused, copy=ph_copy, linear_bias=linear_bias,
+               gemm_bias=ph_gemm_bias)
     for b in sweep_bs:
         fns[f"quantize_bs{b}"] = quantize_at(b, False)
         fns[f"dequantize_bs{b}"] = dequantize_at(b)
@@ -514,6 +524,7 @@ def main():
     M = prefill.ms[0]
     work["gemm"] = dict(flops=2 * M * pm.rows * pm.cols * len(gemm_w), launches=len(gemm_w))
     work["gemm_bias"] = dict(work["gemm"])
+    work["gemm_fused"] = dict(work["gemm"])
     work["linear_bias"] = dict(bytes=work["gemv"]["bytes"] + sum(2 * d["spec"].rows for d in mats),
                                launches=len(mats))
     work["copy"] = dict(bytes=2 * (1 << 30), launches=1)
@@ -565,7 +576,8 @@ def main():
             "gemm_weights": len(gemm_w),
             "also_timed": "phase gemv_single: the same decode products, one launch per matrix; "
                           "linear_bias / gemm_bias: those products and the prefill GEMM through "
-                          "nf4_linear with a fused bf16 bias; "
+                          "nf4_linear with a fused bf16 bias; gemm_fused: the prefill GEMM "
+                          "through nf4_gemm (dequantization fused into the GEMM's weight tiles); "
                           "phases quantize_grouped / dequantize_grouped: the stack's quantize / "
                           "dequantize with the seven weights of a layer in one call; "
                           "phases *_bs128/*_bs256: the stack at the other blocksizes; mlp_*: "
@@ -594,7 +606,10 @@ def main():
         us = ms["gemm"] * 1e3 / work["gemm"]["launches"]
         tf = work["gemm"]["flops"] / work["gemm"]["launches"] / us / 1e6
         result["roofline_gemm"] = {
-            "kernel": "gemm_kernel (NF4 prefill GEMM)", "bound": "mfma", "achieved": round(tf, 1),
+            "kernel": ("dequantize_kernel + gemm_w16_kernel (NF4 prefill through nf4_linear: the "
+                       "weight dequantized once, then the GEMM on it)" if split else
+                       "gemm_kernel (NF4 prefill GEMM, dequantization fused)"),
+            "bound": "mfma", "achieved": round(tf, 1),
             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic("gemm.hip"),
             "per_launch_us": round(us, 3),

@@ -56,6 +56,7 @@ constexpr uint32_t kOOB = 0x80000000u;     // an offset past every buffer
 // all but the newest n memory loads done
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 constexpr int kWaitVm0 = waitcnt_vm(0);
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (3 << 14);  // lgkmcnt(0) only
 static_assert(BM * BK * 2 == kWaves * 4 * 1024, "X tile: four 1 KB loads per wave");
 
 struct GemmArgs {
@@ -370,6 +371,221 @@ hipError_t launch_ct(const GemmArgs &args, int grid, int out_dtype, int blocksiz
             : launch_cfg<kDqSym, false, CT>(args, grid, out_dtype, stream);
 }
 
+// ---------------------------------------------------------------------------
+// The product on weights already in the compute dtype: w16 [N, K], rows ldw
+// elements apart (the dequantize kernel's output). Same tiles, wave grid and
+// MFMA order as gemm_kernel, so the result is bitwise gemm_kernel's on the
+// weight w16 was dequantized from; what differs is the pipeline. Both tiles
+// stream into LDS with no register round trip, in 32-deep steps through four
+// LDS stages, and a wave reads the next step's operands while its MFMAs run
+// on the current ones:
+//  - step ks issues the loads of step ks + 3 (into the stage step ks - 1
+//    used), reads step ks + 1's operands from LDS and runs step ks's MFMAs on
+//    operands it read during step ks - 1; one barrier per step, before which
+//    a wave waits for its loads of step ks + 2;
+//  - a stage is 256 rows of X and 256 rows of weights (the last 32 zero) of
+//    64 bytes; 16-byte chunk c of row r sits at chunk c ^ ((r / 2) mod 4), so
+//    each 8 lanes of an operand read (8 rows x 16 bytes) cover all 32 banks
+//    (a timing probe of the read patterns: this one as fast as linear reads,
+//    c ^ ((r / 4) mod 4) or no swizzle 1.75 times slower);
+//  - waves 0-3 load the X tile, waves 4-7 the weight tile, four 1 KB loads
+//    each per step.
+constexpr int BK2 = 32;
+constexpr int kStages = 4;
+
+__device__ __forceinline__ int swz2(int row, int chunk) {
+  return row * BK2 + 8 * (chunk ^ ((row >> 1) & 3));
+}
+
+struct GemmW16Args {
+  const uint16_t *x;
+  const uint16_t *w16;
+  void *y;
+  const uint16_t *bias;  // [N] in the compute dtype, or null
+  int32_t M, N, K;
+  uint32_t ldx, ldw, ldy;
+  int32_t m_tiles, n_tiles;
+  int32_t panels_by_xcd;  // n_tiles % 8 == 0: each XCD takes whole weight panels
+};
+
+template <int OUT, int CT>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_w16_kernel(GemmW16Args args) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[kStages][BM * BK2];
+  __shared__ __attribute__((aligned(16))) uint16_t ws[kStages][BM * BK2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int M = args.M, N = args.N, K = args.K;
+  // Consecutive workgroups go to the 8 XCDs in turn. With whole panels per
+  // XCD, XCD x takes weight panels x, x + 8, ... with every M tile of each, so
+  // a panel streams from memory into one XCD's L2 and its M tiles share it;
+  // otherwise M tiles vary fastest.
+  int m_tile, n_tile;
+  if (args.panels_by_xcd) {
+    const int xcd = (int)blockIdx.x & 7, jj = (int)blockIdx.x >> 3;
+    m_tile = jj % args.m_tiles;
+    n_tile = (jj / args.m_tiles) * 8 + xcd;
+  } else {
+    m_tile = (int)blockIdx.x % args.m_tiles;
+    n_tile = (int)blockIdx.x / args.m_tiles;
+  }
+  const int m0 = m_tile * BM, n0 = n_tile * BN;
+  const int nk = (K + BK2 - 1) / BK2;
+  const int x_rows = M - m0 < BM ? M - m0 : BM;
+  const int w_rows = N - n0 < BN ? N - n0 : BN;
+  const uint32_t ldx = args.ldx, ldw = args.ldw;
+  // waves 0-3: X rows, waves 4-7: weight rows; rows past the matrix read zeros
+  const bool x_side = wave < 4;
+  const __amdgpu_buffer_rsrc_t rs = x_side
+      ? __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(args.x + (int64_t)m0 * ldx), (short)0,
+            (int)(2u * ((uint32_t)(x_rows - 1) * ldx + (uint32_t)K)), kBufferFlags)
+      : __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(args.w16 + (int64_t)n0 * ldw), (short)0,
+            (int)(2u * ((uint32_t)(w_rows - 1) * ldw + (uint32_t)K)), kBufferFlags);
+  const uint32_t ld = x_side ? ldx : ldw;
+  const int row_cap = x_side ? BM : BN;
+  // this wave's four loads of step ks into stage st: load i covers tile rows
+  // 16 t .. 16 t + 15 with t = 4 (wave mod 4) + i, lane 4 r' + p landing at
+  // chunk p of row 16 t + r' (so it fetches the chunk the swizzle puts
+  // there); steps past K read zeros (offsets past the buffer)
+  auto fill = [&](int ks, int st) {
+    const int k0 = ks * BK2;
+    uint16_t *base = x_side ? xs[st] : ws[st];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * (wave & 3) + i;
+      const int r = 16 * t + (lane >> 2), p = lane & 3;
+      const int kc = k0 + 8 * (p ^ ((r >> 1) & 3));
+      const uint32_t off = (ks < nk && kc < K && r < row_cap) ? 2u * ((uint32_t)r * ld + (uint32_t)kc)
+                                                             : kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(base + t * 512), 16, (int)off, 0, 0, 0);
+    }
+  };
+
+  const bool has_bias = args.bias != nullptr;
+  float bias_n[FN];
+  {
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)args.bias, (short)0, has_bias ? (int)(2u * (uint32_t)N) : 0, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + 16 * j + (lane & 15);
+      bias_n[j] = widen16<CT>(
+          __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)n), 0, 0));
+    }
+  }
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // operand rows of this lane: A row wm*64 + 16 i + lane%16, B row
+  // wn*112 + 16 j + lane%16, k chunk lane / 16
+  const int lr = lane & 15, lc = lane >> 4;
+  auto read_ops = [&](int st, uint4 (&a)[FM], uint4 (&b)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      a[i] = *reinterpret_cast<const uint4 *>(&xs[st][swz2(wm * TM + 16 * i + lr, lc)]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      b[j] = *reinterpret_cast<const uint4 *>(&ws[st][swz2(wn * TN + 16 * j + lr, lc)]);
+  };
+  auto mfmas = [&](const uint4 (&a)[FM], const uint4 (&b)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<CT>(a[i], b[j], acc[i][j]);
+  };
+  // one step: loads of step ks + 3, operands of step ks + 1 into (an, bn),
+  // MFMAs of step ks from (ac, bc); then the wait for this wave's loads of
+  // step ks + 2 (all but the four just issued) and the barrier
+  auto step = [&](int ks, const uint4 (&ac)[FM], const uint4 (&bc)[FN], uint4 (&an)[FM],
+                  uint4 (&bn)[FN]) {
+    fill(ks + kStages - 1, (ks + kStages - 1) % kStages);
+    // (at the last step this reads a stage that is not used again)
+    read_ops((ks + 1) % kStages, an, bn);
+    mfmas(ac, bc);
+    // issue order: the loads and operand reads each behind one MFMA, so the
+    // matrix core starts right after the barrier and the reads complete under
+    // the MFMAs; all MFMAs ahead of the wait (the scheduler would otherwise
+    // sink them past the barrier and make them wait for these reads)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one memory load
+    }
+#pragma unroll
+    for (int i = 0; i < FM + FN; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, FM * FN - 4 - FM - FN, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // this step's operand reads and the loads of step ks + 2 done, then a bare
+    // barrier: a workgroup fence would make the compiler wait for every load
+    // in flight, the ones just issued included
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * (kStages - 3)) & ~(15 << 8));
+    __builtin_amdgcn_s_barrier();
+  };
+
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) fill(s, s);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  uint4 a0[FM], b0[FN], a1[FM], b1[FN];
+  read_ops(0, a0, b0);
+  // (waited here, so the loop's first MFMAs do not count these reads as
+  // possibly in flight on every later trip)
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    step(ks, a0, b0, a1, b1);
+    step(ks + 1, a1, b1, a0, b0);
+  }
+  if (ks < nk) mfmas(a0, b0);
+
+  constexpr uint32_t kOut = OUT == kFP32 ? 4u : 2u;
+  const uint32_t ldy = args.ldy;
+  const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)((char *)args.y + (int64_t)m0 * ldy * kOut), (short)0,
+      (int)(((uint32_t)(x_rows - 1) * ldy + (uint32_t)N) * kOut), kBufferFlags);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + wn * TN + 16 * j + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = wm * TM + 16 * i + 4 * (lane >> 4) + r;
+        const uint32_t off = (n < N && m < x_rows) ? ((uint32_t)m * ldy + (uint32_t)n) * kOut : kOOB;
+        const float v = has_bias ? acc[i][j][r] + bias_n[j] : acc[i][j][r];
+        if (OUT != kFP32)
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)out_bits<OUT>(v), yrs, (int)off, 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), yrs, (int)off, 0,
+                                                0);
+      }
+    }
+}
+
+template <int CT>
+hipError_t launch_w16_ct(const GemmW16Args &args, int grid, int out_dtype, hipStream_t stream) {
+  if (out_dtype == kFP32)
+    hipLaunchKernelGGL((gemm_w16_kernel<kFP32, CT>), dim3(grid), dim3(kThreads), 0, stream, args);
+  else if (out_dtype == kFP16)
+    hipLaunchKernelGGL((gemm_w16_kernel<kFP16, CT>), dim3(grid), dim3(kThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL((gemm_w16_kernel<kBF16, CT>), dim3(grid), dim3(kThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const void *x, int64_t ldx, int M, const uint8_t *packed, int N, int K,
@@ -396,6 +612,30 @@ hipError_t launch_gemm(const void *x, int64_t ldx, int M, const uint8_t *packed,
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (compute_dtype == kFP16) return launch_ct<kFP16>(args, (int)grid, out_dtype, blocksize, stream);
   return launch_ct<kBF16>(args, (int)grid, out_dtype, blocksize, stream);
+}
+
+hipError_t launch_gemm_w16(const void *x, int64_t ldx, int M, const void *w16, int64_t ldw, int N,
+                           int K, int compute_dtype, int out_dtype, void *y, int64_t ldy,
+                           const void *bias, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmW16Args args;
+  args.x = static_cast<const uint16_t *>(x);
+  args.w16 = static_cast<const uint16_t *>(w16);
+  args.y = y;
+  args.bias = static_cast<const uint16_t *>(bias);
+  args.M = M;
+  args.N = N;
+  args.K = K;
+  args.ldx = (uint32_t)ldx;
+  args.ldw = (uint32_t)ldw;
+  args.ldy = (uint32_t)ldy;
+  args.m_tiles = (M + BM - 1) / BM;
+  args.n_tiles = (N + BN - 1) / BN;
+  args.panels_by_xcd = args.n_tiles % 8 == 0;
+  const int64_t grid = (int64_t)args.m_tiles * args.n_tiles;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (compute_dtype == kFP16) return launch_w16_ct<kFP16>(args, (int)grid, out_dtype, stream);
+  return launch_w16_ct<kBF16>(args, (int)grid, out_dtype, stream);
 }
 
 }  // namespace nf4

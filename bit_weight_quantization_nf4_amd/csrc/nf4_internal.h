@@ -117,6 +117,14 @@ hipError_t launch_gemm(const void *x, int64_t ldx, int M, const uint8_t *packed,
                        int blocksize, int quant_type, const ScaleArgs &sc, int compute_dtype,
                        int out_dtype, void *y, int64_t ldy, const void *bias, hipStream_t stream);
 
+// The same GEMM with the weights already dequantized: w16 [N, K] in the
+// compute dtype, rows ldw elements apart (the tile streams into LDS like x).
+// With w16 = the dequantize kernel's output of a weight, its result is bitwise
+// launch_gemm's on that weight.
+hipError_t launch_gemm_w16(const void *x, int64_t ldx, int M, const void *w16, int64_t ldw, int N,
+                           int K, int compute_dtype, int out_dtype, void *y, int64_t ldy,
+                           const void *bias, hipStream_t stream);
+
 // Products in the fp32 compute dtype (weights RN(c a') kept in fp32, fp32
 // activations and bias, fp32 accumulation), any M; same descriptor rules.
 hipError_t launch_matmul_f32(const GemvDesc &d, int M, int quant_type, int out_dtype,

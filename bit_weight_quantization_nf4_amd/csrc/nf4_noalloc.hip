@@ -44,8 +44,12 @@ extern "C" nf4_status nf4_linear_noalloc(const void *x, int64_t ldx, int32_t M,
                                          const void *bias, int32_t compute_dtype,
                                          int32_t out_dtype, void *y, int64_t ldy, void *stream) {
   if (w == nullptr) return NF4_ERR_INVALID_ARGUMENT;
-  const int64_t need = nf4::linear_workspace_bytes(M, N, K, w->blocksize, compute_dtype,
-                                                   out_dtype, w->double_quant);
+  // decode products take their K split from the scratch; prefill products the
+  // fused GEMM (their dequantized weight would not fit)
+  const int64_t need = M <= NF4_GEMV_MAX_M
+                           ? nf4::linear_workspace_bytes(M, N, K, w->blocksize, compute_dtype,
+                                                         out_dtype, w->double_quant)
+                           : 0;
   if (need > (int64_t)kScratchBytes) return NF4_ERR_SCRATCH;
   void *ws = nullptr;
   if (need > 0) {

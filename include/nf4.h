@@ -299,10 +299,20 @@ nf4_status nf4_linear_ex(const void *x, int64_t ldx, int32_t M, const nf4_qweigh
                          int32_t K, const void *bias, int32_t compute_dtype, int32_t out_dtype,
                          void *y, int64_t ldy, void *stream);
 
+/* Prefill products (bf16 / fp16 compute) of at least this many rows take the
+ * dequantized-weight path of nf4_linear_ws when the workspace allows. */
+#define NF4_PREFILL_DEQUANT_MIN_M 1536
+
 /* Bytes of device workspace nf4_linear_ws uses for one product of this shape
  * and these types (double_quant is the nf4_double_quant_mode; blocksize as in
- * nf4_qweight), 0 when its kernels need none. It is non-zero only for decode
- * shapes (M <= NF4_GEMV_MAX_M, bf16 / fp16 compute) whose activations, x[M,
+ * nf4_qweight), 0 when its kernels need none. For a prefill product of at
+ * least NF4_PREFILL_DEQUANT_MIN_M rows (bf16 / fp16 compute) it is 2 * N * K,
+ * rounded up to 256: room for W dequantized once to the compute dtype, which
+ * the GEMM then reads instead of dequantizing each weight tile again for every
+ * 256-row tile of x [usage page icman.com.cn/news/48546, "Configuration":
+ * 4-bit weights are dequantized to the compute dtype for the matmul]. Among
+ * decode shapes (M <= NF4_GEMV_MAX_M, bf16 / fp16 compute) it is non-zero for
+ * those whose activations, x[M,
  * K], do not fit the registers of one compute unit -- 9 <= M <= 16 with K >
  * 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048 (at most 8 K ranges;
  * fewer rows, or longer K, stream x) -- which are then split along K: each K
@@ -320,8 +330,11 @@ int64_t nf4_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t bloc
  * else NF4_ERR_INVALID_ARGUMENT / NF4_ERR_MISALIGNED). With workspace_bytes >=
  * nf4_linear_workspace_bytes(M, N, K, w->blocksize, compute_dtype, out_dtype,
  * w->double_quant) a decode product that the query sizes is split along K as
- * described there; with less (or none) the call is nf4_linear_ex, bit for
- * bit. The split changes the summation order, not the accuracy contract: the
+ * described there, and a prefill product it sizes dequantizes W into the
+ * workspace and runs the GEMM on it (the same tiles, MFMA order and weight
+ * values as the fused GEMM, so bitwise nf4_linear_ex's result); with less (or
+ * none) the call is nf4_linear_ex, bit for bit. The split changes the
+ * summation order, not the accuracy contract: the
  * result is within the same fp32 bounds, and repeated calls with a workspace
  * give identical bits. The workspace holds no state between calls; it must
  * not be used by other work on the device while the call runs (calls on one
@@ -351,8 +364,9 @@ nf4_status nf4_gemv_grouped_ws(int32_t count, const void *const *x, int32_t M,
  * ends; nothing is allocated or freed by the call. Same arguments, layouts,
  * results (bitwise those of nf4_linear_ws with a sufficient workspace) and
  * errors as nf4_linear_ex, plus NF4_ERR_SCRATCH, returned before anything is
- * launched, when nf4_linear_workspace_bytes for the product exceeds
- * NF4_NOALLOC_SCRATCH_BYTES. The scratch holds only partial sums that each
+ * launched, when a decode product's nf4_linear_workspace_bytes exceeds
+ * NF4_NOALLOC_SCRATCH_BYTES. Prefill products (M > NF4_GEMV_MAX_M) take the
+ * fused GEMM and no scratch. The scratch holds only partial sums that each
  * call writes before reading, so it needs no clearing; but every call on one
  * device shares it, so calls that may overlap on one device (other streams,
  * other host threads) race and must be serialised by the caller. */

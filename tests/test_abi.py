@@ -228,11 +228,13 @@ def test_oracle_build_callable_after_submodule_import():
 
 
 def test_workspace_bytes_query(nf4):
-    """nf4_linear_workspace_bytes: zero where the dispatch splits nothing (the
-    single-row kernel, x that fits one CU's registers, fp32 compute, the GEMM,
-    more K ranges than the kernel takes); S * M * N * 4 rounded up to 256
-    otherwise (S K ranges of at most 48 / 32 / 16 chunks of 128 codes at
-    M <= 16 / 32 / 64; up to M = 8 x streams instead)."""
+    """nf4_linear_workspace_bytes: zero where the dispatch uses none (the
+    single-row kernel, x that fits one CU's registers, fp32 compute, the GEMM
+    below 1536 rows, more K ranges than the kernel takes); S * M * N * 4
+    rounded up to 256 for a decode K split (S K ranges of at most 48 / 32 / 16
+    chunks of 128 codes at M <= 16 / 32 / 64; up to M = 8 x streams instead);
+    2 * N * K rounded up to 256 for a prefill product of 1536 rows or more (the
+    weight dequantized once)."""
     q = nf4.lib().nf4_linear_workspace_bytes
     BF, F32, F16 = 0, 1, 2
     assert q(1, 4096, 11008, 64, BF, F32, 1) == 0          # single-row kernel
@@ -249,7 +251,12 @@ def test_workspace_bytes_query(nf4):
     assert q(40, 33, 2176, 64, BF, F32, 0) == (2 * 40 * 33 * 4 + 255) // 256 * 256
     assert q(64, 4096, 2048, 64, BF, F32, 1) == 0
     assert q(64, 4096, 1 << 20, 64, BF, F32, 1) == 0      # beyond 8 K ranges: x streams
-    assert q(65, 4096, 11008, 64, BF, F32, 1) == 0         # the GEMM
+    assert q(65, 4096, 11008, 64, BF, F32, 1) == 0         # the GEMM, dequantizing per tile
+    assert q(1535, 14336, 4096, 64, BF, BF, 1) == 0
+    # from 1536 rows: the weight dequantized once (2 N K bytes, rounded up to 256)
+    assert q(1536, 14336, 4096, 64, BF, BF, 1) == 2 * 14336 * 4096
+    assert q(2048, 100, 96, 32, F16, F32, 2) == (2 * 100 * 96 + 255) // 256 * 256
+    assert q(2048, 14336, 4096, 64, F32, F32, 1) == 0      # fp32 compute
     assert q(16, 4096, 11008, 64, F32, F32, 1) == 0        # fp32 compute
     assert q(0, 4096, 11008, 64, BF, F32, 1) == 0
 

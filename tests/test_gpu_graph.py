@@ -1,6 +1,7 @@
 """The C-ABI calls under HIP graph capture: quantize with double quant,
 dequantize, a grouped M = 1 decode call, the K-split decode products (their
-workspace allocated by torch during capture) and the prefill GEMM, captured
+workspace allocated by torch during capture), the prefill GEMM and a 1536-row
+prefill product that dequantizes its weight into a workspace, captured
 once and replayed several times with eager work and synchronisations between
 the replays; every replay must equal the eager results bit for bit."""
 import pytest
@@ -31,6 +32,8 @@ def _run(nf4, w_up, w_down, xs):
     out.append(nf4.linear(xs["m64_up"], qu, None, out_dtype=torch.bfloat16))              # 2 K ranges
     out.append(nf4.linear(xs["m40_down"], qd, None, out_dtype=torch.float32))             # 6 K ranges
     out.append(nf4.gemm(xs["prefill"], qu, torch.bfloat16))
+    # 1536 rows with a workspace: the weight dequantized once, then the GEMM
+    out.append(nf4.linear(xs["prefill_long"], qd, out_dtype=torch.bfloat16))
     return out
 
 
@@ -45,6 +48,7 @@ def test_graph_replays_equal_eager(nf4):
         "m64_up": workloads.normal_bf16((64, 4096), 1.0, 4407).cuda(),
         "m40_down": workloads.normal_bf16((40, 11008), 1.0, 4408).cuda(),
         "prefill": workloads.normal_bf16((300, 4096), 1.0, 4409).cuda(),
+        "prefill_long": workloads.normal_bf16((1536, 11008), 1.0, 4410).cuda(),
     }
     eager = _run(nf4, w_up, w_down, xs)
     torch.cuda.synchronize()

@@ -449,8 +449,9 @@ def test_gemm_small_shapes(nf4, orc):
 def test_gemm_prefill_config(nf4, orc):
     """Full prefill shape 2048 x 4096 x 14336, NF4 bs64 + double quant:
     quantize bit-exact; 4096 sampled outputs against the fp64 oracle; all
-    outputs: bf16 == RNE(fp32), determinism, and the first 16 rows against the
-    (separately parity-tested) GEMV kernel."""
+    outputs: bf16 == RNE(fp32), determinism, nf4_linear with a workspace (the
+    weight dequantized once) bitwise nf4_gemm, and the first 16 rows against
+    the (separately parity-tested) GEMV kernel."""
     cfg = workloads.PREFILL
     m = cfg.matrices[0]
     w = m.make()
@@ -466,6 +467,8 @@ def test_gemm_prefill_config(nf4, orc):
     y16 = nf4.gemm(xd, qs, torch.bfloat16)
     assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
     assert torch.equal(nf4.gemm(xd, qs, torch.float32), y32), "GEMM is not deterministic"
+    # nf4_linear with a workspace: the weight dequantized once, the same bits
+    assert torch.equal(nf4.linear(xd, qs, out_dtype=torch.float32), y32)
     rng = np.random.default_rng(5)
     ms = rng.integers(0, M, 4096)
     ns = rng.integers(0, N, 4096)

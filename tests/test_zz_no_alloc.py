@@ -60,8 +60,11 @@ def _ws(nf4, x, qs, bias, out):
 def test_noalloc_matches_workspace_entry_point(nf4, orc, out_dtype):
     # first call: M = 64 over [4096, 11008] (six K ranges, 6 MiB of partials);
     # second, smaller: M = 16 over [1000, 11008] (two K ranges); third: a
-    # product that needs no workspace (M = 4, K = 4096)
-    cases = [(64, 4096, 11008, 11), (16, 1000, 11008, 12), (4, 512, 4096, 13)]
+    # product that needs no workspace (M = 4, K = 4096); fourth: a prefill
+    # product that nf4_linear_ws runs on a dequantized weight and the static
+    # scratch variant through the fused GEMM (the same bits)
+    cases = [(64, 4096, 11008, 11), (16, 1000, 11008, 12), (4, 512, 4096, 13),
+             (1600, 1000, 1088, 14)]
     for M, N, K, seed in cases:
         w = workloads.normal_bf16((N, K), 0.02, 8800 + seed)
         x = workloads.normal_bf16((M, K), 1.0, 8900 + seed)
