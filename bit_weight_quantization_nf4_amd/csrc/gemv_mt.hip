@@ -1106,6 +1106,10 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   for (int i = 0; i < count; ++i)
     fits = fits && (int64_t)S * M * descs[i].N < ((int64_t)1 << 29);
   if (same_bs && S > 1 && fits && workspace != nullptr && workspace_bytes >= need) {
+    if (log_on())
+      log_msg("decode M=%d K=%d: gemv_mtx_kernel with %d row tile(s), K split into %d ranges "
+              "(%zu workspace bytes), then gemv_split_reduce_kernel; %d product(s)",
+              M, K, MT, S, need, count);
     // products in launches of at most kMaxGroup / S, each with its part buffer
     float *part[kMaxGroup];
     char *ws = static_cast<char *>(workspace);
@@ -1155,6 +1159,11 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   args.nt = nt;
   args.total_items = items;
   const int grid = items < cu ? items : cu;
+  if (log_on())
+    log_msg("decode M=%d K=%d: %s, %d row tile(s), %d-row items (%d), grid %d; %d product(s)%s",
+            M, K, xreg ? "gemv_mtx_kernel (x in registers)" : "gemv_mt_kernel (x streamed)", MT,
+            16 * nt, items, grid, args.count,
+            S > 1 && !xreg ? "; a K split needs a workspace of the queried size" : "");
   if (xreg) return launch_xreg(args, grid, MT, nch, dq, compute_dtype, stream);
   if (MT == 1) {
     if (nt == 2) return launch_dq<16, 1, 2>(args, grid, dq, compute_dtype, stream);

@@ -1,6 +1,8 @@
 // nf4_api.hip -- the extern "C" boundary of libnf4 (declared in include/nf4.h):
 // argument validation, device checks and dispatch to the kernel launchers.
 // Every check runs before the first launch, so a rejected call writes nothing.
+#include <stdarg.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -250,8 +252,12 @@ nf4_status nf4_quantize_grouped(int32_t count, const void *const *w_bf16, const 
   nf4_status st = check_device();
   if (st != NF4_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (double_quant && quantize_dq_fused(blocksize, 256))
-    return from_hip(launch_quantize_dq(count, ds, blocksize, quant_type, s));
+  const bool fused = double_quant && quantize_dq_fused(blocksize, 256);
+  if (log_on())
+    log_msg("quantize %d tensor(s) (first n=%lld) bs=%d: %s", count, (long long)n[0], blocksize,
+            fused ? "quantize_dq_kernel (double quant in the same pass)"
+                  : double_quant ? "quantize_kernel, then the second level" : "quantize_kernel");
+  if (fused) return from_hip(launch_quantize_dq(count, ds, blocksize, quant_type, s));
   for (int i = 0; i < count && st == NF4_OK; ++i) {
     if (ds[i].n == 0) continue;
     st = from_hip(
@@ -284,6 +290,10 @@ nf4_status nf4_quantize_ex(const void *w, int32_t w_dtype, int64_t rows, int64_t
   if (st != NF4_OK) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   QuantTensorDesc d{static_cast<const uint16_t *>(w), n, packed, absmax, absmax_q, absmax_scale};
+  if (log_on())
+    log_msg("quantize rows=%lld cols=%lld ld=%lld dtype=%d bs=%d double_quant=%d: %s",
+            (long long)rows, (long long)cols, (long long)ld, w_dtype, blocksize, double_quant,
+            w_dtype == NF4_DTYPE_BF16 && !strided ? "bf16 kernels" : "quantize_generic_kernel");
   if (w_dtype == NF4_DTYPE_BF16 && !strided) {
     // the bf16 kernels (one pass with the symmetric second level at 64/128/256)
     if (double_quant == NF4_DQ_SYMMETRIC && quantize_dq_fused(blocksize, 256))
@@ -352,6 +362,9 @@ nf4_status nf4_dequantize_grouped(int32_t count, const nf4_qweight *w, int32_t o
   if (!any) return NF4_OK;
   nf4_status st = check_device();
   if (st != NF4_OK) return st;
+  if (log_on())
+    log_msg("dequantize %d tensor(s) (first n=%lld) out_dtype=%d: dequantize_kernel", count,
+            (long long)w[0].n, out_dtype);
   return from_hip(launch_dequantize(count, ds, w[0].quant_type, w[0].double_quant, out_dtype,
                                     reinterpret_cast<hipStream_t>(stream)));
 }
@@ -416,8 +429,11 @@ nf4_status gemv_grouped_impl(int32_t count, const void *const *x, const int64_t 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int dq = w[0].double_quant, qt = w[0].quant_type;
   if (compute_dtype == NF4_DTYPE_FP32) {
-    for (int i = 0; i < count && st == NF4_OK; ++i)
+    for (int i = 0; i < count && st == NF4_OK; ++i) {
+      if (log_on() && descs[i].N > 0)
+        log_msg("product M=%d N=%d K=%d: matmul_f32_kernel (fp32 compute)", M, descs[i].N, K[i]);
       if (descs[i].N > 0) st = from_hip(launch_matmul_f32(descs[i], M, qt, out_dtype, s));
+    }
     return st;
   }
   GemvDesc one[NF4_GEMV_MAX_GROUP];
@@ -429,6 +445,9 @@ nf4_status gemv_grouped_impl(int32_t count, const void *const *x, const int64_t 
       done[i] = true;
     }
   if (n_one > 0) {
+    if (log_on())
+      log_msg("decode M=1: gemv1_kernel, %d product(s) in one launch (first N=%d K=%d)", n_one,
+              one[0].N, one[0].K);
     st = from_hip(launch_gemv1_grouped(n_one, one, qt, dq != NF4_DQ_NONE,
                                        out_dtype == NF4_DTYPE_BF16, s));
     if (st != NF4_OK) return st;
@@ -494,6 +513,7 @@ nf4_status gemm_impl(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (compute_dtype == NF4_DTYPE_FP32) {
     const GemvDesc d{x, w->packed, y, sc, N, K, w->blocksize, bias, ldx, ldy};
+    if (log_on()) log_msg("product M=%d N=%d K=%d: matmul_f32_kernel (fp32 compute)", M, N, K);
     return from_hip(launch_matmul_f32(d, M, w->quant_type, out_dtype, s));
   }
   const int64_t need = prefill_workspace_bytes(M, N, K, compute_dtype);
@@ -501,11 +521,17 @@ nf4_status gemm_impl(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w
     // the weight once in the compute dtype (the dequantize kernel's values,
     // the ones the fused GEMM forms tile by tile), then the GEMM on it
     DequantDesc d{w->packed, (int64_t)N * K, w->blocksize, sc, workspace};
+    if (log_on())
+      log_msg("prefill M=%d N=%d K=%d bs=%d: dequantize once into the workspace (%lld bytes), "
+              "then gemm_w16_kernel", M, N, K, w->blocksize, (long long)need);
     hipError_t e = launch_dequantize(1, &d, w->quant_type, sc.double_quant, compute_dtype, s);
     if (e != hipSuccess) return from_hip(e);
     return from_hip(launch_gemm_w16(x, ldx, M, workspace, K, N, K, compute_dtype, out_dtype, y,
                                     ldy, bias, s));
   }
+  if (log_on())
+    log_msg("prefill M=%d N=%d K=%d bs=%d: gemm_kernel (dequantization fused)%s", M, N, K,
+            w->blocksize, need > 0 ? "; workspace below the 2 N K bytes it would use" : "");
   return from_hip(launch_gemm(x, ldx, M, w->packed, N, K, w->blocksize, w->quant_type, sc,
                               compute_dtype, out_dtype, y, ldy, bias, s));
 }
@@ -528,6 +554,23 @@ nf4_status linear_impl(const void *x, int64_t ldx, int32_t M, const nf4_qweight 
 }  // namespace
 
 namespace nf4 {
+
+bool log_on() {
+  static const bool on = [] {
+    const char *v = getenv("NF4_LOG");
+    return v != nullptr && *v != '\0' && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void log_msg(const char *fmt, ...) {
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "[nf4] %s\n", line);
+}
 
 nf4_status linear_with_workspace(const void *x, int64_t ldx, int32_t M, const nf4_qweight *w,
                                  int32_t N, int32_t K, const void *bias, int32_t compute_dtype,

@@ -109,6 +109,12 @@ hipError_t launch_gemv1_grouped(int count, const GemvDesc *descs, int quant_type
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// NF4_LOG set (and not "0") in the environment: log_msg writes one line per
+// dispatch decision to stderr, prefixed "[nf4] ". log_on() reads the variable
+// once per process.
+bool log_on();
+void log_msg(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+
 // Prefill GEMM, any M, compute dtype bf16 or fp16 (x, bias), output dtype
 // kBF16 / kFP16 / kFP32; x rows ldx elements apart, y rows ldy apart.
 // bias: [N] in the compute dtype, added in fp32 before the output rounding,
