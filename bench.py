@@ -52,25 +52,33 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
-# HBM bytes per launch measured by two rocprofv3 counter passes (FETCH_SIZE, then
-# WRITE_SIZE, KiB per dispatch) over this benchmark, each scaled by what the same
-# counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.000, WRITE_SIZE x
-# 1.000); the summary is profiles/bench_7b_stack_hbm_bytes.md. A figure holds only
-# for the kernel source it was taken on (its SHA-256); after any change to that
-# source the benchmark reports null until the counters are taken again.
+# HBM bytes per launch (per call for the prefill: the dequantize launch of the
+# weight plus the GEMM) measured by two rocprofv3 counter passes (FETCH_SIZE,
+# then WRITE_SIZE, KiB per dispatch) over this benchmark, each scaled by what
+# the same counter reads for a plain 1 GiB device copy (FETCH_SIZE x 2.000,
+# WRITE_SIZE x 1.000); the summary is profiles/bench_7b_stack_hbm_bytes.md. A
+# figure holds only for the kernel sources it was taken on (their SHA-256);
+# after any change to one of them the benchmark reports null until the counters
+# are taken again.
 MEASURED_TRAFFIC = {
-    "gemv1.hip": ("7b1ccadc5157fddf8a1f38d17beacfca638e543b73d4c0a898f745af8ad4d1b1", 105754706),
-    "gemm.hip": ("8d027daf9bfc44e2f2c69d891e66ebdf3ffa75937ae131bb2dd468c70f3d9ff6", 335316992),
+    "gemv": ({"gemv1.hip": "7b1ccadc5157fddf8a1f38d17beacfca638e543b73d4c0a898f745af8ad4d1b1"},
+             105667624),
+    "gemm": ({"dequantize.hip": "1ae016441a333232dba8dbd5b07b9ef38751bc2fd662a64786aec8209bb3e1c9",
+              "gemm.hip": "1de4b49fe46fca0f023488a02c9c55bb0985bfae51d97d387f6e373065534135"},
+             593958228),
 }
 
 
-def measured_traffic(source):
+def measured_traffic(key):
     import hashlib
 
-    digest, nbytes = MEASURED_TRAFFIC[source]
-    path = os.path.join(ROOT, "bit_weight_quantization_nf4_amd", "csrc", source)
-    with open(path, "rb") as f:
-        return nbytes if hashlib.sha256(f.read()).hexdigest() == digest else None
+    digests, nbytes = MEASURED_TRAFFIC[key]
+    for source, digest in digests.items():
+        path = os.path.join(ROOT, "bit_weight_quantization_nf4_amd", "csrc", source)
+        with open(path, "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return nbytes
 
 
 def progress(msg: str) -> None:
@@ -598,7 +606,7 @@ def main():
         result["roofline"] = {
             "kernel": "gemv1_kernel (NF4 decode GEMV, M=1, one launch per layer of 7 products)",
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gemv1.hip"),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic("gemv"),
             "per_launch_us": round(us, 3),
             "algorithmic_bytes_per_launch": per_launch,
         }
@@ -611,7 +619,7 @@ def main():
                        "gemm_kernel (NF4 prefill GEMM, dequantization fused)"),
             "bound": "mfma", "achieved": round(tf, 1),
             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic("gemm.hip"),
+            "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": measured_traffic("gemm") if split else None,
             "per_launch_us": round(us, 3),
         }
     result["phases"] = phase_out
