@@ -777,6 +777,7 @@ struct SplitReduceProblem {
   char *y;               // row m at m * ldy_bytes
   const char *bias;      // [N] compute dtype, or null
   int32_t N;
+  int32_t S;             // K ranges of the problem (1 .. kMaxSplit)
   uint32_t ldy_bytes;
   int32_t block_begin;   // first workgroup of the problem
 };
@@ -784,7 +785,7 @@ struct SplitReduceProblem {
 struct SplitReduceArgs {
   int32_t block_begin[kMaxGroup];  // unused: INT_MAX
   SplitReduceProblem p[kMaxGroup];
-  int32_t M, S, out_dtype;
+  int32_t M, out_dtype;
 };
 
 constexpr int kReduceThreads = 256;
@@ -795,7 +796,7 @@ __global__ __launch_bounds__(kReduceThreads) void gemv_split_reduce_kernel(Split
 #pragma unroll
   for (int k = 1; k < kMaxGroup; ++k) p = args.block_begin[k] <= (int)blockIdx.x ? k : p;
   const SplitReduceProblem &P = args.p[p];
-  const int N = P.N, M = args.M, S = args.S;
+  const int N = P.N, M = args.M, S = P.S;
   const int n4 = (N + 3) >> 2;  // quads of a row
   const int64_t q = (int64_t)((int)blockIdx.x - P.block_begin) * kReduceThreads + threadIdx.x;
   if (q >= (int64_t)M * n4) return;
@@ -1009,12 +1010,9 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
   args.nchs = nchs;
   const int nt = xreg_row_tiles(count, descs, M, S, nchs);
   args.nt = nt;
-  SplitReduceArgs rargs;
-  rargs.M = M;
-  rargs.S = S;
-  rargs.out_dtype = out_dtype;
-  int items = 0, blocks = 0, nred = 0;
-  for (int i = 0; i < kMaxGroup; ++i) rargs.block_begin[i] = INT_MAX;
+  GemvDesc live[kMaxGroup];
+  float *live_part[kMaxGroup];
+  int items = 0, nlive = 0;
   for (int i = 0; i < count; ++i) {
     const GemvDesc &d = descs[i];
     if (d.N == 0) continue;
@@ -1037,16 +1035,8 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
       p.item_begin = items;
       items += (d.N + 16 * nt - 1) / (16 * nt);
     }
-    SplitReduceProblem &q = rargs.p[nred];
-    q.part = part[i];
-    q.y = static_cast<char *>(d.y);
-    q.bias = static_cast<const char *>(d.bias);
-    q.N = d.N;
-    q.ldy_bytes = (uint32_t)(d.ldy * (out_dtype == kFP32 ? 4 : 2));
-    q.block_begin = blocks;
-    rargs.block_begin[nred++] = blocks;
-    const int64_t quads = (int64_t)M * ((d.N + 3) / 4);
-    blocks += (int)((quads + kReduceThreads - 1) / kReduceThreads);
+    live[nlive] = d;
+    live_part[nlive++] = part[i];
   }
   if (args.count == 0) return hipSuccess;
   args.total_items = items;
@@ -1054,6 +1044,40 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
   const int grid = items < cu ? items : cu;
   hipError_t e = launch_xreg(args, grid, mt, nchs, dq, compute_dtype, stream);
   if (e != hipSuccess) return e;
+  int ranges[kMaxGroup];
+  for (int i = 0; i < nlive; ++i) ranges[i] = S;
+  return launch_gemv_split_sum(nlive, live, live_part, ranges, M, compute_dtype, out_dtype,
+                               stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemv_split_sum(int count, const GemvDesc *descs, float *const *part,
+                                 const int *S, int M, int compute_dtype, int out_dtype,
+                                 hipStream_t stream) {
+  if (count == 0) return hipSuccess;
+  if (count > kMaxGroup) return hipErrorInvalidValue;
+  for (int i = 0; i < count; ++i)
+    if (S[i] < 1 || S[i] > kMaxSplit) return hipErrorInvalidValue;
+  SplitReduceArgs rargs;
+  rargs.M = M;
+  rargs.out_dtype = out_dtype;
+  for (int i = 0; i < kMaxGroup; ++i) rargs.block_begin[i] = INT_MAX;
+  int blocks = 0;
+  for (int i = 0; i < count; ++i) {
+    const GemvDesc &d = descs[i];
+    SplitReduceProblem &q = rargs.p[i];
+    q.part = part[i];
+    q.y = static_cast<char *>(d.y);
+    q.bias = static_cast<const char *>(d.bias);
+    q.N = d.N;
+    q.S = S[i];
+    q.ldy_bytes = (uint32_t)(d.ldy * (out_dtype == kFP32 ? 4 : 2));
+    q.block_begin = blocks;
+    rargs.block_begin[i] = blocks;
+    const int64_t quads = (int64_t)M * ((d.N + 3) / 4);
+    blocks += (int)((quads + kReduceThreads - 1) / kReduceThreads);
+  }
   if (compute_dtype == kFP16)
     hipLaunchKernelGGL((gemv_split_reduce_kernel<kFP16>), dim3(blocks), dim3(kReduceThreads), 0,
                        stream, rargs);
@@ -1062,8 +1086,6 @@ hipError_t launch_split(int count, const GemvDesc *descs, float *const *part, in
                        stream, rargs);
   return hipGetLastError();
 }
-
-}  // namespace
 
 int gemv_max_group() { return kMaxGroup; }
 
@@ -1081,7 +1103,20 @@ int gemv_split_ranges(int M, int K) {
   return s <= kMaxSplit ? s : 0;
 }
 
+// The tiled kernel takes a 17..64-row product whose x the register-resident
+// kernel would split into three or more K ranges (or could not hold at all):
+// on [4096, 11008] it measured 20.5 / 25.8 us at M = 32 / 64 against 29-31 /
+// 34-35 us; with one or two ranges ([11008, 4096]) the two were even or the
+// register-resident kernel faster, and a layer launch mixing 4096- and
+// 11008-row products slower (more workgroups than one round of CUs).
+static bool use_tk(int M, int N, int K) {
+  if (M <= 16 || !gemv_tk_enabled() || gemv_tk_ranges(M, N, K) <= 0) return false;
+  const int s = gemv_split_ranges(M, K);
+  return s == 0 || s >= 3;
+}
+
 size_t gemv_split_bytes(int M, int N, int K) {
+  if (use_tk(M, N, K)) return gemv_tk_bytes(M, N, K);
   const int s = gemv_split_ranges(M, K);
   if (s <= 1 || M <= 0 || N <= 0) return 0;
   return ((size_t)s * (size_t)M * (size_t)N * 4u + 255u) & ~(size_t)255u;
@@ -1092,6 +1127,19 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
                           size_t workspace_bytes, hipStream_t stream) {
   if (count == 0 || M == 0) return hipSuccess;
   if (count > kMaxGroup || M > 64) return hipErrorInvalidValue;
+  if (M > 16) {
+    // 17..64 activation rows: the tiled kernel where use_tk picks it for every
+    // product and each K split has the workspace it needs
+    size_t tk_need = 0;
+    bool tk_ok = true;
+    for (int i = 0; i < count; ++i) {
+      tk_ok = tk_ok && use_tk(M, descs[i].N, K);
+      tk_need += gemv_tk_bytes(M, descs[i].N, K);
+    }
+    if (tk_ok && (tk_need == 0 || (workspace != nullptr && workspace_bytes >= tk_need)))
+      return launch_gemv_tk(count, descs, M, K, quant_type, dq, compute_dtype, out_dtype,
+                            workspace, stream);
+  }
   const int MT = gemv_row_tiles(M);
   const int cu = device_cu_count();
   const int nch = (K + kChunk - 1) / kChunk;

@@ -92,6 +92,27 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
                           int compute_dtype, int out_dtype, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+// The summing launch of a K split: product i's S[i] fp32 partial-sum planes
+// part[i][r][M][N_i] are added in range order, the bias (compute dtype) added,
+// and the result rounded to the output dtype into descs[i].y (row stride ldy).
+hipError_t launch_gemv_split_sum(int count, const GemvDesc *descs, float *const *part,
+                                 const int *S, int M, int compute_dtype, int out_dtype,
+                                 hipStream_t stream);
+
+// The tiled decode kernel for 17 <= M <= 64 (x staged in LDS, K split over
+// workgroups into gemv_tk_ranges(M, N, K) ranges, chosen from the product's
+// shape and the CU count; 0 where the kernel does not apply). With more than
+// one range a product needs gemv_tk_bytes(M, N, K) workspace bytes (256-byte
+// aligned, the call's products consecutive in its order). A product's result
+// depends only on its own data, its shape and the device's CU count.
+// gemv_tk_enabled() is false when NF4_DECODE_TILED=0 is set in the
+// environment (the other decode kernels then take these products).
+int gemv_tk_ranges(int M, int N, int K);
+size_t gemv_tk_bytes(int M, int N, int K);
+bool gemv_tk_enabled();
+hipError_t launch_gemv_tk(int count, const GemvDesc *descs, int M, int K, int quant_type, int dq,
+                          int compute_dtype, int out_dtype, void *workspace, hipStream_t stream);
+
 // 16-row MFMA tiles that hold M activation rows (1, 2 or 4).
 int gemv_row_tiles(int M);
 // K ranges a product of this M and K is split into (1: none; 0: more than

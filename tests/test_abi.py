@@ -232,7 +232,9 @@ def test_workspace_bytes_query(nf4):
     single-row kernel, x that fits one CU's registers, fp32 compute, the GEMM
     below 1536 rows, more K ranges than the kernel takes); S * M * N * 4
     rounded up to 256 for a decode K split (S K ranges of at most 48 / 32 / 16
-    chunks of 128 codes at M <= 16 / 32 / 64; up to M = 8 x streams instead);
+    chunks of 128 codes at M <= 16 / 32 / 64; up to M = 8 x streams instead;
+    from 17 rows, a split into three or more such ranges takes the tiled
+    kernel's split instead);
     2 * N * K rounded up to 256 for a prefill product of 1536 rows or more (the
     weight dequantized once)."""
     q = nf4.lib().nf4_linear_workspace_bytes
@@ -247,7 +249,13 @@ def test_workspace_bytes_query(nf4):
     assert q(32, 11008, 4096, 64, BF, F32, 1) == 0
     assert q(32, 11008, 4224, 64, BF, F32, 1) == 2 * 32 * 11008 * 4
     assert q(64, 11008, 4096, 64, BF, F32, 1) == 2 * 64 * 11008 * 4
-    assert q(64, 4096, 11008, 64, BF, F32, 1) == 6 * 64 * 4096 * 4
+    # three or more ranges at 17..64 rows: the tiled kernel's split, ranges of
+    # at most 16 chunks, as many as keep one round of workgroups on 256 CUs
+    # (32 blocks of 128 rows -> 8) and the partial sums within the codes' size
+    assert q(64, 4096, 11008, 64, BF, F32, 1) == 8 * 64 * 4096 * 4
+    assert q(32, 4096, 11008, 64, BF, BF, 1) == 8 * 32 * 4096 * 4
+    assert q(64, 21846, 11008, 64, BF, F32, 1) == 6 * 64 * 21846 * 4  # 171 blocks: 86 / 16 -> 6
+    assert q(64, 4096, 5120, 64, BF, F32, 1) == 5 * 64 * 4096 * 4     # cap K / (16 M) = 5
     assert q(40, 33, 2176, 64, BF, F32, 0) == (2 * 40 * 33 * 4 + 255) // 256 * 256
     assert q(64, 4096, 2048, 64, BF, F32, 1) == 0
     assert q(64, 4096, 1 << 20, 64, BF, F32, 1) == 0      # beyond 8 K ranges: x streams

@@ -218,3 +218,62 @@ def test_gemv_7b_layer_m64_split(nf4, orc):
     for y, x, qs, (rows, y_ref, wn, x16) in zip(ys, xs, qss, refs):
         assert torch.equal(y, nf4.gemv(x, qs, torch.float32))
         check(y[:, torch.as_tensor(rows, device="cuda")], y_ref, wn, x16)
+
+
+def test_tiled_decode_ragged_modes_and_groups(nf4, orc):
+    """The tiled decode kernel (17..64 rows whose x would take three or more K
+    ranges in registers): ragged N (a partial 128-row block), K that ends
+    inside a 128-code chunk and ranges with an odd number of chunks, the three
+    double-quant modes, bf16 and fp16 compute, every output against the
+    oracle; the 16-bit output equals the rounding of the fp32 run, repeated
+    runs are bitwise equal, and a grouped call over two products of one K
+    equals the single calls bit for bit."""
+    cases = [  # N, K, M, blocksize, double-quant mode, compute dtype
+        (200, 8352, 17, 32, 2, "bf16"),   # 66 chunks, the last a quarter; 8 ranges of <= 9
+        (131, 5184, 33, 64, 1, "fp16"),   # 41 chunks, the last a half; 2 blocks, the second of 3 rows
+        (4097, 4224, 64, 128, 0, "bf16"), # 33 chunks; 33 blocks, the last of 1 row
+    ]
+    for i, (N, K, M, bs, dq, ct) in enumerate(cases):
+        ws = []
+        for j, n in enumerate((N, N + 40)):
+            w = workloads.normal_bf16((n, K), 0.02, 8100 + 10 * i + j)
+            qs = nf4.quantize(dev(w), bs, "nf4", double_quant=dq)
+            p_ref, a_ref = orc.quantize(to_u16(w.reshape(-1)), bs, "nf4")
+            sc = dict(absmax=a_ref)
+            if dq == 1:
+                q, s = orc.double_quant(a_ref, 256)
+                sc = dict(absmax_q=q, absmax_scale=s)
+            elif dq == 2:
+                q, s, mu = orc.double_quant_centred(a_ref, 256)
+                sc = dict(absmax_q=q, absmax_scale=s, absmax_offset=mu)
+            ws.append((qs, p_ref, sc, n))
+        g = torch.Generator().manual_seed(8200 + i)
+        if ct == "fp16":
+            x = torch.randn((M, K), generator=g).to(torch.float16)
+            xh = x.view(torch.int16).numpy().view(np.uint16)
+            half, out16 = "fp16", torch.float16
+        else:
+            x = workloads.normal_bf16((M, K), 1.0, 8200 + i)
+            xh = to_u16(x)
+            half, out16 = "bf16", torch.bfloat16
+        xn = np.linalg.norm(orc.convert(xh, half, "fp32").astype(np.float64).reshape(M, K), axis=1)
+        xd = dev(x)
+        singles = []
+        for qs, p_ref, sc, n in ws:
+            assert nf4.workspace_bytes(M, qs, x.dtype, torch.float32) > 0, (n, K, M)
+            y_ref = orc.gemv_quantized_typed(xh, p_ref, n, K, bs, "nf4", dtype=half, **sc)
+            _, wh = orc.dequantize(p_ref, n * K, bs, "nf4", half=half, **sc)
+            wn = np.linalg.norm(orc.convert(wh, half, "fp32").astype(np.float64).reshape(n, K),
+                                axis=1)
+            y = nf4.gemv(xd, qs, torch.float32)
+            yy = y.cpu().numpy().astype(np.float64)
+            rel = np.linalg.norm(yy - y_ref) / np.linalg.norm(y_ref)
+            assert rel <= REL_L2, (i, n, rel)
+            assert np.all(np.abs(yy - y_ref) <= PER_ELEM * np.outer(xn, wn)), (i, n)
+            assert torch.equal(nf4.gemv(xd, qs, torch.float32), y), "not deterministic"
+            y16 = nf4.gemv(xd, qs, out16)
+            assert torch.equal(y16.view(torch.int16), y.to(out16).view(torch.int16))
+            singles.append(y16)
+        ys = nf4.gemv_grouped([xd, xd], [ws[0][0], ws[1][0]], out16)
+        for y, y1 in zip(ys, singles):
+            assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
