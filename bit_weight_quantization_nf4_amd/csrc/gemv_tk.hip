@@ -33,8 +33,9 @@
 //    rounds to the output dtype and stores; with S > 1 ranges it stores fp32
 //    partial sums [S][M][N] into the caller's workspace and the summing kernel
 //    of the split decode path adds the ranges in range order, then the bias.
-//    The split depends only on M and K, so a product's bits never depend on
-//    what it is grouped with.
+//    The split depends only on the product's own shape and the CU count, so
+//    its bits never depend on what it is grouped with. (The dispatch sends
+//    this kernel products of three or more ranges.)
 // Out-of-range chunks, rows past N and activation rows m >= M are offsets out
 // of the buffer resources' ranges: they read zeros and store nothing.
 #include <limits.h>
