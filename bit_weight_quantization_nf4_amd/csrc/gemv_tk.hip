@@ -428,7 +428,10 @@ int tk_chunks_per_range(int M, int N, int K) {
 
 int gemv_tk_ranges(int M, int N, int K) {
   if (M <= 16 || M > 64 || K <= 0 || N <= 0) return 0;
-  return tk_ranges(M, N, K);
+  const int s = tk_ranges(M, N, K);
+  // the partial sums are addressed with 31-bit byte offsets
+  if ((int64_t)s * M * N * 4 >= ((int64_t)1 << 31)) return 0;
+  return s;
 }
 
 size_t gemv_tk_bytes(int M, int N, int K) {
