@@ -1128,17 +1128,28 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
   if (count == 0 || M == 0) return hipSuccess;
   if (count > kMaxGroup || M > 64) return hipErrorInvalidValue;
   if (M > 16) {
-    // 17..64 activation rows: the tiled kernel where use_tk picks it for every
-    // product and each K split has the workspace it needs
+    // 17..64 activation rows: the products use_tk picks go to the tiled
+    // kernel when the call brings their workspace, the others (a launch of
+    // their own, which may use the whole workspace after it) below, so each
+    // product takes the kernel it takes alone
+    GemvDesc tk[kMaxGroup], rest[kMaxGroup];
+    int ntk = 0, nrest = 0;
     size_t tk_need = 0;
-    bool tk_ok = true;
     for (int i = 0; i < count; ++i) {
-      tk_ok = tk_ok && use_tk(M, descs[i].N, K);
-      tk_need += gemv_tk_bytes(M, descs[i].N, K);
+      if (use_tk(M, descs[i].N, K)) {
+        tk[ntk++] = descs[i];
+        tk_need += gemv_tk_bytes(M, descs[i].N, K);
+      } else {
+        rest[nrest++] = descs[i];
+      }
     }
-    if (tk_ok && (tk_need == 0 || (workspace != nullptr && workspace_bytes >= tk_need)))
-      return launch_gemv_tk(count, descs, M, K, quant_type, dq, compute_dtype, out_dtype,
-                            workspace, stream);
+    if (ntk > 0 && (tk_need == 0 || (workspace != nullptr && workspace_bytes >= tk_need))) {
+      const hipError_t e = launch_gemv_tk(ntk, tk, M, K, quant_type, dq, compute_dtype, out_dtype,
+                                          workspace, stream);
+      if (e != hipSuccess || nrest == 0) return e;
+      return launch_gemv_mt(nrest, rest, M, K, quant_type, dq, compute_dtype, out_dtype, workspace,
+                            workspace_bytes, stream);
+    }
   }
   const int MT = gemv_row_tiles(M);
   const int cu = device_cu_count();
