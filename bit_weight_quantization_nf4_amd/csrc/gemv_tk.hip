@@ -1,5 +1,5 @@
 // gemv_tk.hip -- decode products y_i[M, N_i] = x_i[M, K] . cd(dequant(W_i))^T
-// for 17 <= M <= 64 on gfx950 matrix cores, with x staged through LDS and the
+// for 9 <= M <= 64 on gfx950 matrix cores, with x staged through LDS and the
 // K dimension split over workgroups; cd is the rounding to the compute dtype
 // (bf16 or fp16).
 //
@@ -9,11 +9,11 @@
 //  quantization and the bias fused in; usage page icman.com.cn/news/48546,
 //  "Configuration": weights are dequantized to the compute dtype.]
 //
-// Why a second decode kernel. From 17 activation rows up, x of a long row no
-// longer fits the registers of a CU, and a kernel that splits K over the waves
-// of a workgroup pays, for every 16-row item, a meeting of all its waves whose
-// LDS traffic grows with M (at M = 64 four times the item's code bytes). Here
-// no wave shares an output with another wave of its group:
+// Why a second decode kernel. Once x of a long row no longer fits the
+// registers of a CU, a kernel that splits K over the waves of a workgroup
+// pays, for every 16-row item, a meeting of all its waves whose LDS traffic
+// grows with M (at M = 64 four times the item's code bytes). Here no wave
+// shares an output with another wave of its group:
 //  - a workgroup (8 waves, two per SIMD) owns a block of 128 weight rows over
 //    one K range of nchs 128-code chunks; the waves form two groups that take
 //    the even and the odd chunks of the range, and each wave of a group owns
@@ -35,7 +35,7 @@
 //    of the split decode path adds the ranges in range order, then the bias.
 //    The split depends only on the product's own shape and the CU count, so
 //    its bits never depend on what it is grouped with. (The dispatch sends
-//    this kernel products of three or more ranges.)
+//    this kernel products of two or more ranges.)
 // Out-of-range chunks, rows past N and activation rows m >= M are offsets out
 // of the buffer resources' ranges: they read zeros and store nothing.
 #include <limits.h>
@@ -128,8 +128,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   __shared__ float vals[16];
 
   const int tid = (int)threadIdx.x;
-  if (tid < 16) vals[tid] = args.value[tid];
-
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave / kWpg, wig = wave % kWpg;  // group, wave in the group
@@ -137,10 +135,27 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
   const int M = args.M, K = args.K;
 
-  // problem (blockIdx.y), row block and K range of this workgroup: the
-  // problem's fields come in one batch of argument loads, with no load
-  // waiting on another; workgroups past the problem's own count end at once
-  const TkProblem &P = args.p[blockIdx.y];
+  // problem (blockIdx.y), row block and K range of this workgroup;
+  // workgroups past the problem's own count end at once
+  const TkProblem P = args.p[blockIdx.y];
+  // every argument needed before the first memory loads, in registers before
+  // the early exit, so they come in one batch of loads (otherwise the
+  // compiler loads the count first and the rest after the branch: two round
+  // trips to the argument block)
+  asm volatile("" ::"s"(P.x), "s"(P.packed), "s"(P.absmax), "s"(P.absmax_q), "s"(P.N),
+               "s"(P.wgs), "s"(P.S), "s"(P.nchs), "s"(P.log2_bs), "s"(P.log2_bs2),
+               "s"(P.ldx_bytes), "s"(P.x_bytes), "s"(args.M), "s"(args.K),
+               "s"(args.value[0]), "s"(args.value[15]));
+  {
+    // (lane i of v gets value[i] through v_writelane: the compiler turns an
+    // index by the thread, or a chain of selects, into a vector load that
+    // wave 0 waits for first)
+    float v = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(args.value[i]), "n"(i));
+    if (tid < 16) vals[tid] = v;
+  }
   const int S = P.S;
   const int local = (int)blockIdx.x;
   if (local >= P.wgs) return;
@@ -291,8 +306,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
     issue_x(st, xr[st]);
     ring[st] = issue_codes(st);
   }
-  // the table is built while the first loads are in flight
-  __syncthreads();  // vals
+  // the table is built while the first loads are in flight (a bare barrier:
+  // a workgroup fence here would wait for all of them)
+  lds_barrier();  // vals
   // pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy;
   // consecutive threads write consecutive copies
   for (int idx = tid; idx < 256 * kCopies; idx += 64 * kWaves) {
@@ -427,7 +443,7 @@ int tk_chunks_per_range(int M, int N, int K) {
 }  // namespace
 
 int gemv_tk_ranges(int M, int N, int K) {
-  if (M <= 16 || M > 64 || K <= 0 || N <= 0) return 0;
+  if (M <= 8 || M > 64 || K <= 0 || N <= 0) return 0;
   const int s = tk_ranges(M, N, K);
   // the partial sums are addressed with 31-bit byte offsets
   if ((int64_t)s * M * N * 4 >= ((int64_t)1 << 31)) return 0;
@@ -513,8 +529,9 @@ hipError_t launch_gemv_tk(int count, const GemvDesc *descs, int M, int K, int qu
             ns > 0 ? ", then gemv_split_reduce_kernel" : "", np);
   const int mt = gemv_row_tiles(M);
   const dim3 g(grid, np);
-  hipError_t e = mt == 4 ? launch_tk_nst<4>(args, g, nst, dq, compute_dtype, stream)
-                         : launch_tk_nst<2>(args, g, nst, dq, compute_dtype, stream);
+  hipError_t e = mt == 4   ? launch_tk_nst<4>(args, g, nst, dq, compute_dtype, stream)
+                 : mt == 2 ? launch_tk_nst<2>(args, g, nst, dq, compute_dtype, stream)
+                           : launch_tk_nst<1>(args, g, nst, dq, compute_dtype, stream);
   if (e != hipSuccess || ns == 0) return e;
   return launch_gemv_split_sum(ns, split, part, ranges, M, compute_dtype, out_dtype, stream);
 }

@@ -99,14 +99,14 @@ hipError_t launch_gemv_split_sum(int count, const GemvDesc *descs, float *const 
                                  const int *S, int M, int compute_dtype, int out_dtype,
                                  hipStream_t stream);
 
-// The tiled decode kernel for 17 <= M <= 64 (x staged in LDS, K split over
+// The tiled decode kernel for 9 <= M <= 64 (x staged in LDS, K split over
 // workgroups into gemv_tk_ranges(M, N, K) ranges, chosen from the product's
 // shape and the CU count; 0 where the kernel does not apply). With more than
 // one range a product needs gemv_tk_bytes(M, N, K) workspace bytes (256-byte
 // aligned, the call's products consecutive in its order). A product's result
 // depends only on its own data, its shape and the device's CU count.
 // gemv_tk_enabled() is false when NF4_DECODE_TILED=0 is set in the
-// environment (the other decode kernels then take these products).
+// environment (the register-resident kernel then takes these products).
 int gemv_tk_ranges(int M, int N, int K);
 size_t gemv_tk_bytes(int M, int N, int K);
 bool gemv_tk_enabled();

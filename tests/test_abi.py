@@ -233,19 +233,21 @@ def test_workspace_bytes_query(nf4):
     below 1536 rows, more K ranges than the kernel takes); S * M * N * 4
     rounded up to 256 for a decode K split (S K ranges of at most 48 / 32 / 16
     chunks of 128 codes at M <= 16 / 32 / 64; up to M = 8 x streams instead;
-    from 17 rows, a split into three or more such ranges takes the tiled
-    kernel's split instead);
+    from 9 rows, a split into two or more such ranges (three or more from 17
+    rows) takes the tiled kernel's split instead);
     2 * N * K rounded up to 256 for a prefill product of 1536 rows or more (the
     weight dequantized once)."""
     q = nf4.lib().nf4_linear_workspace_bytes
     BF, F32, F16 = 0, 1, 2
     assert q(1, 4096, 11008, 64, BF, F32, 1) == 0          # single-row kernel
     assert q(16, 4096, 6144, 64, BF, F32, 1) == 0          # 48 chunks fit
-    assert q(16, 4096, 6272, 64, BF, F32, 1) == 2 * 16 * 4096 * 4
-    assert q(16, 4096, 11008, 64, BF, BF, 1) == 2 * 16 * 4096 * 4
+    # 9..16 rows with x past one CU: the tiled kernel's split (ranges of at
+    # most 16 chunks, as many as keep one round of workgroups on 256 CUs)
+    assert q(16, 4096, 6272, 64, BF, F32, 1) == 7 * 16 * 4096 * 4  # 49 chunks -> 7 x 7
+    assert q(16, 4096, 11008, 64, BF, BF, 1) == 8 * 16 * 4096 * 4
     assert q(1, 4096, 11008, 64, F16, F16, 1) == 0         # M <= 8 streams x
     assert q(8, 4096, 11008, 64, BF, F32, 1) == 0
-    assert q(9, 100, 11008, 64, BF, BF, 2) == (2 * 9 * 100 * 4 + 255) // 256 * 256  # centred
+    assert q(9, 100, 11008, 64, BF, BF, 2) == (8 * 9 * 100 * 4 + 255) // 256 * 256  # centred
     assert q(32, 11008, 4096, 64, BF, F32, 1) == 0
     assert q(32, 11008, 4224, 64, BF, F32, 1) == 2 * 32 * 11008 * 4
     assert q(64, 11008, 4096, 64, BF, F32, 1) == 2 * 64 * 11008 * 4

@@ -49,8 +49,8 @@ def test_log_lines_name_each_dispatch():
     assert "dequantize 1 tensor(s) (first n=4931584) out_dtype=0: dequantize_kernel" in text, text
     assert "decode M=1: gemv1_kernel" in text, text
     assert "decode M=4 K=11008: gemv_mt_kernel (x streamed)" in text, text
-    assert "decode M=16 K=11008: gemv_mtx_kernel with 1 row tile(s), K split into 2 ranges" in text, \
-        text
+    assert ("decode M=16 K=11008: gemv_tk_kernel (x staged in LDS; first product in 8 K range(s) "
+            "of 11 chunks), 6 steps, grid 32 x 1, then gemv_split_reduce_kernel") in text, text
     # 448 rows = 4 blocks of 128: 8 K ranges (at most K / (16 M) = 21), 11 chunks each
     assert ("decode M=32 K=11008: gemv_tk_kernel (x staged in LDS; first product in 8 K range(s) "
             "of 11 chunks), 6 steps, grid 32 x 1, then gemv_split_reduce_kernel") in text, text
@@ -59,13 +59,15 @@ def test_log_lines_name_each_dispatch():
 
 
 def test_tiled_decode_switch():
-    """NF4_DECODE_TILED=0 keeps a 32-row product on the register-resident
-    kernel's split (3 K ranges of at most 32 chunks)."""
+    """NF4_DECODE_TILED=0 keeps 16- and 32-row products on the register-
+    resident kernel's split (2 / 3 K ranges of at most 48 / 32 chunks)."""
     r = _run({"NF4_LOG": "1", "NF4_DECODE_TILED": "0"})
     assert r.returncode == 0, r.stderr[-2000:]
     text = "\n".join(ln for ln in r.stderr.splitlines() if ln.startswith("[nf4] "))
     assert "gemv_tk_kernel" not in text, text
     assert "decode M=32 K=11008: gemv_mtx_kernel with 2 row tile(s), K split into 3 ranges" in text, \
+        text
+    assert "decode M=16 K=11008: gemv_mtx_kernel with 1 row tile(s), K split into 2 ranges" in text, \
         text
 
 
