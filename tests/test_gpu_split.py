@@ -4,7 +4,8 @@ Activations that do not fit the registers of one compute unit (9 <= M <= 16
 with K > 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048) are split along K
 when the caller brings a workspace (nf4_linear_ws, nf4_gemv_grouped_ws): each
 K range is summed into fp32 partials and a second kernel adds the ranges in
-order. Without a workspace the same products stream x (nf4_linear_ex). Both
+order. Where that split would take two (M <= 16) or three (M > 16) or more
+ranges, the tiled kernel (x staged in LDS, its own split) takes the product. Without a workspace the same products stream x (nf4_linear_ex). Both
 are held to the product bar against the fp64 oracle: rel-L2 <= 1e-4 and
 |y - y_ref| <= 1e-3 ||w_row|| ||x_row|| (+ 1e-3 |bias|), bf16 output = RNE of
 the fp32-output run, repeated runs bitwise identical, and a grouped call equal
