@@ -28,9 +28,9 @@ def _run(nf4, w_up, w_down, xs):
     out = [qu.packed, qu.absmax_q, qu.absmax_scale, qd.packed]
     out.append(nf4.dequantize(qd, torch.bfloat16))
     out += nf4.gemv_grouped([xs["m1_up"], xs["m1_down"]], [qu, qd], torch.float32)
-    out.append(nf4.linear(xs["m16_down"], qd, xs["bias_down"], out_dtype=torch.float32))  # 2 K ranges
+    out.append(nf4.linear(xs["m16_down"], qd, xs["bias_down"], out_dtype=torch.float32))  # tiled, 8 ranges
     out.append(nf4.linear(xs["m64_up"], qu, None, out_dtype=torch.bfloat16))              # 2 K ranges
-    out.append(nf4.linear(xs["m40_down"], qd, None, out_dtype=torch.float32))             # 6 K ranges
+    out.append(nf4.linear(xs["m40_down"], qd, None, out_dtype=torch.float32))             # tiled, 8 ranges
     out.append(nf4.gemm(xs["prefill"], qu, torch.bfloat16))
     # 1536 rows with a workspace: the weight dequantized once, then the GEMM
     out.append(nf4.linear(xs["prefill_long"], qd, out_dtype=torch.bfloat16))
