@@ -278,3 +278,29 @@ def test_tiled_decode_ragged_modes_and_groups(nf4, orc):
         ys = nf4.gemv_grouped([xd, xd], [ws[0][0], ws[1][0]], out16)
         for y, y1 in zip(ys, singles):
             assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+
+
+def test_tiled_decode_strided_x_and_y(nf4, orc):
+    """The tiled kernel's products on a row-strided activation slice, writing
+    (through the summing kernel) into a row-strided output window with a
+    bias: bitwise the contiguous call, the rest of the output buffer
+    untouched, and within the bar of the oracle."""
+    N, K, M = 300, 8256, 24  # 65 chunks: three K ranges of the register-resident split
+    w = workloads.normal_bf16((N, K), 0.02, 8301)
+    qs, packed, sc = quantized(nf4, orc, w, 64, "nf4", True)
+    big = workloads.normal_bf16((M, K + 64), 1.0, 8302)
+    x = dev(big)[:, 32:32 + K]
+    bias = workloads.normal_bf16((N,), 0.5, 8303)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        ref = nf4.linear(x.contiguous(), qs, dev(bias), out_dtype)
+        out = torch.full((M, N + 24), 7.0, device="cuda", dtype=out_dtype)
+        win = out[:, 8:8 + N]
+        nf4.linear(x, qs, dev(bias), out_dtype, out=win)
+        assert torch.equal(win, ref)
+        assert torch.all(out[:, :8] == 7.0) and torch.all(out[:, 8 + N:] == 7.0)
+    x16 = to_u16(big[:, 32:32 + K].contiguous())
+    b16 = to_u16(bias)
+    y_ref = orc.gemv_quantized_threads(x16, packed, N, K, THREADS, 64, "nf4", **sc)
+    y_ref = y_ref + u16_to_f64(b16)[None, :]
+    check(nf4.linear(x, qs, dev(bias), torch.float32), y_ref, wc_norms(orc, packed, N, K, 64, "nf4", sc),
+          x16, b16)
