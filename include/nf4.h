@@ -317,7 +317,12 @@ nf4_status nf4_linear_ex(const void *x, int64_t ldx, int32_t M, const nf4_qweigh
  * 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048 (at most 8 K ranges;
  * fewer rows, or longer K, stream x) -- which are then split along K: each K
  * range is summed into fp32 partials in the workspace and a second kernel adds
- * the ranges in order [repo page ossradar.top bitsandbytes, release notes
+ * the ranges in order. Where that split would take two (M <= 16) or three
+ * (M > 16) or more ranges and K <= 16384, a tiled kernel takes the product
+ * with a split of its own (up to 8 ranges of at most 2048 codes, as many as
+ * keep the product within one round of workgroups on the device's compute
+ * units), so the size depends on N and the CU count as well [repo page
+ * ossradar.top bitsandbytes, release notes
  * 0.50.0, "Highlights": fused 4-bit kernels for batch 2..64, chosen at run
  * time from the shape]. At most S * M * N * 4 bytes (S <= 8 K ranges),
  * rounded up to 256. Never negative. */
