@@ -24,7 +24,9 @@
 //    two LDS stages; the 16-byte pieces of an x row sit at
 //    piece ^ (row mod 16), so the MFMA operand reads (16 rows, one piece
 //    each) and the row writes cover all banks. One barrier per step;
-//  - a wave's code words and block scales are loaded three steps ahead; dequantization goes through the conflict-free
+//  - a wave's code words and block scales are loaded three steps ahead, and
+//    dequantized one step ahead, between the MFMAs of the step before (2-3 %
+//    faster than dequantizing a step's weights ahead of its own MFMAs); dequantization goes through the conflict-free
 //    LDS pair table (entry = fp32 code values of both nibbles of a code byte,
 //    32 interleaved copies, address built by one v_perm_b32), times the block
 //    scale, rounded to the compute dtype in pairs -- the dequantize kernel's
@@ -269,11 +271,30 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int stage, const TkCodes &u) {
+  // The weights of a step, dequantized to MFMA B operands (row tile t, 8-code
+  // word s).
+  struct TkB {
+    uint4 b[kNtw][4];
+  };
+  auto dequant = [&](const TkCodes &u) {
+    TkB r;
+#pragma unroll
+    for (int t = 0; t < kNtw; ++t) {
+      const float ap = scale_from<DQ>(u.q[t], u.s[t], u.mu[t]);
+      const uint32_t wd[4] = {u.w[t].x, u.w[t].y, u.w[t].z, u.w[t].w};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) r.b[t][s] = tk_dequant8<CT>(wd[s], ap, tbl, lane_base);
+    }
+    return r;
+  };
+  // One step's MFMAs on weights dequantized during the step before, with the
+  // next step's dequantization interleaved: the matrix core runs while the
+  // wave's VALU and table reads work on the next weights.
+  auto compute = [&](int stage, const TkB &cur, const TkCodes &next, TkB &nb) {
+    const char *xb = xs + stage * kStageBytes + grp * kXRows * kXRowBytes;
     float ap[kNtw];
 #pragma unroll
-    for (int t = 0; t < kNtw; ++t) ap[t] = scale_from<DQ>(u.q[t], u.s[t], u.mu[t]);
-    const char *xb = xs + stage * kStageBytes + grp * kXRows * kXRowBytes;
+    for (int t = 0; t < kNtw; ++t) ap[t] = scale_from<DQ>(next.q[t], next.s[t], next.mu[t]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 xa[MT];
@@ -284,10 +305,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
       }
 #pragma unroll
       for (int t = 0; t < kNtw; ++t) {
-        const uint32_t word = s == 0 ? u.w[t].x : s == 1 ? u.w[t].y : s == 2 ? u.w[t].z : u.w[t].w;
-        const uint4 b = tk_dequant8<CT>(word, ap[t], tbl, lane_base);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[t][mt] = mfma16x16x32<CT>(xa[mt], b, acc[t][mt]);
+        for (int mt = 0; mt < MT; ++mt)
+          acc[t][mt] = mfma16x16x32<CT>(xa[mt], cur.b[t][s], acc[t][mt]);
+        const uint32_t word =
+            s == 0 ? next.w[t].x : s == 1 ? next.w[t].y : s == 2 ? next.w[t].z : next.w[t].w;
+        nb.b[t][s] = tk_dequant8<CT>(word, ap[t], tbl, lane_base);
       }
     }
   };
@@ -319,6 +342,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
 
   store_x(0, xr[0]);
   lds_barrier();  // table and stage 0
+  TkB bq[NST + 1];
+  bq[0] = dequant(ring[0]);
 
 #pragma unroll
   for (int st = 0; st < NST; ++st) {
@@ -330,7 +355,8 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
     // the loads stay ahead of the arithmetic, so the compiler's waits count
     // them as the newest in flight
     __builtin_amdgcn_sched_barrier(0);
-    compute(st & 1, ring[st]);
+    // (past the last step the codes read zeros: that dequantization is unused)
+    compute(st & 1, bq[st], ring[st + 1 < NST ? st + 1 : st], bq[st + 1]);
     __builtin_amdgcn_sched_barrier(0);
     if (st + 1 < NST) store_x((st + 1) & 1, xr[st + 1]);  // zeros past the range
     lds_barrier();
