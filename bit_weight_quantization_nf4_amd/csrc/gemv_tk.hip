@@ -127,7 +127,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   constexpr int kXLoads = kStageBytes / (16 * 64 * kWaves);  // 16-byte loads per thread
   __shared__ __attribute__((aligned(16))) char tbl[kTableBytes];
   __shared__ __attribute__((aligned(16))) char xs[2 * kStageBytes];
-  __shared__ float vals[16];
 
   const int tid = (int)threadIdx.x;
   const int lane = tid & 63;
@@ -146,18 +145,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   // trips to the argument block)
   asm volatile("" ::"s"(P.x), "s"(P.packed), "s"(P.absmax), "s"(P.absmax_q), "s"(P.N),
                "s"(P.wgs), "s"(P.S), "s"(P.nchs), "s"(P.log2_bs), "s"(P.log2_bs2),
-               "s"(P.ldx_bytes), "s"(P.x_bytes), "s"(args.M), "s"(args.K),
-               "s"(args.value[0]), "s"(args.value[15]));
-  {
-    // (lane i of v gets value[i] through v_writelane: the compiler turns an
-    // index by the thread, or a chain of selects, into a vector load that
-    // wave 0 waits for first)
-    float v = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(args.value[i]), "n"(i));
-    if (tid < 16) vals[tid] = v;
-  }
+               "s"(P.ldx_bytes), "s"(P.x_bytes), "s"(args.M), "s"(args.K));
   const int S = P.S;
   const int local = (int)blockIdx.x;
   if (local >= P.wgs) return;
@@ -329,15 +317,21 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
     issue_x(st, xr[st]);
     ring[st] = issue_codes(st);
   }
-  // the table is built while the first loads are in flight (a bare barrier:
-  // a workgroup fence here would wait for all of them)
-  lds_barrier();  // vals
-  // pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy;
-  // consecutive threads write consecutive copies
-  for (int idx = tid; idx < 256 * kCopies; idx += 64 * kWaves) {
-    const int e = idx >> 5;
-    const f32x2 v = {vals[e >> 4], vals[e & 15]};
-    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * (idx & 31)) = v;
+  // The pair table, built while the first loads are in flight: entry
+  // e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy. Iteration i of wave
+  // w writes entry 16 i + 2 w (lanes 0-31) and the next one (lanes 32-63),
+  // copy = lane mod 32; both take value[i] and one of two low values, so
+  // every value comes from scalar registers (no staging in LDS, no barrier).
+  float lo0 = args.value[2 * wave], lo1 = args.value[2 * wave + 1];
+  // (in scalar registers first: a select between the two would otherwise be
+  // folded into a vector load indexed by the lane)
+  asm volatile("" : "+s"(lo0), "+s"(lo1));
+#pragma unroll
+  for (int i = 0; i < 256 / (2 * kWaves); ++i) {
+    const float hi = args.value[i];
+    const float lo = lane < 32 ? lo0 : lo1;
+    const int e = 16 * i + 2 * wave + (lane >> 5);
+    *reinterpret_cast<f32x2 *>(tbl + 256 * e + 8 * (lane & 31)) = f32x2{hi, lo};
   }
 
   store_x(0, xr[0]);
