@@ -157,7 +157,6 @@ void gemv1_kernel(Gemv1Args args) {
   // piece read (same q) and the 16 threads of a store (8 q's, 2 l's) each
   // cover all 16 bank groups, so neither conflicts
   __shared__ uint4 xs[J * 512];
-  __shared__ f32x4 vs[4];  // the 16 code values, for the table build
 
   const int lane = threadIdx.x & 63;
   const uint32_t lane_base = 8u * (uint32_t)(lane & (kCopies - 1));
@@ -182,11 +181,6 @@ void gemv1_kernel(Gemv1Args args) {
   for (int i = 0; i < 16; ++i) val[i] = args.value[i];
   // keep these loads in the first batch, ahead of the wave's vector loads
   __builtin_amdgcn_sched_barrier(0);
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vs[i] = f32x4{val[4 * i], val[4 * i + 1], val[4 * i + 2], val[4 * i + 3]};
-  }
   int pi = -1, g = 0, ng = 1, nrows = 0;
 #pragma unroll
   for (int i = 0; i < kMaxGroup; ++i) {
@@ -371,17 +365,34 @@ void gemv1_kernel(Gemv1Args args) {
     // Pair table, entry e = (value[e >> 4], value[e & 15]) at 256 e + 8 copy,
     // built while the first loads are in flight, two copies per 16-byte
     // store; consecutive threads write consecutive copies (no bank
-    // conflicts). Both values are read from the 16 staged in LDS: indexing
-    // the kernel-argument copy with a lane-dependent index would make the
-    // compiler move all 16 into vector registers for every store.
-    __syncthreads();  // code values staged
-    const float *vsf = reinterpret_cast<const float *>(vs);
+    // conflicts). Iteration k of wave w writes entries 32 k + 4 w + lane / 16:
+    // their high value, value[2 k + w / 4], is the wave's, and their low one,
+    // value[4 (w mod 4) + lane / 16], one of four the wave picks in scalar
+    // registers, so every value comes from the argument block's scalars (no
+    // staging in LDS, no barrier for it; a lane-dependent index into the
+    // argument copy would move all 16 values into vector registers).
+    {
+      const int w = wave_in_block;
+      float c[4];
 #pragma unroll
-    for (int k = 0; k < 256 * kCopies / 2 / kThreads; ++k) {
-      const int base = (k * kThreads + 64 * wave_in_block) / (kCopies / 2);
-      const int e = base + lane / (kCopies / 2);
-      const f32x4 v = {vsf[e >> 4], vsf[e & 15], vsf[e >> 4], vsf[e & 15]};
-      *reinterpret_cast<f32x4 *>(tbl + 256 * e + 16 * (lane % (kCopies / 2))) = v;
+      for (int i = 0; i < 4; ++i) {
+        float v = val[i];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) v = (w & 3) == q ? val[4 * q + i] : v;
+        // (made explicitly uniform, so the lane select below cannot be folded
+        // into a load indexed by the lane)
+        c[i] = __builtin_bit_cast(float,
+                                  __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+      }
+      const int l16 = lane >> 4;
+      const float lo = l16 == 0 ? c[0] : l16 == 1 ? c[1] : l16 == 2 ? c[2] : c[3];
+#pragma unroll
+      for (int k = 0; k < 256 * kCopies / 2 / kThreads; ++k) {
+        const float hi = (w >> 2) ? val[2 * k + 1] : val[2 * k];
+        const int e = 32 * k + 4 * w + l16;
+        const f32x4 v = {hi, lo, hi, lo};
+        *reinterpret_cast<f32x4 *>(tbl + 256 * e + 16 * (lane % (kCopies / 2))) = v;
+      }
     }
     // piece t of a slice belongs to lane t / 8, as its piece t % 8
 #pragma unroll
