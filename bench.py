@@ -61,8 +61,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # after any change to one of them the benchmark reports null until the counters
 # are taken again.
 MEASURED_TRAFFIC = {
-    "gemv": ({"gemv1.hip": "7b1ccadc5157fddf8a1f38d17beacfca638e543b73d4c0a898f745af8ad4d1b1"},
-             105667624),
+    "gemv": ({"gemv1.hip": "765fdc608a7b93162dcbb945341432151cdfb1718232c885eb4acfb046b15a1e"},
+             105719270),
     "gemm": ({"dequantize.hip": "1ae016441a333232dba8dbd5b07b9ef38751bc2fd662a64786aec8209bb3e1c9",
               "gemm.hip": "1de4b49fe46fca0f023488a02c9c55bb0985bfae51d97d387f6e373065534135"},
              593958228),
