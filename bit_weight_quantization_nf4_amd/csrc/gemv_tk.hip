@@ -14,11 +14,14 @@
 // pays, for every 16-row item, a meeting of all its waves whose LDS traffic
 // grows with M (at M = 64 four times the item's code bytes). Here no wave
 // shares an output with another wave of its group:
-//  - a workgroup (8 waves, two per SIMD) owns a block of 128 weight rows over
-//    one K range of nchs 128-code chunks; the waves form two groups that take
-//    the even and the odd chunks of the range, and each wave of a group owns
-//    32 of the block's rows (two 16-row MFMA tiles) over all of its group's
-//    chunks, so partial sums meet once per workgroup, at its end;
+//  - a workgroup (8 waves) owns a block of weight rows over one K range of
+//    nchs 128-code chunks; the waves form two groups that take the even and
+//    the odd chunks of the range, and each wave of a group owns a quarter of
+//    the block's rows over all of its group's chunks, so partial sums meet
+//    once per workgroup, at its end. Up to 16 activation rows a block is 64
+//    rows (one 16-row MFMA tile per wave; under 100 registers and 80 KB of
+//    LDS, so two workgroups share a CU and overlap their step chains), above
+//    that 128 rows (two tiles per wave, one workgroup per CU);
 //  - x of a pair of chunks (both groups' steps) is loaded by all 512 threads
 //    with coalesced 16-byte loads, three steps ahead, and written to one of
 //    two LDS stages; the 16-byte pieces of an x row sit at
@@ -54,8 +57,10 @@ constexpr int kMaxGroup = 16;
 constexpr int kMaxRanges = 8;                 // K ranges, at most (the summing kernel's limit)
 constexpr int kWaves = 8;                     // per workgroup (two per SIMD)
 constexpr int kWpg = 4;                       // waves per group
-constexpr int kNtw = 2;                       // 16-row MFMA tiles per wave
-constexpr int kBlockRows = 16 * kNtw * kWpg;  // weight rows per workgroup
+// 16-row MFMA tiles per wave: one up to 16 activation rows (64-row blocks, two
+// workgroups per CU), else two (128-row blocks, one workgroup per CU)
+constexpr int tiles_per_wave(int mt) { return mt == 1 ? 1 : 2; }
+constexpr int block_rows(int mt) { return 16 * tiles_per_wave(mt) * kWpg; }
 constexpr int kXRowBytes = 2 * kChunk;        // one activation row of a chunk
 constexpr int kBufferFlags = 0x00020000;      // word 3 of a raw buffer resource (gfx9)
 constexpr uint32_t kOOB = 0x80000000u;        // an offset past every buffer's range
@@ -83,7 +88,8 @@ struct TkArgs {
   float value[16];
 };
 
-// A wave's loads for one chunk of its two row tiles.
+// A wave's loads for one chunk of its row tiles.
+template <int kNtw>
 struct TkCodes {
   uint4 w[kNtw];     // 32 codes of row 16 t + n at k0 + 32 kg
   int32_t q[kNtw];   // int8 block code (double quant)
@@ -122,6 +128,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int MT, int NST, int DQ, int CT>
 __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
+  constexpr int kNtw = tiles_per_wave(MT);
+  constexpr int kBlockRows = block_rows(MT);
   constexpr int kXRows = 16 * MT;                         // activation rows staged
   constexpr int kStageBytes = 2 * kXRows * kXRowBytes;    // both groups' chunks
   constexpr int kXLoads = kStageBytes / (16 * 64 * kWaves);  // 16-byte loads per thread
@@ -188,7 +196,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   uint32_t wof[kNtw], rk[kNtw];
 #pragma unroll
   for (int t = 0; t < kNtw; ++t) {
-    const uint32_t r = (uint32_t)(32 * wig + 16 * t + n);  // row in the block
+    const uint32_t r = (uint32_t)(16 * kNtw * wig + 16 * t + n);  // row in the block
     wof[t] = r * row_bytes + ((uint32_t)kw0 >> 1);
     rk[t] = r * (uint32_t)K + (uint32_t)kw0;  // element index in the block at step 0
   }
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
 
   // code words and scales of this wave's chunk of step st (zeros past the range)
   auto issue_codes = [&](int st) {
-    TkCodes u;
+    TkCodes<kNtw> u;
     const bool ok = kw0 + 2 * kChunk * st < kend;
 #pragma unroll
     for (int t = 0; t < kNtw; ++t) {
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   struct TkB {
     uint4 b[kNtw][4];
   };
-  auto dequant = [&](const TkCodes &u) {
+  auto dequant = [&](const TkCodes<kNtw> &u) {
     TkB r;
 #pragma unroll
     for (int t = 0; t < kNtw; ++t) {
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   // One step's MFMAs on weights dequantized during the step before, with the
   // next step's dequantization interleaved: the matrix core runs while the
   // wave's VALU and table reads work on the next weights.
-  auto compute = [&](int stage, const TkB &cur, const TkCodes &next, TkB &nb) {
+  auto compute = [&](int stage, const TkB &cur, const TkCodes<kNtw> &next, TkB &nb) {
     const char *xb = xs + stage * kStageBytes + grp * kXRows * kXRowBytes;
     float ap[kNtw];
 #pragma unroll
@@ -311,7 +319,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
   // no loop-carried registers the compiler's waits are exact.
   constexpr int kAhead = 3;
   uint4 xr[NST + kAhead][kXLoads];
-  TkCodes ring[NST + kAhead];
+  TkCodes<kNtw> ring[NST + kAhead];
 #pragma unroll
   for (int st = 0; st < kAhead; ++st) {
     issue_x(st, xr[st]);
@@ -382,7 +390,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemv_tk_kernel(TkArgs args) {
 #pragma unroll
   for (int t = 0; t < kNtw; ++t) {
     // D layout of the 16x16 MFMA: lane l holds rows 4 (l / 16) + r of column l % 16
-    const int row = row0 + 32 * wig + 16 * t + n;
+    const int row = row0 + 16 * kNtw * wig + 16 * t + n;
     const float bias = widen16<CT>(
         __builtin_amdgcn_raw_buffer_load_b16(brs, (int)(2u * (uint32_t)row), 0, 0));
 #pragma unroll
@@ -439,12 +447,17 @@ hipError_t launch_tk_nst(const TkArgs &args, dim3 grid, int nst, int dq, int ct,
 // workgroups (blocks x ranges) within one round on the CUs, but no more than
 // make the partial sums (written and read back, 8 S M N bytes) as large as
 // the codes (N K / 2 bytes): S <= K / (16 M).
+// Rows of a workgroup's block, and workgroups a CU holds at once, by M.
+int tk_block_rows(int M) { return block_rows(gemv_row_tiles(M)); }
+int tk_wgs_per_cu(int M) { return gemv_row_tiles(M) == 1 ? 2 : 1; }
+
 int tk_ranges(int M, int N, int K) {
   const int nch = (K + kChunk - 1) / kChunk;
   const int smin = (nch + 15) / 16;
   if (smin > kMaxRanges) return 0;
-  const int blocks = (N + kBlockRows - 1) / kBlockRows;
-  int s = device_cu_count() / (blocks > 0 ? blocks : 1);
+  const int br = tk_block_rows(M);
+  const int blocks = (N + br - 1) / br;
+  int s = device_cu_count() * tk_wgs_per_cu(M) / (blocks > 0 ? blocks : 1);
   const int cap = K / (16 * M);
   if (s > cap) s = cap;
   if (s > kMaxRanges) s = kMaxRanges;
@@ -534,7 +547,7 @@ hipError_t launch_gemv_tk(int count, const GemvDesc *descs, int M, int K, int qu
       q.ldy_bytes = (uint32_t)(d.ldy * ye);
       q.y_bytes = (uint32_t)(((int64_t)(M - 1) * d.ldy + d.N) * ye);
     }
-    q.wgs = (d.N + kBlockRows - 1) / kBlockRows * S;
+    q.wgs = (d.N + tk_block_rows(M) - 1) / tk_block_rows(M) * S;
     if (q.wgs > grid) grid = q.wgs;
     const int st = (q.nchs + 1) / 2;
     if (st > steps) steps = st;

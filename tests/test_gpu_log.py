@@ -49,8 +49,9 @@ def test_log_lines_name_each_dispatch():
     assert "dequantize 1 tensor(s) (first n=4931584) out_dtype=0: dequantize_kernel" in text, text
     assert "decode M=1: gemv1_kernel" in text, text
     assert "decode M=4 K=11008: gemv_mt_kernel (x streamed)" in text, text
+    # 448 rows = 7 blocks of 64 at M = 16 (two workgroups per CU): 8 K ranges
     assert ("decode M=16 K=11008: gemv_tk_kernel (x staged in LDS; first product in 8 K range(s) "
-            "of 11 chunks), 6 steps, grid 32 x 1, then gemv_split_reduce_kernel") in text, text
+            "of 11 chunks), 6 steps, grid 56 x 1, then gemv_split_reduce_kernel") in text, text
     # 448 rows = 4 blocks of 128: 8 K ranges (at most K / (16 M) = 21), 11 chunks each
     assert ("decode M=32 K=11008: gemv_tk_kernel (x staged in LDS; first product in 8 K range(s) "
             "of 11 chunks), 6 steps, grid 32 x 1, then gemv_split_reduce_kernel") in text, text
