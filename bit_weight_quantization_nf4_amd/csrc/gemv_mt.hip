@@ -1103,15 +1103,18 @@ int gemv_split_ranges(int M, int K) {
   return s <= kMaxSplit ? s : 0;
 }
 
-// The tiled kernel takes a 9..64-row product whose x the register-resident
-// kernel would split into K ranges: two or more ranges at 9..16 rows, three or
+// The tiled kernel takes an 8..64-row product whose x the register-resident
+// kernel would split into K ranges: two or more ranges at 8..16 rows, three or
 // more (or x it could not hold at all) from 17 rows. On [4096, 11008] it
 // measured 17.8 / 20.5 / 25.8 us at M = 16 / 32 / 64 against 19.3 / 29-31 /
 // 34-35 us; with one or two ranges at 17..64 rows ([11008, 4096]) the two were
 // even or the register-resident kernel faster, and a layer launch mixing
 // 4096- and 11008-row products slower (more workgroups than one round of CUs).
 static bool use_tk(int M, int N, int K) {
-  if (M <= 8 || !gemv_tk_enabled() || gemv_tk_ranges(M, N, K) <= 0) return false;
+  if (M <= 7 || !gemv_tk_enabled() || gemv_tk_ranges(M, N, K) <= 0) return false;
+  // 8 rows: where x would take two ranges of the register-resident kernel
+  // (which streams x instead at this M); on [4096, 11008] 15.7 against 16.6 us
+  if (M == 8) return (K + kChunk - 1) / kChunk > 48;
   const int s = gemv_split_ranges(M, K);
   return M > 16 ? (s == 0 || s >= 3) : s >= 2;
 }
@@ -1128,8 +1131,8 @@ hipError_t launch_gemv_mt(int count, const GemvDesc *descs, int M, int K, int qu
                           size_t workspace_bytes, hipStream_t stream) {
   if (count == 0 || M == 0) return hipSuccess;
   if (count > kMaxGroup || M > 64) return hipErrorInvalidValue;
-  if (M > 8) {
-    // 9..64 activation rows: the products use_tk picks go to the tiled
+  if (M >= 8) {
+    // 8..64 activation rows: the products use_tk picks go to the tiled
     // kernel when the call brings their workspace, the others (a launch of
     // their own, which may use the whole workspace after it) below, so each
     // product takes the kernel it takes alone

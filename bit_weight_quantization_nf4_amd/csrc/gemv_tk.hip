@@ -1,5 +1,5 @@
 // gemv_tk.hip -- decode products y_i[M, N_i] = x_i[M, K] . cd(dequant(W_i))^T
-// for 9 <= M <= 64 on gfx950 matrix cores, with x staged through LDS and the
+// for 8 <= M <= 64 on gfx950 matrix cores, with x staged through LDS and the
 // K dimension split over workgroups; cd is the rounding to the compute dtype
 // (bf16 or fp16).
 //
@@ -476,7 +476,7 @@ int tk_chunks_per_range(int M, int N, int K) {
 }  // namespace
 
 int gemv_tk_ranges(int M, int N, int K) {
-  if (M <= 8 || M > 64 || K <= 0 || N <= 0) return 0;
+  if (M <= 7 || M > 64 || K <= 0 || N <= 0) return 0;
   const int s = tk_ranges(M, N, K);
   // the partial sums are addressed with 31-bit byte offsets
   if ((int64_t)s * M * N * 4 >= ((int64_t)1 << 31)) return 0;

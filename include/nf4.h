@@ -313,12 +313,13 @@ nf4_status nf4_linear_ex(const void *x, int64_t ldx, int32_t M, const nf4_qweigh
  * 4-bit weights are dequantized to the compute dtype for the matmul]. Among
  * decode shapes (M <= NF4_GEMV_MAX_M, bf16 / fp16 compute) it is non-zero for
  * those whose activations, x[M,
- * K], do not fit the registers of one compute unit -- 9 <= M <= 16 with K >
+ * K], do not fit the registers of one compute unit -- 8 <= M <= 16 with K >
  * 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048 (at most 8 K ranges;
  * fewer rows, or longer K, stream x) -- which are then split along K: each K
  * range is summed into fp32 partials in the workspace and a second kernel adds
  * the ranges in order. Where that split would take two (M <= 16) or three
- * (M > 16) or more ranges and K <= 16384, a tiled kernel takes the product
+ * (M > 16) or more ranges and K <= 16384 (at 8 rows, every such product), a
+ * tiled kernel takes the product
  * with a split of its own (up to 8 ranges of at most 2048 codes, as many as
  * keep the product within one round of workgroups on the device's compute
  * units), so the size depends on N and the CU count as well [repo page

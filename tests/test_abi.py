@@ -242,11 +242,16 @@ def test_workspace_bytes_query(nf4):
     assert q(1, 4096, 11008, 64, BF, F32, 1) == 0          # single-row kernel
     assert q(16, 4096, 6144, 64, BF, F32, 1) == 0          # 48 chunks fit
     # 9..16 rows with x past one CU: the tiled kernel's split (ranges of at
-    # most 16 chunks, as many as keep one round of workgroups on 256 CUs)
+    # most 16 chunks, as many as keep one round of workgroups, two per CU, on
+    # 256 CUs)
     assert q(16, 4096, 6272, 64, BF, F32, 1) == 7 * 16 * 4096 * 4  # 49 chunks -> 7 x 7
     assert q(16, 4096, 11008, 64, BF, BF, 1) == 8 * 16 * 4096 * 4
     assert q(1, 4096, 11008, 64, F16, F16, 1) == 0         # M <= 8 streams x
-    assert q(8, 4096, 11008, 64, BF, F32, 1) == 0
+    # 8 rows with x past two ranges of the register-resident kernel: the tiled
+    # kernel (64-row blocks, two workgroups per CU: 64 blocks x 8 ranges)
+    assert q(8, 4096, 11008, 64, BF, F32, 1) == 8 * 8 * 4096 * 4
+    assert q(7, 4096, 11008, 64, BF, F32, 1) == 0          # M <= 7 streams x
+    assert q(8, 4096, 6144, 64, BF, F32, 1) == 0           # 48 chunks fit
     assert q(9, 100, 11008, 64, BF, BF, 2) == (8 * 9 * 100 * 4 + 255) // 256 * 256  # centred
     assert q(32, 11008, 4096, 64, BF, F32, 1) == 0
     assert q(32, 11008, 4224, 64, BF, F32, 1) == 2 * 32 * 11008 * 4

@@ -1,6 +1,6 @@
 """GPU parity of the decode products for M up to 64 and of the K split.
 
-Activations that do not fit the registers of one compute unit (9 <= M <= 16
+Activations that do not fit the registers of one compute unit (8 <= M <= 16
 with K > 6144, 17 <= M <= 32 with K > 4096, M > 32 with K > 2048) are split along K
 when the caller brings a workspace (nf4_linear_ws, nf4_gemv_grouped_ws): each
 K range is summed into fp32 partials and a second kernel adds the ranges in
@@ -222,8 +222,9 @@ def test_gemv_7b_layer_m64_split(nf4, orc):
 
 
 def test_tiled_decode_ragged_modes_and_groups(nf4, orc):
-    """The tiled decode kernel (17..64 rows whose x would take three or more K
-    ranges in registers): ragged N (a partial 128-row block), K that ends
+    """The tiled decode kernel (8..16 rows whose x would take two or more K
+    ranges in registers, 64-row blocks; 17..64 rows with three or more, 128-row
+    blocks): ragged N (a partial block), K that ends
     inside a 128-code chunk and ranges with an odd number of chunks, the three
     double-quant modes, bf16 and fp16 compute, every output against the
     oracle; the 16-bit output equals the rounding of the fp32 run, repeated
@@ -233,6 +234,8 @@ def test_tiled_decode_ragged_modes_and_groups(nf4, orc):
         (200, 8352, 17, 32, 2, "bf16"),   # 66 chunks, the last a quarter; 8 ranges of <= 9
         (131, 5184, 33, 64, 1, "fp16"),   # 41 chunks, the last a half; 2 blocks, the second of 3 rows
         (4097, 4224, 64, 128, 0, "bf16"), # 33 chunks; 33 blocks, the last of 1 row
+        (70, 8384, 8, 64, 1, "bf16"),     # 8 rows, 66 chunks, the last a half; 2 blocks of 64, the second of 6 rows
+        (131, 7232, 12, 32, 2, "fp16"),   # 57 chunks, the last a half; 3 blocks, the last of 3 rows
     ]
     for i, (N, K, M, bs, dq, ct) in enumerate(cases):
         ws = []
