@@ -232,9 +232,10 @@ def test_workspace_bytes_query(nf4):
     single-row kernel, x that fits one CU's registers, fp32 compute, the GEMM
     below 1536 rows, more K ranges than the kernel takes); S * M * N * 4
     rounded up to 256 for a decode K split (S K ranges of at most 48 / 32 / 16
-    chunks of 128 codes at M <= 16 / 32 / 64; up to M = 8 x streams instead;
-    from 9 rows, a split into two or more such ranges (three or more from 17
-    rows) takes the tiled kernel's split instead);
+    chunks of 128 codes at M <= 16 / 32 / 64; up to M = 8 the register-
+    resident kernel streams x instead; from 8 rows, a product whose x would
+    take two or more such ranges (three or more from 17 rows) takes the tiled
+    kernel's split instead);
     2 * N * K rounded up to 256 for a prefill product of 1536 rows or more (the
     weight dequantized once)."""
     q = nf4.lib().nf4_linear_workspace_bytes
